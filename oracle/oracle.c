@@ -1,0 +1,289 @@
+/*
+ * oracle.c -- plain, slow, fp64 CPU oracle for sink-aware grouped-query
+ * attention with per-head RMSNorm and NeoX RoPE on Q and K.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file.  Only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header or table with the HIP path.
+ *
+ * Sources (NeMo AutoModel API reference pages):
+ *   [L]  "nemo_automodel.components.models.flint.layers" -- FlintAttention
+ *        (class summary: separate Q/K/V, per-head RMSNorm, selective NeoX RoPE,
+ *        learned sinks; _apply_rope: rotate corresponding channels in the two
+ *        halves of each head; forward: full-sequence causal attention with a
+ *        zero-value sink category, document-local zero-based THD positions),
+ *        _FlintSinkParameters (FP32 denominator logits, returned unscaled,
+ *        one per query head).
+ *   [C]  "nemo_automodel.components.models.flint.config" -- FlintConfig
+ *        (docstring: full layers have no RoPE, sliding layers rotate all head
+ *        channels with NeoX RoPE, the window counts the current token;
+ *        fields rms_norm_eps = 1e-6, head_dim = 128, 32 / 4 heads).
+ *   [U]  "nemo_automodel.components.attention.utils" --
+ *        preprocess_args_and_kwargs_for_attn (THD tensors [tokens, heads,
+ *        head_dim]; cu_seqlens int32 [documents + 1]; a positive left window
+ *        counts visible keys including the current token, negative means
+ *        unbounded).
+ *
+ * Every step is the plain definition, evaluated in double precision from the
+ * exactly widened inputs, one (token, head) row at a time:
+ *   1. per-head RMSNorm      y = w * x / sqrt(mean(x^2) + eps)              [L],[C]
+ *   2. NeoX RoPE (optional)  pair channel i with i + d/2, angle p*theta^(-2i/d) [L],[C]
+ *   3. visible set J(t)      same document, p(u) <= p(t), and p(t) - p(u) < W  [L],[C],[U]
+ *   4. scores               s_u = scale * <q_hat, k_hat_u>                    [L]
+ *   5. softmax with the sink as one extra category of value zero:
+ *        M = max(sink, max_J s),  Z = exp(sink - M) + sum_J exp(s_u - M),
+ *        out = sum_J exp(s_u - M) v_u / Z,   lse = M + log Z                  [L]
+ * Readings where the pages leave a step open (scale 1/sqrt(d), weight shape
+ * [d] shared by all heads, norm before RoPE, inv_freq = theta^(-2i/d),
+ * kv head = h / (Hq/Hkv), lse including the sink, an empty row giving
+ * out = 0 and lse = sink) are listed with the tests that pin them.
+ *
+ * Parity pinned by tests/test_oracle_pins.py except where noted there.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_EINVAL -1
+
+/* Document of each token and the token's position inside its document.
+ * [L] forward(): THD position_ids are document-local, contiguous and
+ * zero-based by default.  cu has num_docs + 1 entries, cu[0] = 0,
+ * non-decreasing, cu[num_docs] = T ([U] cu_seqlens). */
+static int doc_layout(int T, int num_docs, const int32_t* cu, int32_t* doc_of,
+                      int32_t* pos_of) {
+  if (cu[0] != 0 || cu[num_docs] != T) return ORACLE_EINVAL;
+  for (int n = 0; n < num_docs; ++n) {
+    if (cu[n + 1] < cu[n]) return ORACLE_EINVAL;
+    for (int t = cu[n]; t < cu[n + 1]; ++t) {
+      doc_of[t] = n;
+      pos_of[t] = t - cu[n];
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* Step 1: per-head RMSNorm of one head vector ([L] FlintAttention q_norm /
+ * k_norm; [C] rms_norm_eps).  The weight has head_dim entries shared by all
+ * heads of the projection. */
+static void rmsnorm_vec(int d, const double* x, const double* w, double eps,
+                        double* y) {
+  double ss = 0.0;
+  for (int i = 0; i < d; ++i) ss += x[i] * x[i];
+  double inv = 1.0 / sqrt(ss / (double)d + eps);
+  for (int i = 0; i < d; ++i) y[i] = w[i] * x[i] * inv;
+}
+
+/* Step 2: NeoX rotary embedding at integer position p ([L] _apply_rope:
+ * corresponding channels of the two halves are rotated together; [C] all
+ * channels are rotated).  Channel i (i < d/2) and channel i + d/2 form one
+ * pair turned by the angle p * theta^(-2i/d). */
+static void rope_neox_vec(int d, double p, double theta, double* y) {
+  int half = d / 2;
+  for (int i = 0; i < half; ++i) {
+    double inv_freq = pow(theta, -2.0 * (double)i / (double)d);
+    double ang = p * inv_freq;
+    double c = cos(ang), s = sin(ang);
+    double a = y[i], b = y[i + half];
+    y[i] = a * c - b * s;
+    y[i + half] = b * c + a * s;
+  }
+}
+
+/* Steps 1-2 for a whole [rows, H, d] tensor.  x and y may not alias.
+ * pos[r] is the document-local position of row r. */
+static void prologue_rows(int rows, const int32_t* pos, int H, int d,
+                          const double* x, const double* w, double eps,
+                          double theta, int use_rope, double* y) {
+  for (int r = 0; r < rows; ++r)
+    for (int h = 0; h < H; ++h) {
+      const double* xi = x + ((size_t)r * H + h) * d;
+      double* yi = y + ((size_t)r * H + h) * d;
+      rmsnorm_vec(d, xi, w, eps, yi);
+      if (use_rope) rope_neox_vec(d, (double)pos[r], theta, yi);
+    }
+}
+
+/* Public: steps 1-2 on every token of a packed THD tensor x [T, H, d]. */
+int oracle_rmsnorm_rope(int T, int num_docs, const int32_t* cu, int H, int d,
+                        const double* x, const double* w, double eps,
+                        double theta, int use_rope, double* y) {
+  if (T < 0 || num_docs < 0 || H <= 0 || d <= 0 || (d & 1)) return ORACLE_EINVAL;
+  int32_t* doc_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  int32_t* pos_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  int rc = doc_layout(T, num_docs, cu, doc_of, pos_of);
+  if (rc == ORACLE_OK)
+    prologue_rows(T, pos_of, H, d, x, w, eps, theta, use_rope, y);
+  free(doc_of);
+  free(pos_of);
+  return rc;
+}
+
+/* Step 3: is key u visible to query t?  Same document, not in the future
+ * ([L] forward: causal), and inside the window when one is set: the window
+ * counts the current token, so W = 1 sees only the query itself ([C]
+ * docstring; [U] window_size).  window < 0 means unbounded. */
+static int visible(int t, int u, const int32_t* doc_of, const int32_t* pos_of,
+                   int window) {
+  if (doc_of[u] != doc_of[t]) return 0;
+  int dp = pos_of[t] - pos_of[u];
+  if (dp < 0) return 0;
+  if (window > 0 && dp >= window) return 0;
+  return 1;
+}
+
+/* Steps 3-5 for one (token t, query head) row.  qh: the row's normalised and
+ * rotated query [d]; kh, v: [T, Hkv, d]; g: the kv head of this query head.
+ * The sink is one more softmax category whose value vector is zero and whose
+ * logit is used as given, without the softmax scale ([L]
+ * _FlintSinkParameters.forward returns unscaled logits; FlintAttention.forward
+ * names the zero-value sink category).  scores is scratch of T doubles. */
+static void attend_row(int t, int T, int Hkv, int g, int d, const double* qh,
+                       const double* kh, const double* v, double sink,
+                       double scale, int window, const int32_t* doc_of,
+                       const int32_t* pos_of, double* scores, double* out_row,
+                       double* lse_out) {
+  /* scores over the visible set */
+  int n_vis = 0;
+  double M = sink;
+  for (int u = 0; u < T; ++u) {
+    scores[u] = -INFINITY;
+    if (!visible(t, u, doc_of, pos_of, window)) continue;
+    const double* ku = kh + ((size_t)u * Hkv + g) * d;
+    double dot = 0.0;
+    for (int i = 0; i < d; ++i) dot += qh[i] * ku[i];
+    scores[u] = scale * dot;
+    if (scores[u] > M) M = scores[u];
+    ++n_vis;
+  }
+  for (int i = 0; i < d; ++i) out_row[i] = 0.0;
+  if (n_vis == 0) {
+    /* No visible key: only the zero-value sink category remains. */
+    *lse_out = sink;
+    return;
+  }
+  /* denominator Z includes the sink category; the numerator does not */
+  double Z = exp(sink - M);
+  for (int u = 0; u < T; ++u) {
+    if (scores[u] == -INFINITY) continue;
+    double e = exp(scores[u] - M);
+    Z += e;
+    const double* vu = v + ((size_t)u * Hkv + g) * d;
+    for (int i = 0; i < d; ++i) out_row[i] += e * vu[i];
+  }
+  for (int i = 0; i < d; ++i) out_row[i] /= Z;
+  *lse_out = M + log(Z);
+}
+
+/* Public: steps 3-5 given already normalised/rotated queries and keys.
+ *   qh   [n_rows, Hq, d]   query rows for the tokens listed in rows
+ *   kh,v [T, Hkv, d]       every key / value token
+ *   rows token index of each query row, or NULL for all T tokens in order
+ *   out  [n_rows, Hq, d];  lse [Hq, n_rows] (may be NULL)
+ * Query head h reads kv head h / (Hq / Hkv).  nthreads <= 0 uses every
+ * OpenMP thread.  Returns 0, or -1 on an invalid argument. */
+int oracle_attention(int T, int num_docs, const int32_t* cu, int Hq, int Hkv,
+                     int d, const double* qh, const double* kh,
+                     const double* v, const double* sinks, double scale,
+                     int window, const int32_t* rows, int n_rows, double* out,
+                     double* lse, int nthreads) {
+  if (T < 0 || num_docs < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv)
+    return ORACLE_EINVAL;
+  if (window == 0) return ORACLE_EINVAL;
+  if (rows == NULL) n_rows = T;
+  if (n_rows < 0) return ORACLE_EINVAL;
+  int32_t* doc_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  int32_t* pos_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  int rc = doc_layout(T, num_docs, cu, doc_of, pos_of);
+  if (rc == ORACLE_OK && rows)
+    for (int r = 0; r < n_rows; ++r)
+      if (rows[r] < 0 || rows[r] >= T) rc = ORACLE_EINVAL;
+  if (rc != ORACLE_OK) {
+    free(doc_of);
+    free(pos_of);
+    return rc;
+  }
+  int group = Hq / Hkv;
+#ifdef _OPENMP
+  int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
+#endif
+  {
+    double* scores = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    double lse_val;
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+    for (long item = 0; item < (long)n_rows * Hq; ++item) {
+      int r = (int)(item / Hq), h = (int)(item % Hq);
+      int t = rows ? rows[r] : r;
+      attend_row(t, T, Hkv, h / group, d, qh + ((size_t)r * Hq + h) * d, kh, v,
+                 sinks[h], scale, window, doc_of, pos_of, scores,
+                 out + ((size_t)r * Hq + h) * d, &lse_val);
+      if (lse) lse[(size_t)h * n_rows + r] = lse_val;
+    }
+    free(scores);
+  }
+  free(doc_of);
+  free(pos_of);
+  return ORACLE_OK;
+}
+
+/* Public: the whole forward pass, steps 1-5.
+ *   q [n_rows, Hq, d] raw (projected) queries of the tokens in rows (all T
+ *   tokens when rows is NULL); k, v [T, Hkv, d] raw keys and values;
+ *   qnorm_w, knorm_w [d]; sinks [Hq]; scale <= 0 selects 1/sqrt(d).
+ * V passes through untouched ([L]: only Q and K are normalised and rotated). */
+int oracle_sink_attn_fwd(int T, int num_docs, const int32_t* cu, int Hq,
+                         int Hkv, int d, const double* q, const double* k,
+                         const double* v, const double* sinks,
+                         const double* qnorm_w, const double* knorm_w,
+                         double eps, double theta, double scale, int window,
+                         int use_rope, const int32_t* rows, int n_rows,
+                         double* out, double* lse, int nthreads) {
+  if (T < 0 || num_docs < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || (d & 1) ||
+      Hq % Hkv || window == 0)
+    return ORACLE_EINVAL;
+  if (rows == NULL) n_rows = T;
+  if (n_rows < 0) return ORACLE_EINVAL;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+  int32_t* doc_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  int32_t* pos_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  int32_t* qpos = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n_rows > 0 ? n_rows : 1));
+  int rc = doc_layout(T, num_docs, cu, doc_of, pos_of);
+  for (int r = 0; rc == ORACLE_OK && r < n_rows; ++r) {
+    int t = rows ? rows[r] : r;
+    if (t < 0 || t >= T) rc = ORACLE_EINVAL;
+    else qpos[r] = pos_of[t];
+  }
+  double* qh = NULL;
+  double* kh = NULL;
+  if (rc == ORACLE_OK) {
+    qh = (double*)malloc(sizeof(double) * ((size_t)n_rows * Hq * d + 1));
+    kh = (double*)malloc(sizeof(double) * ((size_t)T * Hkv * d + 1));
+    prologue_rows(n_rows, qpos, Hq, d, q, qnorm_w, eps, theta, use_rope, qh);
+    prologue_rows(T, pos_of, Hkv, d, k, knorm_w, eps, theta, use_rope, kh);
+    rc = oracle_attention(T, num_docs, cu, Hq, Hkv, d, qh, kh, v, sinks, scale,
+                          window, rows, n_rows, out, lse, nthreads);
+  }
+  free(qh);
+  free(kh);
+  free(qpos);
+  free(doc_of);
+  free(pos_of);
+  return rc;
+}
+
+/* Number of OpenMP threads a call with nthreads <= 0 would use. */
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

@@ -1,0 +1,152 @@
+"""ctypes front end of the fp64 CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline leg import this module.  The product package never does, and this
+module imports nothing from the product package.
+
+All arrays are numpy float64 / int32, C-contiguous.  Inputs are widened from
+their storage dtype exactly (bf16 -> fp64 and fp32 -> fp64 are exact) by the
+caller; the oracle then follows the definition in oracle.c step by step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+LIB_PATH = os.environ.get("SINKATTN_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True, src: str = _SRC, out: str | None = None) -> str:
+    """Compile oracle.c (or another copy of it) into a shared library with
+    plain gcc and OpenMP; by default into liboracle.so next to it."""
+    out = out or LIB_PATH
+    if not force and os.path.exists(out):
+        return out
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fopenmp", "-fPIC",
+           "-shared", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    D = ctypes.c_double
+    lib.oracle_rmsnorm_rope.argtypes = [I, I, P, I, I, P, P, D, D, I, P]
+    lib.oracle_rmsnorm_rope.restype = I
+    lib.oracle_attention.argtypes = [I, I, P, I, I, I, P, P, P, P, D, I, P, I,
+                                     P, P, I]
+    lib.oracle_attention.restype = I
+    lib.oracle_sink_attn_fwd.argtypes = [I, I, P, I, I, I, P, P, P, P, P, P,
+                                         D, D, D, I, I, P, I, P, P, I]
+    lib.oracle_sink_attn_fwd.restype = I
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = I
+    _lib = lib
+    return lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class OracleError(ValueError):
+    pass
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def rmsnorm_rope(x, cu_seqlens, w, eps=1e-6, theta=1e6, use_rope=True):
+    """Per-head RMSNorm then (optionally) NeoX RoPE of a THD tensor [T, H, d]."""
+    x = _f64(x)
+    T, H, d = x.shape
+    cu = _i32(cu_seqlens)
+    w = _f64(w)
+    y = np.empty_like(x)
+    rc = _load().oracle_rmsnorm_rope(T, len(cu) - 1, _ptr(cu), H, d, _ptr(x),
+                                     _ptr(w), float(eps), float(theta),
+                                     int(bool(use_rope)), _ptr(y))
+    if rc:
+        raise OracleError(f"oracle_rmsnorm_rope rejected its arguments ({rc})")
+    return y
+
+
+def attention(qh, kh, v, cu_seqlens, sinks, window=-1, scale=None, rows=None,
+              nthreads=0):
+    """Sink attention on already normalised/rotated rows.
+
+    qh [n_rows, Hq, d] (rows of the listed tokens, or all T tokens),
+    kh / v [T, Hkv, d].  Returns (out [n_rows, Hq, d], lse [Hq, n_rows]).
+    """
+    qh, kh, v = _f64(qh), _f64(kh), _f64(v)
+    T, Hkv, d = kh.shape
+    n_rows, Hq, _ = qh.shape
+    cu = _i32(cu_seqlens)
+    sinks = _f64(sinks)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.empty((n_rows, Hq, d), dtype=np.float64)
+    lse = np.empty((Hq, n_rows), dtype=np.float64)
+    rows_arr = None if rows is None else _i32(rows)
+    rc = _load().oracle_attention(
+        T, len(cu) - 1, _ptr(cu), Hq, Hkv, d, _ptr(qh), _ptr(kh), _ptr(v),
+        _ptr(sinks), float(scale), int(window),
+        None if rows_arr is None else _ptr(rows_arr), n_rows, _ptr(out),
+        _ptr(lse), int(nthreads))
+    if rc:
+        raise OracleError(f"oracle_attention rejected its arguments ({rc})")
+    return out, lse
+
+
+def sink_attn_fwd(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window,
+                  use_rope, eps=1e-6, theta=1e6, scale=None, rows=None,
+                  nthreads=0):
+    """The whole forward pass in fp64.
+
+    q [n_rows, Hq, d] holds the raw queries of the tokens listed in rows (all
+    T tokens when rows is None); k, v [T, Hkv, d].  Returns
+    (out [n_rows, Hq, d], lse [Hq, n_rows]) as float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, Hkv, d = k.shape
+    n_rows, Hq, _ = q.shape
+    cu = _i32(cu_seqlens)
+    out = np.empty((n_rows, Hq, d), dtype=np.float64)
+    lse = np.empty((Hq, n_rows), dtype=np.float64)
+    rows_arr = None if rows is None else _i32(rows)
+    if rows_arr is None and n_rows != T:
+        raise OracleError("q must hold all T tokens when rows is None")
+    rc = _load().oracle_sink_attn_fwd(
+        T, len(cu) - 1, _ptr(cu), Hq, Hkv, d, _ptr(q), _ptr(k), _ptr(v),
+        _ptr(_f64(sinks)), _ptr(_f64(qnorm_w)), _ptr(_f64(knorm_w)),
+        float(eps), float(theta), float(scale) if scale else 0.0, int(window),
+        int(bool(use_rope)), None if rows_arr is None else _ptr(rows_arr),
+        n_rows, _ptr(out), _ptr(lse), int(nthreads))
+    if rc:
+        raise OracleError(f"oracle_sink_attn_fwd rejected its arguments ({rc})")
+    return out, lse

@@ -1,0 +1,52 @@
+"""Each plausible mistake planted in a copy of the oracle (dropped term, wrong
+sign, wrong index, wrong operand) must make at least one pin fail.
+
+The mutants are compiled on the CPU from text substitutions of oracle.c into a
+temporary directory; the pins run against them in a subprocess through the
+SINKATTN_ORACLE_LIB override.  The oracle itself is never modified."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "eps_dropped": ("ss / (double)d + eps", "ss / (double)d"),
+    "sum_not_mean": ("sqrt(ss / (double)d + eps)", "sqrt(ss + eps)"),
+    "norm_weight_dropped": ("y[i] = w[i] * x[i] * inv;", "y[i] = x[i] * inv;"),
+    "rope_sign": ("y[i] = a * c - b * s;", "y[i] = a * c + b * s;"),
+    "rope_interleaved_halves": ("int half = d / 2;", "int half = d / 4;"),
+    "rope_exponent": ("-2.0 * (double)i / (double)d", "-1.0 * (double)i / (double)d"),
+    "global_positions": ("pos_of[t] = t - cu[n];", "pos_of[t] = t;"),
+    "window_off_by_one": ("dp >= window", "dp > window"),
+    "anti_causal": ("if (dp < 0) return 0;", "if (dp > 0) return 0;"),
+    "cross_document": ("if (doc_of[u] != doc_of[t]) return 0;", ""),
+    "gqa_modulo": ("h / group, d, qh", "h % Hkv, d, qh"),
+    "score_scale_dropped": ("scores[u] = scale * dot;", "scores[u] = dot;"),
+    "sink_term_dropped": ("double Z = exp(sink - M);", "double Z = 0.0;"),
+    "sink_scaled": ("double Z = exp(sink - M);", "double Z = exp(sink * scale - M);"),
+    "sink_in_max_dropped": ("double M = sink;", "double M = -INFINITY;"),
+    "lse_shift_dropped": ("*lse_out = M + log(Z);", "*lse_out = log(Z);"),
+    "value_of_query_token": ("v + ((size_t)u * Hkv + g) * d", "v + ((size_t)t * Hkv + g) * d"),
+    "key_head_zero": ("kh + ((size_t)u * Hkv + g) * d", "kh + ((size_t)u * Hkv) * d"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    import oracle.oracle as O
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(old, new)
+    csrc = tmp_path / "oracle_mutant.c"
+    csrc.write_text(mutated)
+    lib = O.build(force=True, src=str(csrc), out=str(tmp_path / "liboracle_mutant.so"))
+    env = dict(os.environ, SINKATTN_ORACLE_LIB=lib, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} survived every pin:\n{r.stdout[-2000:]}"
