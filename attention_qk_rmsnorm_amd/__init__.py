@@ -1,0 +1,17 @@
+"""MI355X (gfx950) sink-aware grouped-query attention forward.
+
+Per-head RMSNorm and NeoX RoPE on Q and K, then causal or sliding-window
+attention over packed variable-length documents (THD, cu_seqlens) with one
+learned fp32 sink logit per query head, in hand-written HIP kernels behind the
+C ABI of include/sink_attn.h.  This package is the thin Python binding.
+"""
+from .binding import (SINK_ATTN_BF16, SINK_ATTN_F32, Call, SinkAttnDesc, SinkAttnError,
+                      header_functions, library_path, load_library, make_desc,
+                      sink_attn_fwd, sink_attn_prologue, sink_attn_workspace_bytes,
+                      status_string, workspace_bytes)
+
+__all__ = [
+    "SINK_ATTN_BF16", "SINK_ATTN_F32", "Call", "SinkAttnDesc", "SinkAttnError",
+    "header_functions", "library_path", "load_library", "make_desc", "sink_attn_fwd",
+    "sink_attn_prologue", "sink_attn_workspace_bytes", "status_string", "workspace_bytes",
+]

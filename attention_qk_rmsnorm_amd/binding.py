@@ -1,0 +1,225 @@
+"""Thin Python binding of libsinkattn (the C ABI of include/sink_attn.h).
+
+Argument marshalling only: this module turns torch tensors into device
+pointers and the current HIP stream, allocates outputs and the workspace with
+torch when the caller does not pass them, and raises on a non-zero status.
+Every step of the computation runs in the library's HIP kernels; there is no
+other path.  The library must have been built (attention_qk_rmsnorm_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+from .build import LIB_PATH
+
+SINK_ATTN_BF16 = 0
+SINK_ATTN_F32 = 1
+
+_DTYPES = {torch.bfloat16: SINK_ATTN_BF16, torch.float32: SINK_ATTN_F32}
+
+
+class SinkAttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("total_tokens", ctypes.c_int32),
+        ("num_docs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("max_seqlen", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("rms_eps", ctypes.c_double),
+        ("rope_theta", ctypes.c_double),
+        ("softmax_scale", ctypes.c_double),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class SinkAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load_library():
+    """Load libsinkattn.so; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with attention_qk_rmsnorm_amd.build.build() "
+            "(hipcc --offload-arch=gfx950); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32 = ctypes.c_void_p, ctypes.c_int32
+    DP = ctypes.POINTER(SinkAttnDesc)
+    lib.sink_attn_workspace_bytes.argtypes = [DP]
+    lib.sink_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.sink_attn_fwd.argtypes = [DP, P, P, P, P, P, P, P, I32, I32, P, P, P]
+    lib.sink_attn_fwd.restype = ctypes.c_int
+    lib.sink_attn_prologue.argtypes = [DP, P, P, P, P, I32, P]
+    lib.sink_attn_prologue.restype = ctypes.c_int
+    lib.sink_attn_attention.argtypes = [DP, P, P, P, P, I32, I32, P, P, P]
+    lib.sink_attn_attention.restype = ctypes.c_int
+    lib.sink_attn_status_string.argtypes = [ctypes.c_int]
+    lib.sink_attn_status_string.restype = ctypes.c_char_p
+    lib.sink_attn_version.argtypes = []
+    lib.sink_attn_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().sink_attn_status_string(int(status)).decode()
+
+
+def header_functions() -> list:
+    """Names of the functions include/sink_attn.h declares."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    with open(os.path.join(os.path.dirname(here), "include", "sink_attn.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^[A-Za-z_][\w \*]*?\b(sink_attn_\w+)\s*\(", text, flags=re.M)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def make_desc(total_tokens, num_docs, num_q_heads, num_kv_heads, head_dim, dtype,
+              rms_eps=1e-6, rope_theta=1e6, softmax_scale=0.0, workspace=None,
+              max_seqlen=0) -> SinkAttnDesc:
+    d = SinkAttnDesc()
+    d.total_tokens = int(total_tokens)
+    d.num_docs = int(num_docs)
+    d.num_q_heads = int(num_q_heads)
+    d.num_kv_heads = int(num_kv_heads)
+    d.head_dim = int(head_dim)
+    d.dtype = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    d.max_seqlen = int(max_seqlen)
+    d.reserved = 0
+    d.rms_eps = float(rms_eps)
+    d.rope_theta = float(rope_theta)
+    d.softmax_scale = float(softmax_scale or 0.0)
+    if workspace is not None:
+        d.workspace = workspace.data_ptr()
+        d.workspace_bytes = workspace.numel() * workspace.element_size()
+    return d
+
+
+def workspace_bytes(desc: SinkAttnDesc) -> int:
+    return int(load_library().sink_attn_workspace_bytes(ctypes.byref(desc)))
+
+
+def _check_tensor(name, t, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Call:
+    """Marshalled arguments of one forward call (shared by the three entry points)."""
+
+    def __init__(self, q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope,
+                 out=None, lse=None, *, rms_eps=1e-6, rope_theta=1e6, softmax_scale=None,
+                 workspace=None, stream=None, return_lse=True):
+        if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+            raise ValueError("q, k, v must be THD tensors [tokens, heads, head_dim]")
+        dev = q.device
+        T, Hq, d = q.shape
+        Hkv = k.shape[1]
+        if k.shape != (T, Hkv, d) or v.shape != k.shape:
+            raise ValueError("k and v must be [T, Hkv, head_dim] with q's T and head_dim")
+        if q.dtype not in _DTYPES:
+            raise ValueError(f"unsupported dtype {q.dtype}")
+        for name, t in (("k", k), ("v", v)):
+            _check_tensor(name, t, q.dtype, dev)
+        _check_tensor("cu_seqlens", cu_seqlens, torch.int32, dev)
+        for name, t in (("sinks", sinks), ("qnorm_w", qnorm_w), ("knorm_w", knorm_w)):
+            _check_tensor(name, t, torch.float32, dev)
+        self.desc = make_desc(T, cu_seqlens.numel() - 1, Hq, Hkv, d, q.dtype, rms_eps,
+                              rope_theta, softmax_scale or 0.0)
+        need = workspace_bytes(self.desc)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if workspace is not None:
+            self.desc.workspace = workspace.data_ptr()
+            self.desc.workspace_bytes = workspace.numel() * workspace.element_size()
+        if out is None:
+            out = torch.empty_like(q)
+        else:
+            _check_tensor("out", out, q.dtype, dev)
+        if lse is None and return_lse:
+            lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+        elif lse is not None:
+            _check_tensor("lse", lse, torch.float32, dev)
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        elif isinstance(stream, torch.cuda.Stream):
+            stream = stream.cuda_stream
+        self.q, self.k, self.v, self.cu = q, k, v, cu_seqlens
+        self.sinks, self.qnorm_w, self.knorm_w = sinks, qnorm_w, knorm_w
+        self.window, self.use_rope = int(window), int(bool(use_rope))
+        self.out, self.lse, self.workspace = out, lse, workspace
+        self.stream = ctypes.c_void_p(stream)
+
+    def fwd(self):
+        rc = load_library().sink_attn_fwd(
+            ctypes.byref(self.desc), _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.cu),
+            _ptr(self.sinks), _ptr(self.qnorm_w), _ptr(self.knorm_w), self.window,
+            self.use_rope, _ptr(self.out), _ptr(self.lse), self.stream)
+        if rc:
+            raise SinkAttnError(rc, "sink_attn_fwd")
+
+    def prologue(self):
+        rc = load_library().sink_attn_prologue(
+            ctypes.byref(self.desc), _ptr(self.k), _ptr(self.v), _ptr(self.cu),
+            _ptr(self.knorm_w), self.use_rope, self.stream)
+        if rc:
+            raise SinkAttnError(rc, "sink_attn_prologue")
+
+    def attention(self):
+        rc = load_library().sink_attn_attention(
+            ctypes.byref(self.desc), _ptr(self.q), _ptr(self.cu), _ptr(self.sinks),
+            _ptr(self.qnorm_w), self.window, self.use_rope, _ptr(self.out), _ptr(self.lse),
+            self.stream)
+        if rc:
+            raise SinkAttnError(rc, "sink_attn_attention")
+
+
+def sink_attn_fwd(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope,
+                  out=None, lse=None, **kw):
+    """Forward pass on the current stream.  Returns (out, lse); lse is None
+    when return_lse=False and no lse buffer is given."""
+    c = Call(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope, out, lse, **kw)
+    c.fwd()
+    return c.out, c.lse
+
+
+def sink_attn_prologue(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope,
+                       **kw) -> Call:
+    """Run the first stage; returns the Call whose .attention() runs the second."""
+    c = Call(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope, **kw)
+    c.prologue()
+    return c
+
+
+def sink_attn_workspace_bytes(total_tokens, num_docs, num_q_heads, num_kv_heads, head_dim,
+                              dtype=torch.bfloat16) -> int:
+    return workspace_bytes(make_desc(total_tokens, num_docs, num_q_heads, num_kv_heads,
+                                     head_dim, dtype))

@@ -1,0 +1,297 @@
+// attn_bf16.hip -- sink-aware GQA attention forward, bf16 in/out, gfx950 MFMA.
+//
+// Computes, for every (token t, query head h) of a packed THD batch
+//   out = sum_{j visible} exp(s_j - M) v_j / (exp(sink_h - M) + sum_j exp(s_j - M))
+//   lse = M + log(denominator)
+// with s_j = scale * <q_hat, k_hat_j> (flint.layers FlintAttention.forward: causal
+// attention with a zero-value sink category; _FlintSinkParameters: unscaled fp32
+// logits), keys j <= t of the same document and, for a window W > 0,
+// t - W < j (flint.config: the window counts the current token).
+//
+// Workgroup = 4 waves = one query block of one kv head g: tokens
+// [a, a + 128/G) of one document, times the G query heads that read kv head g.
+// Each wave owns 32 (token, head) columns.  RMSNorm and RoPE of the wave's
+// queries are done once at the start, in fp32, straight into bf16 MFMA
+// operands.  The key loop walks 64-key tiles of k_hat and V^T (written by the
+// prologue) through LDS, shared by all 4 waves, i.e. by the 8 query heads of
+// the group at 4 tokens per wave.  Per tile and wave:
+//   S^T[key][col] = K Q^T      2 x 8 v_mfma_f32_32x32x16_bf16
+//   online softmax in the log2 domain, the sink seeding the running max and
+//   denominator; band masks only on tiles that cross a document, causal or
+//   window edge; tiles outside the band are never visited
+//   O^T[d][col] += V^T P^T     16 v_mfma_f32_32x32x16_bf16 (P rounded to bf16)
+// MFMA operand layouts (32x32x16, wave64): A lane l holds A[l%32][8(l/32)..+7],
+// B lane l holds B[8(l/32)..+7][l%32], and accumulator register r of lane l is
+// C[8(r/4) + 4(l/32) + r%4][l%32].  With S^T in that layout a lane holds 16 keys
+// of one query column, so a column's max needs a single exchange with lane l^32
+// and every O^T entry of a lane belongs to one column.
+#include "sa_device.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kThreads = kWaves * 64;
+constexpr int kKPitch = kHeadDim + 8;   // bf16 per K row in LDS (272 B: 16-B aligned, rows shift banks)
+constexpr int kVPitch = kKeyTile + 8;   // bf16 per V^T row in LDS (144 B)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ khat,
+    const bf16* __restrict__ vt, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ sched, const float* __restrict__ sinks,
+    const float* __restrict__ qnorm_w, bf16* __restrict__ out, float* __restrict__ lse,
+    int T, int Hq, int Hkv, int G, int log2G, int64_t t_pad, int window, int use_rope,
+    float eps, double theta, float c_log2, int xcd_per) {
+  // ---- work item: blocks of one kv head stay on one pair of XCDs ----------
+  const int bid = blockIdx.x;
+  int g, item;
+  if (xcd_per > 0) {
+    const int xcd = bid & 7;
+    g = xcd / xcd_per;
+    item = (bid >> 3) * xcd_per + (xcd - g * xcd_per);
+  } else {
+    g = bid % Hkv;
+    item = bid / Hkv;
+  }
+  const int n_items = sched[0];
+  if (item >= n_items) return;
+  const int2 it = reinterpret_cast<const int2*>(sched + 4)[item];
+  const int doc = it.x;
+  const int doc_start = max(cu[doc], 0);
+  const int doc_end = min(cu[doc + 1], T);
+  const int m_tok = (kWaves * kColsPerWave) >> log2G;
+  const int tpw = kColsPerWave >> log2G;  // tokens per wave
+  const int a = doc_start + it.y * m_tok;
+  const int a_end = min(a + m_tok, doc_end);
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, hf = lane >> 5;
+  const int tok = a + wave * tpw + (col >> log2G);
+  const int hq = g * G + (col & (G - 1));
+  const bool tok_ok = tok < a_end;
+  const int tw0 = a + wave * tpw;                 // this wave's tokens [tw0, tw1)
+  const int tw1 = min(tw0 + tpw, a_end);
+
+  __shared__ double s_invf[64];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[kKeyTile][kKPitch];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[kHeadDim][kVPitch];
+
+  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0);
+  __syncthreads();
+
+  // ---- Q: load, RMSNorm, RoPE, round to bf16 B operands --------------------
+  // lane holds channels 16kk + 8hf + e (kk < 8, e < 8) of its column; NeoX
+  // partners i and i + 64 (kk and kk + 4) sit in the same lane.
+  bf16x8 qf[8];
+  {
+    float x[64];
+    if (tok_ok) {
+      const bf16* qp = q + ((size_t)tok * Hq + hq) * kHeadDim + 8 * hf;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[8 * kk + e] = (float)v8[e];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) x[i] = 0.f;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
+    ss += __shfl_xor(ss, 32);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[8 * kk + e] *= inv * qnorm_w[16 * kk + 8 * hf + e];
+    if (use_rope && tok_ok) {
+      const int p = tok - doc_start;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float sn, cs;
+          rope_sincos(p, s_invf[16 * kk + 8 * hf + e], &sn, &cs);
+          const float x1 = x[8 * kk + e], x2 = x[8 * (kk + 4) + e];
+          x[8 * kk + e] = x1 * cs - x2 * sn;
+          x[8 * (kk + 4) + e] = x2 * cs + x1 * sn;
+        }
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[kk][e] = (bf16)x[8 * kk + e];
+  }
+
+  // ---- key range of the block: [lo, hi), visited in 64-aligned tiles ------
+  const int hi = a_end;
+  const int lo = window > 0 ? max(doc_start, a - window + 1) : doc_start;
+  const int wlo = window > 0 ? max(doc_start, tw0 - window + 1) : doc_start;
+
+  const bf16* kbase = khat + (size_t)g * t_pad * kHeadDim;
+  const bf16* vbase = vt + (size_t)g * kHeadDim * t_pad;
+  uint4 kreg[4], vreg[4];
+  auto load_tile = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + kThreads * i;
+      kreg[i] = *reinterpret_cast<const uint4*>(kbase + (size_t)(kt + (c >> 4)) * kHeadDim + (c & 15) * 8);
+      vreg[i] = *reinterpret_cast<const uint4*>(vbase + (size_t)(c >> 3) * t_pad + kt + (c & 7) * 8);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + kThreads * i;
+      *reinterpret_cast<uint4*>(&Ks[c >> 4][(c & 15) * 8]) = kreg[i];
+      *reinterpret_cast<uint4*>(&Vs[c >> 3][(c & 7) * 8]) = vreg[i];
+    }
+  };
+
+  // running state in the log2 domain: m = max(sink, scores) * log2(e) scaled,
+  // l = partial denominator of this lane's keys (the sink's 1 in half 0 only)
+  float m_run = sinks[hq] * kLog2e;
+  float l_part = hf == 0 ? 1.f : 0.f;
+  f32x16 o[4];
+#pragma unroll
+  for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dd][r] = 0.f;
+
+  const int kt_lo = lo & ~(kKeyTile - 1);
+  if (kt_lo < hi) load_tile(kt_lo);
+  for (int kt = kt_lo; kt < hi; kt += kKeyTile) {
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (kt + kKeyTile < hi) load_tile(kt + kKeyTile);
+
+    const bool wave_active = (tw0 < tw1) && (kt < tw1) && (kt + kKeyTile > wlo);
+    if (!wave_active) continue;
+
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[kb * 32 + col][16 * kk + 8 * hf]);
+        s[kb] = mfma32(ka, qf[kk], s[kb]);
+      }
+    }
+
+    // every key of the tile visible to every token of the wave?
+    const bool full = kt >= doc_start && kt + kKeyTile - 1 <= tw0 &&
+                      (window < 0 || kt > tw1 - 1 - window);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float val = s[kb][r] * c_log2;
+        if (!full) {
+          const int u = kt + kb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+          const bool vis = tok_ok && u >= doc_start && u <= tok && (window < 0 || u > tok - window);
+          val = vis ? val : -INFINITY;
+        }
+        s[kb][r] = val;
+        mx = fmaxf(mx, val);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(s[kb][r] - m_use);
+        s[kb][r] = p;
+        psum += p;
+      }
+    l_part = l_part * alpha + psum;
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dd][r] *= alpha;
+
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        // B operand: k-slot 8hf + e <-> key kb*32 + 16st + 8(e/4) + 4hf + e%4
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (bf16)s[kb][8 * st + e];
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) {
+          const bf16* vrow = &Vs[32 * dd + col][kb * 32 + 16 * st + 4 * hf];
+          const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vrow);
+          const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vrow + 8);
+          const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[dd] = mfma32(va, pb, o[dd]);
+        }
+      }
+  }
+
+  // ---- epilogue: out = O / l in bf16, lse = ln2 * (m + log2 l) -------------
+  const float l = l_part + __shfl_xor(l_part, 32);
+  if (tok_ok) {
+    const float inv_l = 1.0f / l;
+    bf16* op = out + ((size_t)tok * Hq + hq) * kHeadDim + 4 * hf;
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[dd][4 * rq + e] * inv_l);
+        *reinterpret_cast<bf16x4*>(op + 32 * dd + 8 * rq) = w;
+      }
+    if (lse != nullptr && hf == 0) lse[(size_t)hq * T + tok] = (m_run + __log2f(l)) * kLn2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention_bf16(const bf16* q, const bf16* khat, const bf16* vt,
+                                 const int32_t* cu, const int32_t* sched,
+                                 const float* sinks, const float* qnorm_w, bf16* out,
+                                 float* lse, int T, int D, int Hq, int Hkv,
+                                 int64_t t_pad, int64_t items_ub, int window,
+                                 int use_rope, double eps, double theta,
+                                 double scale, hipStream_t stream) {
+  const int G = Hq / Hkv;
+  int log2G = 0;
+  while ((1 << log2G) < G) ++log2G;
+  // XCD-aware order: when Hkv divides the 8 XCDs, kv head g runs on XCDs
+  // [g * 8/Hkv, (g+1) * 8/Hkv) so the blocks streaming one head's keys share L2.
+  int xcd_per = 0;
+  int64_t grid;
+  if (Hkv <= 8 && 8 % Hkv == 0) {
+    xcd_per = 8 / Hkv;
+    grid = 8 * ((items_ub + xcd_per - 1) / xcd_per);
+  } else {
+    grid = items_ub * Hkv;
+  }
+  if (grid <= 0) return hipSuccess;
+  const float c_log2 = (float)(scale * 1.4426950408889634);
+  attn_fwd_bf16_kernel<<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+      q, khat, vt, cu, sched, sinks, qnorm_w, out, lse, T, Hq, Hkv, G, log2G, t_pad,
+      window, use_rope, (float)eps, theta, c_log2, xcd_per);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,250 @@
+// prologue.hip -- first stage of the forward pass.
+//
+// bf16 path, one launch:
+//   * block 0 builds the varlen work schedule from cu_seqlens: the number of
+//     query blocks of every document, their exclusive prefix, and the table of
+//     (document, block) items the attention grid walks, longest-running
+//     (highest position) blocks first.
+//   * every other block takes 64 consecutive tokens of one kv head and
+//       - applies per-head RMSNorm and, when enabled, NeoX RoPE to K
+//         (flint.layers FlintAttention: q_norm / k_norm, _apply_rope; positions
+//         are document-local), writing k_hat bf16 [Hkv][t_pad][128];
+//       - copies V transposed to [Hkv][128][t_pad] so the PV product reads
+//         keys contiguously from LDS.
+//     Padding keys [T, t_pad) are written as zeros.
+// fp32 debug path: RMSNorm (+RoPE) of K into k_hat fp32 [T][Hkv][d], and a
+// copy of V beside it, so the attention stage reads only the workspace.
+#include "sa_device.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kLdsPrefix = 4096;  // documents whose prefix fits in LDS
+
+// Varlen schedule.  sched[0] = number of items; items (int2 at sched + 4) hold
+// (document, block index in document) in descending order of block position.
+// prefix_g is global scratch of D + 1 ints used when D + 1 > kLdsPrefix.
+__device__ void build_schedule(const int32_t* __restrict__ cu, int D, int m_tok,
+                               int32_t* __restrict__ sched, int64_t items_ub,
+                               int32_t* __restrict__ prefix_g) {
+  __shared__ int s_scan[kThreads];
+  __shared__ int s_pref[kLdsPrefix];
+  const int tid = threadIdx.x;
+  const bool in_lds = D + 1 <= kLdsPrefix;
+  int* pref = in_lds ? s_pref : prefix_g;
+  int running = 0;
+  for (int base = 0; base < D; base += kThreads) {
+    const int n = base + tid;
+    int cnt = 0;
+    if (n < D) {
+      const int len = cu[n + 1] - cu[n];
+      cnt = len > 0 ? (len + m_tok - 1) / m_tok : 0;
+    }
+    s_scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int add = tid >= off ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += add;
+      __syncthreads();
+    }
+    if (n < D) pref[n] = running + s_scan[tid] - cnt;
+    running += s_scan[kThreads - 1];
+    __syncthreads();
+  }
+  // A malformed cu_seqlens could ask for more items than the grid covers;
+  // never write past the table.
+  if (running > items_ub) running = (int)items_ub;
+  if (tid == 0) {
+    pref[D] = running;
+    sched[0] = running;
+  }
+  __threadfence_block();
+  __syncthreads();
+  int2* items = reinterpret_cast<int2*>(sched + 4);
+  for (int j = tid; j < running; j += kThreads) {
+    int lo = 0, hi = D - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pref[mid] <= j) lo = mid;
+      else hi = mid - 1;
+    }
+    items[running - 1 - j] = make_int2(lo, j - pref[lo]);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
+    const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const int32_t* __restrict__ cu, const float* __restrict__ knorm_w, int T, int D,
+    int Hkv, int64_t t_pad, int m_tok, float eps, double theta, int use_rope,
+    bf16* __restrict__ khat, bf16* __restrict__ vt, int32_t* __restrict__ sched,
+    int64_t items_ub, int32_t* __restrict__ prefix_g) {
+  if (blockIdx.x == 0) {
+    build_schedule(cu, D, m_tok, sched, items_ub, prefix_g);
+    return;
+  }
+  __shared__ double s_invf[64];
+  __shared__ __attribute__((aligned(16))) bf16 s_v[kKeyTile][kHeadDim + 8];
+
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x - 1;
+  const int tile = blk / Hkv;
+  const int g = blk - tile * Hkv;
+  const int t0 = tile * kKeyTile;
+
+  // inv_freq_i = theta^(-2i/128), i < 64: NeoX pairs channel i with i + 64
+  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0);
+
+  // V tile [64 tokens][128] into LDS
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + kThreads * i;
+    const int tt = c >> 4, cc = c & 15;
+    const int t = t0 + tt;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (t < T) val = *reinterpret_cast<const uint4*>(v + ((size_t)t * Hkv + g) * kHeadDim + cc * 8);
+    *reinterpret_cast<uint4*>(&s_v[tt][cc * 8]) = val;
+  }
+  __syncthreads();
+
+  // K rows: 8 lanes per token; lane c holds channels 8c..8c+7 and 64+8c..64+8c+7
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int tt = (tid >> 3) + 32 * it;
+    const int c = tid & 7;
+    const int t = t0 + tt;
+    float x[16];
+    if (t < T) {
+      const bf16* kp = k + ((size_t)t * Hkv + g) * kHeadDim;
+      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(kp + 8 * c);
+      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(kp + 64 + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = (float)lo[e];
+        x[8 + e] = (float)hi[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[e] = 0.f;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ss += x[e] * x[e];
+    ss += __shfl_xor(ss, 1, 8);
+    ss += __shfl_xor(ss, 2, 8);
+    ss += __shfl_xor(ss, 4, 8);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] *= inv * knorm_w[8 * c + e];
+      x[8 + e] *= inv * knorm_w[64 + 8 * c + e];
+    }
+    if (use_rope && t < T) {
+      const int p = t - cu[doc_of_token(cu, D, t)];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float sn, cs;
+        rope_sincos(p, s_invf[8 * c + e], &sn, &cs);
+        const float a = x[e], b = x[8 + e];
+        x[e] = a * cs - b * sn;
+        x[8 + e] = b * cs + a * sn;
+      }
+    }
+    bf16x8 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      lo[e] = (bf16)x[e];
+      hi[e] = (bf16)x[8 + e];
+    }
+    bf16* kh = khat + ((size_t)g * t_pad + t) * kHeadDim;
+    *reinterpret_cast<bf16x8*>(kh + 8 * c) = lo;
+    *reinterpret_cast<bf16x8*>(kh + 64 + 8 * c) = hi;
+  }
+
+  // V^T rows: lane (d, 8-token chunk) writes 16 contiguous bytes of row d
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pidx = tid + kThreads * i;
+    const int tc = pidx & 7, d = pidx >> 3;
+    bf16x8 col;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) col[e] = s_v[8 * tc + e][d];
+    *reinterpret_cast<bf16x8*>(vt + ((size_t)g * kHeadDim + d) * t_pad + t0 + 8 * tc) = col;
+  }
+}
+
+template <int HD>
+__global__ __launch_bounds__(kThreads) void prologue_f32_kernel(
+    const float* __restrict__ k, const float* __restrict__ v,
+    const int32_t* __restrict__ cu, const float* __restrict__ knorm_w, int T, int D,
+    int Hkv, float eps, double theta, int use_rope, float* __restrict__ khat,
+    float* __restrict__ vcopy) {
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (int64_t)T * Hkv) return;
+  const int t = (int)(idx / Hkv);
+  const float* kp = k + idx * HD;
+  float x[HD];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < HD; ++i) {
+    x[i] = kp[i];
+    ss += x[i] * x[i];
+  }
+  const float inv = 1.0f / sqrtf(ss * (1.0f / HD) + eps);
+#pragma unroll
+  for (int i = 0; i < HD; ++i) x[i] *= inv * knorm_w[i];
+  if (use_rope) {
+    const int p = t - cu[doc_of_token(cu, D, t)];
+    for (int i = 0; i < HD / 2; ++i) {
+      float sn, cs;
+      rope_sincos(p, pow(theta, -2.0 * i / HD), &sn, &cs);
+      const float a = x[i], b = x[i + HD / 2];
+      x[i] = a * cs - b * sn;
+      x[i + HD / 2] = b * cs + a * sn;
+    }
+  }
+  float* kh = khat + idx * HD;
+  const float* vp = v + idx * HD;
+  float* vc = vcopy + idx * HD;
+#pragma unroll
+  for (int i = 0; i < HD; ++i) {
+    kh[i] = x[i];
+    vc[i] = vp[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prologue_bf16(const bf16* k, const bf16* v, const int32_t* cu,
+                                const float* knorm_w, int T, int D, int Hkv,
+                                int64_t t_pad, int m_tok, double eps, double theta,
+                                int use_rope, bf16* khat, bf16* vt, int32_t* sched,
+                                hipStream_t stream) {
+  const int64_t n_tiles = t_pad / kKeyTile;
+  const int64_t items_ub = T / m_tok + D;
+  int32_t* prefix_g = sched + 4 + 2 * items_ub;
+  const int64_t grid = 1 + n_tiles * Hkv;
+  prologue_bf16_kernel<<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+      k, v, cu, knorm_w, T, D, Hkv, t_pad, m_tok, (float)eps, theta, use_rope, khat, vt,
+      sched, items_ub, prefix_g);
+  return hipGetLastError();
+}
+
+hipError_t launch_prologue_f32(const float* k, const float* v, const int32_t* cu,
+                               const float* knorm_w, int T, int D, int Hkv, int d,
+                               double eps, double theta, int use_rope, float* khat,
+                               float* vcopy, hipStream_t stream) {
+  const int64_t n = (int64_t)T * Hkv;
+  const unsigned grid = (unsigned)((n + kThreads - 1) / kThreads);
+  if (d == 128)
+    prologue_f32_kernel<128><<<grid, kThreads, 0, stream>>>(
+        k, v, cu, knorm_w, T, D, Hkv, (float)eps, theta, use_rope, khat, vcopy);
+  else
+    prologue_f32_kernel<64><<<grid, kThreads, 0, stream>>>(
+        k, v, cu, knorm_w, T, D, Hkv, (float)eps, theta, use_rope, khat, vcopy);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,69 @@
+// sa_internal.h -- types, constants and launch wrappers shared by the HIP
+// translation units of libsinkattn.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 128;     // head_dim of the bf16 MFMA path
+constexpr int kKeyTile = 64;      // keys per LDS tile; tiles start at multiples of 64
+constexpr int kWaves = 4;         // waves per attention workgroup
+constexpr int kColsPerWave = 32;  // (token, head) query columns per wave
+constexpr int kMaxGroup = 32;     // largest Hq / Hkv of the bf16 path
+
+// Query tokens one attention workgroup covers for a GQA group size G:
+// kWaves * 32 columns = tokens * G.
+inline int tokens_per_block(int G) { return kWaves * kColsPerWave / G; }
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Workspace carve-up (all offsets 256-byte aligned).
+struct Workspace {
+  int64_t t_pad = 0;        // keys padded to a multiple of kKeyTile
+  int64_t items_ub = 0;     // upper bound on (document, query block) items
+  size_t khat_off = 0;      // bf16: [Hkv][t_pad][128]; f32: [T][Hkv][d]
+  size_t vt_off = 0;        // bf16: V transposed [Hkv][128][t_pad]; f32: V copy [T][Hkv][d]
+  size_t sched_off = 0;     // int32 n_items, then int2 items[items_ub]
+  size_t total = 0;
+};
+
+Workspace plan_workspace(int64_t T, int64_t D, int Hq, int Hkv, int d, int dtype);
+
+// ---- launch wrappers (return hipGetLastError after the launches) ----------
+
+hipError_t launch_prologue_bf16(const bf16* k, const bf16* v, const int32_t* cu,
+                                const float* knorm_w, int T, int D, int Hkv,
+                                int64_t t_pad, int m_tok, double eps, double theta,
+                                int use_rope, bf16* khat, bf16* vt, int32_t* sched,
+                                hipStream_t stream);
+
+hipError_t launch_attention_bf16(const bf16* q, const bf16* khat, const bf16* vt,
+                                 const int32_t* cu, const int32_t* sched,
+                                 const float* sinks, const float* qnorm_w, bf16* out,
+                                 float* lse, int T, int D, int Hq, int Hkv,
+                                 int64_t t_pad, int64_t items_ub, int window,
+                                 int use_rope, double eps, double theta,
+                                 double scale, hipStream_t stream);
+
+hipError_t launch_prologue_f32(const float* k, const float* v, const int32_t* cu,
+                               const float* knorm_w, int T, int D, int Hkv, int d,
+                               double eps, double theta, int use_rope, float* khat,
+                               float* vcopy, hipStream_t stream);
+
+hipError_t launch_attention_f32(const float* q, const float* khat, const float* v,
+                                const int32_t* cu, const float* sinks,
+                                const float* qnorm_w, float* out, float* lse, int T,
+                                int D, int Hq, int Hkv, int d, int window, int use_rope,
+                                double eps, double theta, double scale,
+                                hipStream_t stream);
+
+}  // namespace sa

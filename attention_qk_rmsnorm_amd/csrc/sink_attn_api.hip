@@ -1,0 +1,224 @@
+// sink_attn_api.hip -- host side of the C ABI declared in include/sink_attn.h:
+// argument checks, workspace carve-up and kernel launches.  Every check runs
+// before the first HIP call, so a rejected call enqueues nothing (mirroring
+// flint.layers _validate_backend and attention.utils, which reject a backend
+// or layout they cannot consume instead of falling back).
+#include "sink_attn.h"
+
+#include <math.h>
+
+#include "sa_internal.h"
+
+namespace sa {
+
+Workspace plan_workspace(int64_t T, int64_t D, int Hq, int Hkv, int d, int dtype) {
+  Workspace w;
+  if (T <= 0) return w;
+  w.t_pad = round_up(T, kKeyTile);
+  size_t off = 0;
+  if (dtype == SINK_ATTN_BF16) {
+    const int G = Hq / Hkv;
+    w.items_ub = T / tokens_per_block(G) + D;
+    w.khat_off = off;
+    off += (size_t)Hkv * w.t_pad * kHeadDim * sizeof(bf16);
+    off = round_up(off, 256);
+    w.vt_off = off;
+    off += (size_t)Hkv * kHeadDim * w.t_pad * sizeof(bf16);
+    off = round_up(off, 256);
+    w.sched_off = off;
+    off += sizeof(int32_t) * (4 + 2 * w.items_ub + D + 1);
+  } else {
+    w.khat_off = off;
+    off += (size_t)T * Hkv * d * sizeof(float);
+    off = round_up(off, 256);
+    w.vt_off = off;
+    off += (size_t)T * Hkv * d * sizeof(float);
+  }
+  w.total = round_up(off, 256);
+  return w;
+}
+
+}  // namespace sa
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shape checks common to every entry point.
+int check_desc(const sink_attn_desc* d) {
+  if (d == nullptr) return SINK_ATTN_EINVAL;
+  if (d->total_tokens < 0 || d->num_docs < 0 || d->num_q_heads <= 0 ||
+      d->num_kv_heads <= 0 || d->head_dim <= 0 || d->max_seqlen < 0 || d->reserved != 0)
+    return SINK_ATTN_EINVAL;
+  if (d->num_q_heads % d->num_kv_heads != 0) return SINK_ATTN_EINVAL;
+  if (d->total_tokens > 0 && d->num_docs == 0) return SINK_ATTN_EINVAL;
+  if (d->total_tokens > INT32_MAX - 2 * sa::kKeyTile) return SINK_ATTN_EINVAL;
+  if (!(d->rms_eps >= 0.0) || !isfinite(d->rms_eps)) return SINK_ATTN_EINVAL;
+  if (!(d->rope_theta > 0.0) || !isfinite(d->rope_theta)) return SINK_ATTN_EINVAL;
+  if (!isfinite(d->softmax_scale)) return SINK_ATTN_EINVAL;
+  if (d->dtype == SINK_ATTN_BF16) {
+    if (d->head_dim != sa::kHeadDim) return SINK_ATTN_EUNSUPPORTED;
+    const int G = d->num_q_heads / d->num_kv_heads;
+    if (G > sa::kMaxGroup || (G & (G - 1)) != 0) return SINK_ATTN_EUNSUPPORTED;
+  } else if (d->dtype == SINK_ATTN_F32) {
+    if (d->head_dim != 64 && d->head_dim != 128) return SINK_ATTN_EUNSUPPORTED;
+  } else {
+    return SINK_ATTN_EUNSUPPORTED;
+  }
+  return SINK_ATTN_OK;
+}
+
+int check_workspace(const sink_attn_desc* d, const sa::Workspace& w) {
+  if (w.total == 0) return SINK_ATTN_OK;
+  if (d->workspace == nullptr || d->workspace_bytes < w.total) return SINK_ATTN_EWORKSPACE;
+  if (!aligned(d->workspace, 256)) return SINK_ATTN_EWORKSPACE;
+  return SINK_ATTN_OK;
+}
+
+uintptr_t io_align(const sink_attn_desc* d) { return d->dtype == SINK_ATTN_BF16 ? 16 : 4; }
+
+sa::Workspace plan(const sink_attn_desc* d) {
+  return sa::plan_workspace(d->total_tokens, d->num_docs, d->num_q_heads, d->num_kv_heads,
+                            d->head_dim, d->dtype);
+}
+
+double softmax_scale(const sink_attn_desc* d) {
+  return d->softmax_scale > 0.0 ? d->softmax_scale : 1.0 / sqrt((double)d->head_dim);
+}
+
+int check_prologue(const sink_attn_desc* d, const void* k, const void* v,
+                   const int32_t* cu, const float* knorm_w, int32_t use_rope) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (use_rope != 0 && use_rope != 1) return SINK_ATTN_EINVAL;
+  if (cu == nullptr || !aligned(cu, 4)) return SINK_ATTN_EINVAL;
+  if (d->total_tokens == 0) return SINK_ATTN_OK;
+  if (k == nullptr || v == nullptr || knorm_w == nullptr) return SINK_ATTN_EINVAL;
+  const uintptr_t al = io_align(d);
+  if (!aligned(k, al) || !aligned(v, al) || !aligned(knorm_w, 4)) return SINK_ATTN_EINVAL;
+  return check_workspace(d, plan(d));
+}
+
+int check_attention(const sink_attn_desc* d, const void* q, const int32_t* cu,
+                    const float* sinks, const float* qnorm_w, int32_t window,
+                    int32_t use_rope, const void* out, const float* lse) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (window == 0) return SINK_ATTN_EINVAL;
+  if (use_rope != 0 && use_rope != 1) return SINK_ATTN_EINVAL;
+  if (cu == nullptr || !aligned(cu, 4)) return SINK_ATTN_EINVAL;
+  if (d->total_tokens == 0) return SINK_ATTN_OK;
+  if (q == nullptr || sinks == nullptr || qnorm_w == nullptr || out == nullptr)
+    return SINK_ATTN_EINVAL;
+  const uintptr_t al = io_align(d);
+  if (!aligned(q, al) || !aligned(out, al) || !aligned(sinks, 4) || !aligned(qnorm_w, 4) ||
+      (lse != nullptr && !aligned(lse, 4)))
+    return SINK_ATTN_EINVAL;
+  return check_workspace(d, plan(d));
+}
+
+int launch_prologue(const sink_attn_desc* d, const void* k, const void* v,
+                    const int32_t* cu, const float* knorm_w, int32_t use_rope,
+                    hipStream_t stream) {
+  const sa::Workspace w = plan(d);
+  char* ws = static_cast<char*>(d->workspace);
+  hipError_t e;
+  if (d->dtype == SINK_ATTN_BF16) {
+    const int G = d->num_q_heads / d->num_kv_heads;
+    e = sa::launch_prologue_bf16(
+        static_cast<const sa::bf16*>(k), static_cast<const sa::bf16*>(v), cu, knorm_w,
+        d->total_tokens, d->num_docs, d->num_kv_heads, w.t_pad, sa::tokens_per_block(G),
+        d->rms_eps, d->rope_theta, use_rope, reinterpret_cast<sa::bf16*>(ws + w.khat_off),
+        reinterpret_cast<sa::bf16*>(ws + w.vt_off), reinterpret_cast<int32_t*>(ws + w.sched_off),
+        stream);
+  } else {
+    e = sa::launch_prologue_f32(static_cast<const float*>(k), static_cast<const float*>(v), cu,
+                                knorm_w, d->total_tokens, d->num_docs, d->num_kv_heads,
+                                d->head_dim, d->rms_eps, d->rope_theta, use_rope,
+                                reinterpret_cast<float*>(ws + w.khat_off),
+                                reinterpret_cast<float*>(ws + w.vt_off), stream);
+  }
+  return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;
+}
+
+int launch_attention(const sink_attn_desc* d, const void* q, const int32_t* cu, const float* sinks, const float* qnorm_w,
+                     int32_t window, int32_t use_rope, void* out, float* lse,
+                     hipStream_t stream) {
+  const sa::Workspace w = plan(d);
+  char* ws = static_cast<char*>(d->workspace);
+  hipError_t e;
+  if (d->dtype == SINK_ATTN_BF16) {
+    e = sa::launch_attention_bf16(
+        static_cast<const sa::bf16*>(q), reinterpret_cast<const sa::bf16*>(ws + w.khat_off),
+        reinterpret_cast<const sa::bf16*>(ws + w.vt_off),
+        cu, reinterpret_cast<const int32_t*>(ws + w.sched_off), sinks, qnorm_w,
+        static_cast<sa::bf16*>(out), lse, d->total_tokens, d->num_docs, d->num_q_heads,
+        d->num_kv_heads, w.t_pad, w.items_ub, window, use_rope, d->rms_eps, d->rope_theta,
+        softmax_scale(d), stream);
+  } else {
+    e = sa::launch_attention_f32(
+        static_cast<const float*>(q), reinterpret_cast<const float*>(ws + w.khat_off),
+        reinterpret_cast<const float*>(ws + w.vt_off), cu, sinks, qnorm_w, static_cast<float*>(out), lse,
+        d->total_tokens, d->num_docs, d->num_q_heads, d->num_kv_heads, d->head_dim, window,
+        use_rope, d->rms_eps, d->rope_theta, softmax_scale(d), stream);
+  }
+  return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sink_attn_workspace_bytes(const sink_attn_desc* desc) {
+  if (check_desc(desc) != SINK_ATTN_OK) return 0;
+  return plan(desc).total;
+}
+
+int sink_attn_prologue(const sink_attn_desc* desc, const void* k, const void* v,
+                       const int32_t* cu_seqlens, const float* knorm_w, int32_t use_rope,
+                       void* stream) {
+  const int rc = check_prologue(desc, k, v, cu_seqlens, knorm_w, use_rope);
+  if (rc != SINK_ATTN_OK || desc->total_tokens == 0) return rc;
+  return launch_prologue(desc, k, v, cu_seqlens, knorm_w, use_rope,
+                         static_cast<hipStream_t>(stream));
+}
+
+int sink_attn_attention(const sink_attn_desc* desc, const void* q,
+                        const int32_t* cu_seqlens, const float* sinks,
+                        const float* qnorm_w, int32_t window, int32_t use_rope, void* out,
+                        float* lse, void* stream) {
+  const int rc = check_attention(desc, q, cu_seqlens, sinks, qnorm_w, window, use_rope, out,
+                                 lse);
+  if (rc != SINK_ATTN_OK || desc->total_tokens == 0) return rc;
+  return launch_attention(desc, q, cu_seqlens, sinks, qnorm_w, window, use_rope, out,
+                          lse, static_cast<hipStream_t>(stream));
+}
+
+int sink_attn_fwd(const sink_attn_desc* desc, const void* q, const void* k, const void* v,
+                  const int32_t* cu_seqlens, const float* sinks, const float* qnorm_w,
+                  const float* knorm_w, int32_t window, int32_t use_rope, void* out,
+                  float* lse, void* stream) {
+  int rc = check_prologue(desc, k, v, cu_seqlens, knorm_w, use_rope);
+  if (rc != SINK_ATTN_OK) return rc;
+  rc = check_attention(desc, q, cu_seqlens, sinks, qnorm_w, window, use_rope, out, lse);
+  if (rc != SINK_ATTN_OK || desc->total_tokens == 0) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = launch_prologue(desc, k, v, cu_seqlens, knorm_w, use_rope, s);
+  if (rc != SINK_ATTN_OK) return rc;
+  return launch_attention(desc, q, cu_seqlens, sinks, qnorm_w, window, use_rope, out, lse, s);
+}
+
+const char* sink_attn_status_string(int status) {
+  switch (status) {
+    case SINK_ATTN_OK: return "success";
+    case SINK_ATTN_EINVAL: return "invalid argument";
+    case SINK_ATTN_EUNSUPPORTED: return "unsupported configuration";
+    case SINK_ATTN_EWORKSPACE: return "workspace missing, too small or misaligned";
+    case SINK_ATTN_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int sink_attn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,248 @@
+"""Benchmark of the sink-aware GQA attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full]
+
+A step is one sink_attn_fwd call (K prologue + varlen schedule, then attention
+with the fused Q prologue) over one synthetic batch already resident in HBM.
+The default workload is the full-causal layer: one document of 32768 tokens,
+32 query / 4 kv heads, head_dim 128, bf16, no RoPE, sinks N(0,1).
+
+Throughput counts visible score entries only:
+    N_vis = sum over documents of sum_{i < L} min(i + 1, W)   (W = inf when causal)
+    FLOP  = 4 * head_dim * Hq * N_vis      (QK^T and PV, 2 * head_dim each)
+and is reported in TFLOP/s for the whole step.  The printed JSON line also
+carries the roofline of the dominant kernel (the attention kernel, timed with
+HIP events on the stream it is launched on) against the bf16 dense MFMA peak,
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sink-attn fwd TFLOP/s (visible entries) + % bf16 MFMA peak, 32q/4kv d128, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+ATTN_SOURCE = os.path.join(ROOT, "attention_qk_rmsnorm_amd", "csrc", "attn_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_traffic.json")
+
+
+def visible_entries(lengths, window: int) -> int:
+    total = 0
+    for L in lengths:
+        L = int(L)
+        if window <= 0 or window >= L:
+            total += L * (L + 1) // 2
+        else:
+            total += window * (window + 1) // 2 + (L - window) * window
+    return total
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 PMC summary,
+    or None when it is missing, for another workload, or the kernel source has
+    changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload or t.get("source_sha256") != source_digest(ATTN_SOURCE):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, w, out_gpu, lse_gpu, target_seconds: float):
+    """The fp64 oracle as it stands, on an evenly spaced sample of query tokens
+    (all heads of each), sized to about target_seconds of host time."""
+    import oracle.oracle as O
+    k = inp["k"].double().numpy()
+    v = inp["v"].double().numpy()
+    common = dict(cu_seqlens=inp["cu_seqlens"].numpy(), sinks=inp["sinks"].double().numpy(),
+                  qnorm_w=inp["qnorm_w"].double().numpy(),
+                  knorm_w=inp["knorm_w"].double().numpy(), window=w.window,
+                  use_rope=w.use_rope, eps=w.rms_eps, theta=w.rope_theta)
+    T = w.total_tokens
+    cu = inp["cu_seqlens"].numpy()
+    pos = np.concatenate([np.arange(L) for L in w.lengths])
+
+    def vis_of(rows):
+        p = pos[rows].astype(np.int64) + 1
+        return int(np.minimum(p, w.window).sum() if w.window > 0 else p.sum())
+
+    def run(n):
+        rows = np.unique(np.linspace(0, T - 1, n).round().astype(np.int32))
+        q = inp["q"][rows].double().numpy()
+        t0 = time.perf_counter()
+        out, lse = O.sink_attn_fwd(q, k, v, rows=rows, **common)
+        return rows, out, lse, time.perf_counter() - t0
+
+    rows, _, _, dt = run(16)                     # calibration run (not reported)
+    rate = vis_of(rows) / max(dt, 1e-6)
+    per_row = vis_of(np.arange(T, dtype=np.int32)) / T
+    n = int(min(T, max(16, target_seconds * rate / per_row)))
+    rows, out, lse, dt = run(n)
+    n_vis = vis_of(rows)
+    flop = 4.0 * w.head_dim * w.num_q_heads * n_vis
+    got = out_gpu[rows].float().cpu().numpy()
+    err = np.abs(got - out)
+    lerr = np.abs(lse_gpu[:, rows].cpu().numpy() - lse)
+    del cu
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": O.max_threads(),
+        "kind": "oracle",
+        "sample": (f"{len(rows)} query tokens evenly spaced over the {T}-token batch, all "
+                   f"{w.num_q_heads} heads each ({n_vis} visible entries per head, "
+                   f"{flop:.3e} FLOP), fp64, {dt:.1f} s"),
+        "seconds": dt,
+        "parity_on_sample": {"out_max_abs": float(err.max()), "out_mean_abs": float(err.mean()),
+                             "lse_max_abs": float(lerr.max())},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="full",
+                    choices=["full", "sliding", "long", "mixed_sliding", "mixed_causal"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target host time of the oracle sample (0 skips the CPU baseline)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_qk_rmsnorm_amd as A
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
+
+    if not os.path.exists(A.library_path()):
+        from attention_qk_rmsnorm_amd.build import build
+        build()
+    A.load_library()
+
+    w = workloads.named_workloads()[args.workload]
+    inp = workloads.make_inputs(w, seed=0)
+    d_inp = {k: v.to(dev) for k, v in inp.items()}
+    torch.cuda.synchronize()
+    call = A.Call(d_inp["q"], d_inp["k"], d_inp["v"], d_inp["cu_seqlens"], d_inp["sinks"],
+                  d_inp["qnorm_w"], d_inp["knorm_w"], w.window, w.use_rope,
+                  rms_eps=w.rms_eps, rope_theta=w.rope_theta)
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        call.fwd()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, each bracketed by events around the two
+    # stages on the launch stream (the attention stage launches one kernel)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        call.prologue()
+        ev[i][1].record(stream)
+        call.attention()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_step = elapsed * 1e3 / args.steps
+    pro_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    n_vis = visible_entries(w.lengths, w.window)
+    flop = 4.0 * w.head_dim * w.num_q_heads * n_vis
+    value = flop / (ms_step * 1e-3) / 1e12
+    achieved = flop / (attn_ms * 1e-3) / 1e12
+    T = w.total_tokens
+    pro_bytes = T * w.num_kv_heads * w.head_dim * 2 * 4      # read K, V; write k_hat, V^T
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.description}",
+            "tokens": T, "docs": w.num_docs, "q_heads": w.num_q_heads,
+            "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "window": w.window,
+            "rope": w.use_rope, "visible_entries": n_vis, "flop_per_step": flop,
+            "parallelism": "single GPU",
+        },
+        "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_bf16_kernel",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": load_traffic(w.name),
+            "avg_launch_ms": attn_ms,
+        },
+        "kernels": {
+            "prologue_ms": pro_ms,
+            "prologue_GBps": pro_bytes / (pro_ms * 1e-3) / 1e9,
+            "prologue_frac_hbm": pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "attention_ms": attn_ms,
+        },
+    }
+    if args.cpu_seconds > 0:
+        call.fwd()
+        torch.cuda.synchronize()
+        result["cpu_baseline"] = cpu_baseline(inp, w, call.out, call.lse, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

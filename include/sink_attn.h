@@ -1,0 +1,137 @@
+/*
+ * sink_attn.h -- C ABI of the MI355X (gfx950) sink-aware grouped-query
+ * attention forward pass: per-head RMSNorm and NeoX RoPE on Q and K, then
+ * causal or sliding-window attention over packed variable-length documents
+ * with one learned fp32 sink logit per query head.
+ *
+ * Sources (NeMo AutoModel API reference pages):
+ *   "flint.layers"     FlintAttention: separate Q/K/V, per-head RMSNorm,
+ *                      selective NeoX RoPE (_apply_rope rotates corresponding
+ *                      channels of the two halves of each head), forward()
+ *                      computes causal attention with a zero-value sink
+ *                      category over document-local zero-based positions;
+ *                      _FlintSinkParameters: unscaled FP32 logits, one per
+ *                      query head, that enter only the softmax denominator.
+ *   "flint.config"     FlintConfig: head_dim 128, 32 query / 4 KV heads,
+ *                      rms_norm_eps 1e-6; full layers have no RoPE, sliding
+ *                      layers rotate all channels; the window counts the
+ *                      current token.
+ *   "attention.utils"  preprocess_args_and_kwargs_for_attn: THD tensors
+ *                      [tokens, heads, head_dim], K and V share a layout,
+ *                      int32 cu_seqlens [documents + 1], a positive left
+ *                      window counts visible keys including the current token
+ *                      and a negative one is unbounded; a layout that cannot
+ *                      be consumed is rejected with an error.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller, on the
+ *     device that owns `stream`.  The library never allocates, frees or
+ *     synchronises, never writes q, k or v, and keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns at once.  Buffers must stay alive until it completes.
+ *   - Arguments are checked on the host before any HIP call; a failed check
+ *     returns a negative status and enqueues nothing.  There is no fallback to
+ *     another path.
+ *   - Layouts are THD and contiguous: q and out [T, Hq, d]; k and v
+ *     [T, Hkv, d]; lse [Hq, T]; query head h reads kv head h / (Hq / Hkv).
+ *   - Document n holds tokens [cu_seqlens[n], cu_seqlens[n+1]); a token's
+ *     position is its index inside its document.  cu_seqlens must start at 0,
+ *     be non-decreasing and end at T (empty documents are allowed); this is
+ *     not checked on the device.
+ *   - Key j of a document is visible to query i of the same document iff
+ *     j <= i and, when window > 0, i - window < j.  window < 0 is unbounded
+ *     (causal); window == 0 is rejected.
+ *   - out = sum_j softmax weight * v_j where the softmax includes one extra
+ *     category per query head whose logit is sinks[h] (used as given, not
+ *     multiplied by softmax_scale) and whose value is zero.
+ *     lse[h, i] = log of the full denominator, sink included (natural log).
+ */
+#ifndef SINK_ATTN_H
+#define SINK_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SINK_ATTN_OK = 0,
+  SINK_ATTN_EINVAL = -1,        /* invalid argument: null pointer, bad size, window == 0 */
+  SINK_ATTN_EUNSUPPORTED = -2,  /* well-formed but not provided (head_dim, dtype, group) */
+  SINK_ATTN_EWORKSPACE = -3,    /* workspace missing or smaller than required */
+  SINK_ATTN_ELAUNCH = -4        /* a kernel launch failed (hipGetLastError) */
+} sink_attn_status;
+
+typedef enum {
+  SINK_ATTN_BF16 = 0,  /* q, k, v, out bf16; fp32 arithmetic and accumulation */
+  SINK_ATTN_F32 = 1    /* q, k, v, out fp32; fp32 arithmetic throughout (debug path) */
+} sink_attn_dtype;
+
+/* Shapes and settings of one call.  Plain data; the library keeps no pointer
+ * to it after a call returns. */
+typedef struct {
+  int32_t total_tokens;   /* T = cu_seqlens[num_docs] >= 0 */
+  int32_t num_docs;       /* D >= 0; cu_seqlens has D + 1 entries */
+  int32_t num_q_heads;    /* Hq > 0 */
+  int32_t num_kv_heads;   /* Hkv > 0, Hq % Hkv == 0 */
+  int32_t head_dim;       /* d: 128 (bf16 and fp32) or 64 (fp32 only) */
+  int32_t dtype;          /* sink_attn_dtype of q, k, v and out */
+  int32_t max_seqlen;     /* optional hint (0 = unknown); not needed, not trusted */
+  int32_t reserved;       /* must be 0 */
+  double rms_eps;         /* RMSNorm epsilon, added to mean(x^2); 1e-6 for Flint */
+  double rope_theta;      /* RoPE base; inv_freq_i = theta^(-2i/d) */
+  double softmax_scale;   /* <= 0 selects 1/sqrt(head_dim) */
+  void* workspace;        /* device scratch of >= sink_attn_workspace_bytes(desc) */
+  size_t workspace_bytes; /* bytes available at workspace (256-byte aligned) */
+} sink_attn_desc;
+
+/* Bytes of device workspace a call with this descriptor needs (0 when T == 0).
+ * Depends only on total_tokens, num_docs, num_kv_heads, head_dim and dtype.
+ * Returns 0 for a NULL or invalid descriptor. */
+size_t sink_attn_workspace_bytes(const sink_attn_desc* desc);
+
+/* The whole forward pass: normalised/rotated Q and K, band-limited attention
+ * with the sink, out and lse.  Equivalent to sink_attn_prologue followed by
+ * sink_attn_attention on the same stream.
+ *   q [T,Hq,d], k [T,Hkv,d], v [T,Hkv,d]   inputs in desc->dtype (16-byte aligned)
+ *   cu_seqlens  int32 [D+1]
+ *   sinks       fp32 [Hq], unscaled logits (finite, or -inf to disable a head's sink)
+ *   qnorm_w     fp32 [d], RMSNorm weight shared by all query heads
+ *   knorm_w     fp32 [d], RMSNorm weight shared by all kv heads
+ *   window      > 0 sliding window counting the current token, < 0 causal
+ *   use_rope    1: NeoX RoPE on Q and K at document positions; 0: none
+ *   out         [T,Hq,d] in desc->dtype (16-byte aligned), fully written
+ *   lse         fp32 [Hq,T] or NULL (not written) */
+int sink_attn_fwd(const sink_attn_desc* desc, const void* q, const void* k,
+                  const void* v, const int32_t* cu_seqlens, const float* sinks,
+                  const float* qnorm_w, const float* knorm_w, int32_t window,
+                  int32_t use_rope, void* out, float* lse, void* stream);
+
+/* First stage of sink_attn_fwd: RMSNorm (+ RoPE) of K into the workspace, the
+ * value layout the attention stage reads, and the varlen work schedule derived
+ * from cu_seqlens.  Writes only the workspace. */
+int sink_attn_prologue(const sink_attn_desc* desc, const void* k, const void* v,
+                       const int32_t* cu_seqlens, const float* knorm_w,
+                       int32_t use_rope, void* stream);
+
+/* Second stage of sink_attn_fwd: RMSNorm (+ RoPE) of Q fused with the
+ * attention itself.  Reads the workspace a preceding sink_attn_prologue with
+ * the same descriptor, k, v, cu_seqlens, knorm_w and use_rope filled. */
+int sink_attn_attention(const sink_attn_desc* desc, const void* q,
+                        const int32_t* cu_seqlens, const float* sinks,
+                        const float* qnorm_w, int32_t window, int32_t use_rope,
+                        void* out, float* lse, void* stream);
+
+/* Static text for a status code (never NULL). */
+const char* sink_attn_status_string(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int sink_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINK_ATTN_H */

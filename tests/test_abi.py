@@ -1,0 +1,179 @@
+"""The C ABI without a GPU: every declared symbol is exported, the workspace
+query is pure host arithmetic, and every invalid argument is rejected on the
+host with its status code before any HIP call (so these run on a CPU-only
+machine).  Rejecting what cannot be consumed, instead of falling back, follows
+flint.layers _validate_backend and attention.utils (ValueError on a layout a
+backend cannot consume)."""
+import ctypes
+
+import pytest
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
+
+
+@pytest.fixture(scope="module")
+def A():
+    import os
+    import attention_qk_rmsnorm_amd as A
+    if not os.path.exists(A.library_path()):
+        from attention_qk_rmsnorm_amd.build import build
+        build()
+    return A
+
+
+def test_every_declared_symbol_is_exported(A):
+    lib = A.load_library()
+    names = A.header_functions()
+    assert set(names) >= {"sink_attn_fwd", "sink_attn_workspace_bytes",
+                          "sink_attn_status_string", "sink_attn_prologue",
+                          "sink_attn_attention", "sink_attn_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_descriptor_layout_matches_header(A):
+    # 8 int32, 3 doubles, pointer, size_t
+    assert ctypes.sizeof(A.SinkAttnDesc) == 8 * 4 + 3 * 8 + 8 + 8
+    assert A.SinkAttnDesc.rms_eps.offset == 32
+    assert A.SinkAttnDesc.workspace.offset == 56
+
+
+def test_status_strings(A):
+    for code in (OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH, 12345):
+        s = A.status_string(code)
+        assert isinstance(s, str) and s
+    assert A.status_string(12345) == "unknown status"
+
+
+def _desc(A, T=256, D=2, Hq=32, Hkv=4, d=128, dtype=0, ws_bytes=None, **kw):
+    desc = A.make_desc(T, D, Hq, Hkv, d, dtype, **kw)
+    need = A.workspace_bytes(desc)
+    desc.workspace = 0x10000000 if need else None
+    desc.workspace_bytes = need if ws_bytes is None else ws_bytes
+    return desc
+
+
+def test_workspace_bytes(A):
+    assert A.sink_attn_workspace_bytes(0, 0, 32, 4, 128) == 0
+    a = A.sink_attn_workspace_bytes(1000, 3, 32, 4, 128)
+    b = A.sink_attn_workspace_bytes(100000, 3, 32, 4, 128)
+    assert 0 < a < b and a % 256 == 0 and b % 256 == 0
+    # k_hat + V^T for 4 kv heads over keys padded to 64 dominate
+    assert b >= 2 * 4 * 100032 * 128 * 2
+    assert A.sink_attn_workspace_bytes(128, 1, 4, 1, 64, A.SINK_ATTN_F32) > 0
+    assert A.load_library().sink_attn_workspace_bytes(None) == 0
+    assert A.sink_attn_workspace_bytes(100, 1, 32, 5, 128) == 0     # invalid: 32 % 5
+
+
+FAKE = 0x7f0000000000   # 256-byte aligned, never dereferenced: the checks fail first
+
+
+def _fwd(A, desc, window=-1, use_rope=0, q=FAKE, k=FAKE, v=FAKE, cu=FAKE, sinks=FAKE,
+         qw=FAKE, kw=FAKE, out=FAKE, lse=FAKE):
+    lib = A.load_library()
+    P = ctypes.c_void_p
+    return lib.sink_attn_fwd(ctypes.byref(desc) if desc is not None else None, P(q), P(k),
+                             P(v), P(cu), P(sinks), P(qw), P(kw), window, use_rope, P(out),
+                             P(lse), None)
+
+
+@pytest.mark.parametrize("case, expected", [
+    ("null_desc", EINVAL),
+    ("window_zero", EINVAL),
+    ("use_rope_two", EINVAL),
+    ("heads_not_divisible", EINVAL),
+    ("negative_tokens", EINVAL),
+    ("tokens_without_docs", EINVAL),
+    ("reserved_nonzero", EINVAL),
+    ("negative_eps", EINVAL),
+    ("theta_zero", EINVAL),
+    ("nan_scale", EINVAL),
+    ("null_q", EINVAL),
+    ("null_out", EINVAL),
+    ("null_cu", EINVAL),
+    ("null_sinks", EINVAL),
+    ("misaligned_q", EINVAL),
+    ("misaligned_out", EINVAL),
+    ("head_dim_96", EUNSUPPORTED),
+    ("bf16_head_dim_64", EUNSUPPORTED),
+    ("group_3", EUNSUPPORTED),
+    ("group_64", EUNSUPPORTED),
+    ("dtype_7", EUNSUPPORTED),
+    ("no_workspace", EWORKSPACE),
+    ("small_workspace", EWORKSPACE),
+    ("misaligned_workspace", EWORKSPACE),
+])
+def test_invalid_arguments_rejected_before_any_launch(A, case, expected):
+    kwargs = {}
+    desc = _desc(A)
+    if case == "null_desc":
+        desc = None
+    elif case == "window_zero":
+        kwargs["window"] = 0
+    elif case == "use_rope_two":
+        kwargs["use_rope"] = 2
+    elif case == "heads_not_divisible":
+        desc = _desc(A, Hq=30, Hkv=4, ws_bytes=1 << 30)
+    elif case == "negative_tokens":
+        desc = _desc(A, T=-5)
+    elif case == "tokens_without_docs":
+        desc = _desc(A, D=0, ws_bytes=1 << 30)
+    elif case == "reserved_nonzero":
+        desc.reserved = 1
+    elif case == "negative_eps":
+        desc.rms_eps = -1.0
+    elif case == "theta_zero":
+        desc.rope_theta = 0.0
+    elif case == "nan_scale":
+        desc.softmax_scale = float("nan")
+    elif case == "null_q":
+        kwargs["q"] = 0
+    elif case == "null_out":
+        kwargs["out"] = 0
+    elif case == "null_cu":
+        kwargs["cu"] = 0
+    elif case == "null_sinks":
+        kwargs["sinks"] = 0
+    elif case == "misaligned_q":
+        kwargs["q"] = FAKE + 2
+    elif case == "misaligned_out":
+        kwargs["out"] = FAKE + 8
+    elif case == "head_dim_96":
+        desc = _desc(A, d=96, ws_bytes=1 << 30)
+    elif case == "bf16_head_dim_64":
+        desc = _desc(A, d=64, ws_bytes=1 << 30)
+    elif case == "group_3":
+        desc = _desc(A, Hq=12, Hkv=4, ws_bytes=1 << 30)
+    elif case == "group_64":
+        desc = _desc(A, Hq=64, Hkv=1, ws_bytes=1 << 30)
+    elif case == "dtype_7":
+        desc = _desc(A, dtype=7, ws_bytes=1 << 30)
+    elif case == "no_workspace":
+        desc.workspace = None
+    elif case == "small_workspace":
+        desc.workspace_bytes -= 256
+    elif case == "misaligned_workspace":
+        desc.workspace = 0x10000000 + 128
+    assert _fwd(A, desc, **kwargs) == expected
+
+
+def test_stage_entry_points_validate_too(A):
+    lib = A.load_library()
+    P = ctypes.c_void_p
+    desc = _desc(A)
+    assert lib.sink_attn_attention(ctypes.byref(desc), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 0,
+                                   0, P(FAKE), P(FAKE), None) == EINVAL
+    assert lib.sink_attn_prologue(ctypes.byref(desc), P(FAKE), P(0), P(FAKE), P(FAKE), 0,
+                                  None) == EINVAL
+    small = _desc(A, ws_bytes=1024)
+    assert lib.sink_attn_prologue(ctypes.byref(small), P(FAKE), P(FAKE), P(FAKE), P(FAKE), 1,
+                                  None) == EWORKSPACE
+
+
+def test_empty_batch_is_a_no_op(A):
+    # T == 0: nothing to compute, nothing launched, no workspace needed
+    desc = _desc(A, T=0, D=0)
+    assert desc.workspace_bytes == 0
+    assert _fwd(A, desc, q=0, k=0, v=0, sinks=0, qw=0, kw=0, out=0, lse=0) == OK
+    desc = _desc(A, T=0, D=3)
+    assert _fwd(A, desc, q=0, k=0, v=0, sinks=0, qw=0, kw=0, out=0, lse=0) == OK
