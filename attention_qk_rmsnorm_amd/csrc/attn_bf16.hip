@@ -34,11 +34,38 @@ namespace {
 constexpr int kThreads = kWaves * 64;
 constexpr int kKPitch = kHeadDim + 8;   // bf16 per K row in LDS (272 B: 16-B aligned, rows shift banks)
 constexpr int kVPitch = kKeyTile + 8;   // bf16 per V^T row in LDS (144 B)
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// One 64-key tile of k_hat ([64][128], rows contiguous) and V^T ([128][64] out
+// of rows of length t_pad) into registers: 4 + 4 16-byte loads per thread.
+__device__ __forceinline__ void load_tile(const bf16* __restrict__ kbase,
+                                          const bf16* __restrict__ vbase, int64_t t_pad,
+                                          int kt, int tid, u32x4 (&kreg)[4],
+                                          u32x4 (&vreg)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + kThreads * i;
+    kreg[i] = *reinterpret_cast<const u32x4*>(kbase + (size_t)(kt + (c >> 4)) * kHeadDim +
+                                              (c & 15) * 8);
+    vreg[i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)(c >> 3) * t_pad + kt +
+                                              (c & 7) * 8);
+  }
+}
+
+__device__ __forceinline__ void store_tile(bf16 (*Ks)[kKPitch], bf16 (*Vs)[kVPitch], int tid,
+                                           const u32x4 (&kreg)[4], const u32x4 (&vreg)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + kThreads * i;
+    *reinterpret_cast<u32x4*>(&Ks[c >> 4][(c & 15) * 8]) = kreg[i];
+    *reinterpret_cast<u32x4*>(&Vs[c >> 3][(c & 7) * 8]) = vreg[i];
+  }
 }
 
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
@@ -139,23 +166,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 
   const bf16* kbase = khat + (size_t)g * t_pad * kHeadDim;
   const bf16* vbase = vt + (size_t)g * kHeadDim * t_pad;
-  uint4 kreg[4], vreg[4];
-  auto load_tile = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i;
-      kreg[i] = *reinterpret_cast<const uint4*>(kbase + (size_t)(kt + (c >> 4)) * kHeadDim + (c & 15) * 8);
-      vreg[i] = *reinterpret_cast<const uint4*>(vbase + (size_t)(c >> 3) * t_pad + kt + (c & 7) * 8);
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kThreads * i;
-      *reinterpret_cast<uint4*>(&Ks[c >> 4][(c & 15) * 8]) = kreg[i];
-      *reinterpret_cast<uint4*>(&Vs[c >> 3][(c & 7) * 8]) = vreg[i];
-    }
-  };
+  u32x4 kreg[4], vreg[4];
 
   // running state in the log2 domain: m = max(sink, scores) * log2(e) scaled,
   // l = partial denominator of this lane's keys (the sink's 1 in half 0 only)
@@ -168,12 +179,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     for (int r = 0; r < 16; ++r) o[dd][r] = 0.f;
 
   const int kt_lo = lo & ~(kKeyTile - 1);
-  if (kt_lo < hi) load_tile(kt_lo);
+  if (kt_lo < hi) load_tile(kbase, vbase, t_pad, kt_lo, tid, kreg, vreg);
   for (int kt = kt_lo; kt < hi; kt += kKeyTile) {
     __syncthreads();
-    store_tile();
+    store_tile(Ks, Vs, tid, kreg, vreg);
     __syncthreads();
-    if (kt + kKeyTile < hi) load_tile(kt + kKeyTile);
+    // prefetch the next tile (the last iteration re-reads its own tile, which
+    // keeps the prefetch unconditional and the buffers in registers)
+    load_tile(kbase, vbase, t_pad, kt + kKeyTile < hi ? kt + kKeyTile : kt, tid, kreg, vreg);
 
     const bool wave_active = (tw0 < tw1) && (kt < tw1) && (kt + kKeyTile > wlo);
     if (!wave_active) continue;

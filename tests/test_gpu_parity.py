@@ -108,7 +108,8 @@ def test_bf16_window_at_least_length_equals_causal():
 
 def test_bf16_packed_equals_per_document():
     # key tiles start at multiples of 64 of the packed token index, so packing
-    # changes the order of partial sums: equal up to rounding, not bitwise
+    # changes how keys group into tiles, hence the running max each P is
+    # rounded to bf16 against: equal up to that rounding, not bitwise
     _say("case bf16 packed vs per-doc")
     lengths = [130, 7, 64, 300]
     inp = custom_inputs(lengths)
@@ -121,8 +122,8 @@ def test_bf16_packed_equals_per_document():
                    v=dev["v"][a:b].contiguous(),
                    cu_seqlens=torch.tensor([0, L], dtype=torch.int32, device="cuda"))
         o1, l1 = gpu_forward(one, 100, True)
-        x, y = out[a:b].float(), o1.float()
-        assert torch.all((x - y).abs() <= 2.0 ** -7 * torch.maximum(x.abs(), y.abs()) + 1e-6)
+        diff = (out[a:b].float() - o1.float()).abs()
+        assert diff.max().item() <= 1e-2 and diff.mean().item() <= 1e-3
         assert torch.allclose(lse[:, a:b], l1, rtol=0, atol=1e-5)
 
 
