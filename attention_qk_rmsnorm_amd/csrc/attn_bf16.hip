@@ -35,8 +35,10 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kKPitch = kHeadDim + 8;   // bf16 per K row in LDS (272 B: 16-B aligned, rows shift banks)
 constexpr int kVPitch = kKeyTile + 8;   // bf16 per V^T row in LDS (144 B)
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;  // log2-domain slack before the running max moves
 
 __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -107,10 +109,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int tw1 = min(tw0 + tpw, a_end);
 
   __shared__ double s_invf[64];
-  __shared__ __attribute__((aligned(16))) bf16 Ks[kKeyTile][kKPitch];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[kHeadDim][kVPitch];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][kKeyTile][kKPitch];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][kHeadDim][kVPitch];
 
-  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0);
+  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
   __syncthreads();
 
   // ---- Q: load, RMSNorm, RoPE, round to bf16 B operands --------------------
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float sn, cs;
-          rope_sincos(p, s_invf[16 * kk + 8 * hf + e], &sn, &cs);
+          rope_sincos_rev(p, s_invf[16 * kk + 8 * hf + e], &sn, &cs);
           const float x1 = x[8 * kk + e], x2 = x[8 * (kk + 4) + e];
           x[8 * kk + e] = x1 * cs - x2 * sn;
           x[8 * (kk + 4) + e] = x2 * cs + x1 * sn;
@@ -179,84 +181,105 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     for (int r = 0; r < 16; ++r) o[dd][r] = 0.f;
 
   const int kt_lo = lo & ~(kKeyTile - 1);
-  if (kt_lo < hi) load_tile(kbase, vbase, t_pad, kt_lo, tid, kreg, vreg);
+  if (kt_lo < hi) {
+    load_tile(kbase, vbase, t_pad, kt_lo, tid, kreg, vreg);
+    store_tile(Ks[0], Vs[0], tid, kreg, vreg);
+  }
+  __syncthreads();
+  int cur = 0;
   for (int kt = kt_lo; kt < hi; kt += kKeyTile) {
-    __syncthreads();
-    store_tile(Ks, Vs, tid, kreg, vreg);
-    __syncthreads();
-    // prefetch the next tile (the last iteration re-reads its own tile, which
-    // keeps the prefetch unconditional and the buffers in registers)
+    // prefetch the next tile into registers while this one is consumed from
+    // LDS (the last iteration re-reads its own tile, which keeps the prefetch
+    // unconditional and the buffers in registers)
     load_tile(kbase, vbase, t_pad, kt + kKeyTile < hi ? kt + kKeyTile : kt, tid, kreg, vreg);
 
     const bool wave_active = (tw0 < tw1) && (kt < tw1) && (kt + kKeyTile > wlo);
-    if (!wave_active) continue;
-
-    f32x16 s[2];
+    if (wave_active) {
+      const bf16(*Kc)[kKPitch] = Ks[cur];
+      const bf16(*Vc)[kVPitch] = Vs[cur];
+      f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[kb * 32 + col][16 * kk + 8 * hf]);
-        s[kb] = mfma32(ka, qf[kk], s[kb]);
+        for (int kk = 0; kk < 8; ++kk) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Kc[kb * 32 + col][16 * kk + 8 * hf]);
+          s[kb] = mfma32(ka, qf[kk], s[kb]);
+        }
       }
+
+      // band mask, only on tiles that cross a document, causal or window edge
+      const bool full = kt >= doc_start && kt + kKeyTile - 1 <= tw0 &&
+                        (window < 0 || kt > tw1 - 1 - window);
+      if (!full) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int u = kt + kb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
+            const bool vis =
+                tok_ok && u >= doc_start && u <= tok && (window < 0 || u > tok - window);
+            s[kb][r] = vis ? s[kb][r] : -INFINITY;
+          }
+      }
+      // column max of the raw scores (both lane halves hold keys of a column)
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_log2;
+
+      // Lazy rescale: the reference point m_run moves only when a score
+      // exceeds it by more than kLazy (log2 units), so weights stay <= 2^kLazy
+      // and the O / l rescale runs on the few tiles where the max jumps.  The
+      // result is the same softmax; lse uses the reference actually kept.
+      const bool grow = mx > m_run + kLazy;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        m_run = m_new;
+        l_part *= alpha;
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dd][r] *= alpha;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+
+      // P = exp2(s * scale * log2e - m) straight into bf16 B operands; the
+      // denominator sums the same bf16 weights the PV product uses.
+      const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          // B operand: k-slot 8hf + e <-> key kb*32 + 16st + 8(e/4) + 4hf + e%4
+          bf16x8 pb;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pb[e] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][8 * st + e], c_log2, -m_use));
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pr = {pb[e], pb[e + 1]};
+            l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_part, false);
+          }
+#pragma unroll
+          for (int dd = 0; dd < 4; ++dd) {
+            const bf16* vrow = &Vc[32 * dd + col][kb * 32 + 16 * st + 4 * hf];
+            const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vrow);
+            const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vrow + 8);
+            const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+            o[dd] = mfma32(va, pb, o[dd]);
+          }
+        }
     }
 
-    // every key of the tile visible to every token of the wave?
-    const bool full = kt >= doc_start && kt + kKeyTile - 1 <= tw0 &&
-                      (window < 0 || kt > tw1 - 1 - window);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float val = s[kb][r] * c_log2;
-        if (!full) {
-          const int u = kt + kb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-          const bool vis = tok_ok && u >= doc_start && u <= tok && (window < 0 || u > tok - window);
-          val = vis ? val : -INFINITY;
-        }
-        s[kb][r] = val;
-        mx = fmaxf(mx, val);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][r] - m_use);
-        s[kb][r] = p;
-        psum += p;
-      }
-    l_part = l_part * alpha + psum;
-#pragma unroll
-    for (int dd = 0; dd < 4; ++dd)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dd][r] *= alpha;
-
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        // B operand: k-slot 8hf + e <-> key kb*32 + 16st + 8(e/4) + 4hf + e%4
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (bf16)s[kb][8 * st + e];
-#pragma unroll
-        for (int dd = 0; dd < 4; ++dd) {
-          const bf16* vrow = &Vs[32 * dd + col][kb * 32 + 16 * st + 4 * hf];
-          const bf16x4 v0 = *reinterpret_cast<const bf16x4*>(vrow);
-          const bf16x4 v1 = *reinterpret_cast<const bf16x4*>(vrow + 8);
-          const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[dd] = mfma32(va, pb, o[dd]);
-        }
-      }
+    // the other buffer was last read before the previous barrier
+    store_tile(Ks[cur ^ 1], Vs[cur ^ 1], tid, kreg, vreg);
+    __syncthreads();
+    cur ^= 1;
   }
 
   // ---- epilogue: out = O / l in bf16, lse = ln2 * (m + log2 l) -------------

@@ -94,8 +94,9 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
   const int g = blk - tile * Hkv;
   const int t0 = tile * kKeyTile;
 
-  // inv_freq_i = theta^(-2i/128), i < 64: NeoX pairs channel i with i + 64
-  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0);
+  // inv_freq_i / 2pi with inv_freq_i = theta^(-2i/128), i < 64: NeoX pairs
+  // channel i with i + 64
+  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
 
   // V tile [64 tokens][128] into LDS
 #pragma unroll
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float sn, cs;
-        rope_sincos(p, s_invf[8 * c + e], &sn, &cs);
+        rope_sincos_rev(p, s_invf[8 * c + e], &sn, &cs);
         const float a = x[e], b = x[8 + e];
         x[e] = a * cs - b * sn;
         x[8 + e] = b * cs + a * sn;

@@ -30,4 +30,16 @@ __device__ inline void rope_sincos(int p, double inv_freq, float* s, float* c) {
   sincosf((float)ang, s, c);
 }
 
+// sin and cos of the RoPE angle for the bf16 paths: the angle is carried in
+// revolutions (p * inv_freq / 2pi), reduced to [-1/2, 1/2] in fp64, and fed
+// to v_sin_f32 / v_cos_f32, which take revolutions.  Their error (~1e-6) is far
+// below the bf16 rounding the rotated vector gets next.
+__device__ inline void rope_sincos_rev(int p, double inv_freq_rev, float* s, float* c) {
+  double r = (double)p * inv_freq_rev;
+  r -= rint(r);
+  const float rf = (float)r;
+  *s = __builtin_amdgcn_sinf(rf);
+  *c = __builtin_amdgcn_cosf(rf);
+}
+
 }  // namespace sa

@@ -19,6 +19,7 @@ constexpr int kKeyTile = 64;      // keys per LDS tile; tiles start at multiples
 constexpr int kWaves = 4;         // waves per attention workgroup
 constexpr int kColsPerWave = 32;  // (token, head) query columns per wave
 constexpr int kMaxGroup = 32;     // largest Hq / Hkv of the bf16 path
+constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
 
 // Query tokens one attention workgroup covers for a GQA group size G:
 // kWaves * 32 columns = tokens * G.

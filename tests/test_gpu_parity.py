@@ -109,7 +109,8 @@ def test_bf16_window_at_least_length_equals_causal():
 def test_bf16_packed_equals_per_document():
     # key tiles start at multiples of 64 of the packed token index, so packing
     # changes how keys group into tiles, hence the running max each P is
-    # rounded to bf16 against: equal up to that rounding, not bitwise
+    # rounded to bf16 against (the denominator sums those same bf16 weights):
+    # equal up to that rounding, not bitwise
     _say("case bf16 packed vs per-doc")
     lengths = [130, 7, 64, 300]
     inp = custom_inputs(lengths)
@@ -124,7 +125,7 @@ def test_bf16_packed_equals_per_document():
         o1, l1 = gpu_forward(one, 100, True)
         diff = (out[a:b].float() - o1.float()).abs()
         assert diff.max().item() <= 1e-2 and diff.mean().item() <= 1e-3
-        assert torch.allclose(lse[:, a:b], l1, rtol=0, atol=1e-5)
+        assert torch.allclose(lse[:, a:b], l1, rtol=0, atol=1e-3)
 
 
 def test_bf16_deterministic_and_fully_written():
