@@ -9,8 +9,9 @@
 //       - applies per-head RMSNorm and, when enabled, NeoX RoPE to K
 //         (flint.layers FlintAttention: q_norm / k_norm, _apply_rope; positions
 //         are document-local), writing k_hat bf16 [Hkv][t_pad][128];
-//       - copies V transposed to [Hkv][128][t_pad] so the PV product reads
-//         keys contiguously from LDS.
+//       - copies V transposed to [Hkv][128][t_pad] (keys permuted inside
+//         groups of 16, see below) so the PV product reads its operand with
+//         one 16-byte LDS load.
 //     Padding keys [T, t_pad) are written as zeros.
 // fp32 debug path: RMSNorm (+RoPE) of K into k_hat fp32 [T][Hkv][d], and a
 // copy of V beside it, so the attention stage reads only the workspace.
@@ -164,14 +165,18 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
     *reinterpret_cast<bf16x8*>(kh + 64 + 8 * c) = hi;
   }
 
-  // V^T rows: lane (d, 8-token chunk) writes 16 contiguous bytes of row d
+  // V^T rows: lane (d, 8-position chunk) writes 16 contiguous bytes of row d.
+  // Inside each group of 16 keys, position q holds key q with bits 2 and 3
+  // swapped (0-3, 8-11, 4-7, 12-15): the order in which the attention
+  // kernel's PV MFMA takes its A operand, so that operand is one 16-byte read.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int pidx = tid + kThreads * i;
     const int tc = pidx & 7, d = pidx >> 3;
+    const int kbase16 = 16 * (tc >> 1) + 4 * (tc & 1);
     bf16x8 col;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) col[e] = s_v[8 * tc + e][d];
+    for (int e = 0; e < 8; ++e) col[e] = s_v[kbase16 + 8 * (e >> 2) + (e & 3)][d];
     *reinterpret_cast<bf16x8*>(vt + ((size_t)g * kHeadDim + d) * t_pad + t0 + 8 * tc) = col;
   }
 }
