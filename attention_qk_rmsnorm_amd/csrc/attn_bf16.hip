@@ -48,30 +48,19 @@ __device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// LDS tile layouts.  One global_load_lds_dwordx4 writes 64 lanes x 16 B
-// contiguously, so rows cannot be padded; 16-byte chunks are XOR-swizzled
-// instead so the MFMA operand reads (32 lanes on 32 rows, one column) spread
-// over all banks (for a 32- or 64-bank LDS):
-//   k_hat tile: row r = key (256 B), chunk c stored at c ^ (r & 15)
-//   V^T tile:   row r = channel (128 B), chunk c stored at c ^ vswz(r)
-// vswz(r) = (r & 7) ^ ((r >> 3) & 1) keeps chunk positions distinct over any
-// 8 consecutive rows and the (row parity, chunk) pairs distinct over 16 rows.
-__device__ __forceinline__ int vswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-// Issue the direct-to-LDS copy of the 64-key tile at kt into buffer `buf`:
-// 4 + 4 16-byte loads per thread; chunk C = 256 i + tid lands at byte 16 C.
-__device__ __forceinline__ void issue_tile(const bf16* __restrict__ kbase,
-                                           const bf16* __restrict__ vbase, int64_t t_pad,
-                                           int kt, int tid, char* buf) {
-  char* wbase = buf + (tid >> 6) * 1024;
+// Copy the 64-key tile at kt into LDS buffer `buf`: the prologue wrote k_hat
+// and V^T as the exact LDS image (see sa_device.h), so this is a straight
+// 2 x 16 KiB copy by global_load_lds_dwordx4 -- chunk 256 i + tid of each
+// image lands at byte 16 (256 i + tid) -- with no VGPR staging.
+__device__ __forceinline__ void issue_tile(const char* __restrict__ ktile,
+                                           const char* __restrict__ vtile, int tid, int wave,
+                                           char* buf) {
+  char* wbase = buf + wave * 1024;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int C = kThreads * i + tid;
-    const int rk = C >> 4, ck = (C & 15) ^ (rk & 15);
-    __builtin_amdgcn_global_load_lds(kbase + (size_t)(kt + rk) * kHeadDim + ck * 8,
+    __builtin_amdgcn_global_load_lds(ktile + 4096 * i + 16 * tid,
                                      (lds_void*)(wbase + 4096 * i), 16, 0, 0);
-    const int rv = C >> 3, cv = (C & 7) ^ vswz(rv);
-    __builtin_amdgcn_global_load_lds(vbase + (size_t)rv * t_pad + kt + cv * 8,
+    __builtin_amdgcn_global_load_lds(vtile + 4096 * i + 16 * tid,
                                      (lds_void*)(wbase + kTileK + 4096 * i), 16, 0, 0);
   }
 }
@@ -85,48 +74,68 @@ struct ColState {
 };
 
 // One 64-key tile for one wave: S^T = K Q^T, masked online softmax with the
-// sink-seeded state, O^T += V^T P^T.  `buf` is the LDS buffer holding the tile.
+// sink-seeded state, O^T += V^T P^T.  LDS operand reads are issued one step
+// ahead of the MFMAs that consume them; sched_barrier keeps the compiler from
+// sinking them back next to their use.
 template <int BUF>
 __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8],
                                             const int (&voff)[4], ColState& st, int kt,
-                                            int col, int hf, int tok, bool tok_ok, int tw0,
-                                            int tw1, int doc_start, int window, float c_log2) {
-  const char* buf = lds + BUF * kBuf;
-  f32x16 s[2];
+                                            int hf, int tok, bool tok_ok, int tw0, int tw1,
+                                            int doc_start, int window, float c_log2) {
+  const char* kbuf = lds + BUF * kBuf;
+  const char* vbuf = kbuf + kTileK;
+  auto rd = [](const char* p) { return *reinterpret_cast<const bf16x8*>(p); };
+
+  // ---- S^T = K Q^T: two 32-key chains, K fragments one step ahead --------
+  f32x16 s0, s1;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = 0.f;
+    s1[r] = 0.f;
   }
+  bf16x8 a0 = rd(kbuf + koff[0]), a1 = rd(kbuf + 8192 + koff[0]);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(buf + kb * 32 * 256 + koff[kk]);
-      s[kb] = mfma32(ka, st.qf[kk], s[kb]);
+    bf16x8 n0 = a0, n1 = a1;
+    if (kk < 7) {
+      n0 = rd(kbuf + koff[kk + 1]);
+      n1 = rd(kbuf + 8192 + koff[kk + 1]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    s0 = mfma32(a0, st.qf[kk], s0);
+    s1 = mfma32(a1, st.qf[kk], s1);
+    a0 = n0;
+    a1 = n1;
   }
+  // V fragments of the first PV step, read while the softmax runs
+  bf16x8 va[4];
+#pragma unroll
+  for (int dd = 0; dd < 4; ++dd) va[dd] = rd(vbuf + dd * 4096 + voff[0]);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // band mask, only on tiles that cross a document, causal or window edge
+  // ---- band mask, only on tiles that cross a document, causal or window edge
   const bool full = kt >= doc_start && kt + kKeyTile - 1 <= tw0 &&
                     (window < 0 || kt > tw1 - 1 - window);
   if (!full) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int u = kt + kb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-        const bool vis = tok_ok && u >= doc_start && u <= tok && (window < 0 || u > tok - window);
-        s[kb][r] = vis ? s[kb][r] : -INFINITY;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int u0 = kt + (r >> 2) * 8 + hf * 4 + (r & 3);
+      const int u1 = u0 + 32;
+      const bool v0 = tok_ok && u0 >= doc_start && u0 <= tok && (window < 0 || u0 > tok - window);
+      const bool v1 = tok_ok && u1 >= doc_start && u1 <= tok && (window < 0 || u1 > tok - window);
+      // masked by adding -inf rather than selecting it: the sum is a
+      // canonical float, so the max below needs no canonicalising moves
+      s0[r] += v0 ? 0.f : -INFINITY;
+      s1[r] += v1 ? 0.f : -INFINITY;
+    }
   }
-  // column max of the raw scores (both lane halves hold keys of a column)
+  // column max of the raw scores (the lane pair l, l^32 holds one column)
   float mx = -INFINITY;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s0[r]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32)) * c_log2;
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
+  mx = lane_pair_max(mx) * c_log2;
 
   // Lazy rescale: the reference point m_run moves only when a score exceeds
   // it by more than kLazy (log2 units), so weights stay <= 2^kLazy and the
@@ -145,32 +154,43 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
   }
   const float m_use = st.m_run == -INFINITY ? 0.f : st.m_run;
 
-  // P = exp2(s * scale * log2e - m) straight into bf16 B operands; the
-  // denominator sums the same bf16 weights the PV product uses.
+  // ---- P = exp2(s * scale * log2e - m) into bf16 B operands; O^T += V^T P^T.
+  // Step j covers keys 16j..16j+15 (j = 2 kb + sp): B operand k-slot 8hf + e
+  // <-> key 16j + 8(e/4) + 4hf + e%4, which is the order the prologue stored
+  // V^T keys in, so the A operand is one 16-byte read.  The denominator sums
+  // the same bf16 weights the PV product uses.
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  auto weights = [&](int j) {
+    const f32x16& sv = (j < 2) ? s0 : s1;
+    const int base = 8 * (j & 1);
+    bf16x8 pb;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+    for (int e = 0; e < 8; ++e)
+      pb[e] = (bf16)__builtin_amdgcn_exp2f(fmaf(sv[base + e], c_log2, -m_use));
 #pragma unroll
-    for (int sp = 0; sp < 2; ++sp) {
-      // B operand: k-slot 8hf + e <-> key kb*32 + 16sp + 8(e/4) + 4hf + e%4;
-      // the prologue stored V^T keys in exactly this order inside each group
-      // of 16, so the A operand is one 16-byte read.
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        pb[e] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][8 * sp + e], c_log2, -m_use));
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const bf16x2 pr = {pb[e], pb[e + 1]};
-        st.l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, st.l_part, false);
-      }
-#pragma unroll
-      for (int dd = 0; dd < 4; ++dd) {
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(buf + kTileK + dd * 4096 +
-                                                           voff[2 * kb + sp]);
-        st.o[dd] = mfma32(va, pb, st.o[dd]);
-      }
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 pr = {pb[e], pb[e + 1]};
+      st.l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, st.l_part, false);
     }
+    return pb;
+  };
+  bf16x8 pb = weights(0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf16x8 vn[4];
+    if (j < 3) {
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd) vn[dd] = rd(vbuf + dd * 4096 + voff[j + 1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd) st.o[dd] = mfma32(va[dd], pb, st.o[dd]);
+    if (j < 3) {
+      pb = weights(j + 1);
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd) va[dd] = vn[dd];
+    }
+  }
 }
 
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
@@ -219,41 +239,50 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int lo = window > 0 ? max(doc_start, a - window + 1) : doc_start;
   const int wlo = window > 0 ? max(doc_start, tw0 - window + 1) : doc_start;
   const int kt_lo = lo & ~(kKeyTile - 1);
-  const bf16* kbase = khat + (size_t)g * t_pad * kHeadDim;
-  const bf16* vbase = vt + (size_t)g * kHeadDim * t_pad;
-  // the first tile's copy overlaps the Q prologue
-  if (kt_lo < hi) issue_tile(kbase, vbase, t_pad, kt_lo, tid, lds);
-
+  // byte images of this kv head's tiles: tile kt/64 at 16 KiB * (kt/64)
+  const char* kimg = reinterpret_cast<const char*>(khat + (size_t)g * t_pad * kHeadDim);
+  const char* vimg = reinterpret_cast<const char*>(vt + (size_t)g * t_pad * kHeadDim);
+  // wave index as a uniform value with a known range [0, 4): the range lets
+  // the compiler prove the next tile's LDS copy does not alias the buffer
+  // being read, so it does not wait for that copy before the reads
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave) & (kWaves - 1);
   if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
   __syncthreads();
 
   ColState st;
   // ---- Q: load, RMSNorm, RoPE, round to bf16 B operands --------------------
   // lane holds channels 16kk + 8hf + e (kk < 8, e < 8) of its column; NeoX
-  // partners i and i + 64 (kk and kk + 4) sit in the same lane.
+  // partners i and i + 64 (kk and kk + 4) sit in the same lane.  The global
+  // loads go out before the first tile's copy: vmcnt retires in order, so
+  // waiting for them then does not wait for the copy.
   {
-    float x[64];
-    if (tok_ok) {
-      const bf16* qp = q + ((size_t)tok * Hq + hq) * kHeadDim + 8 * hf;
+    bf16x8 qraw[8];
+    float w[64];
+    const bf16* qp = q + ((size_t)(tok_ok ? tok : a) * Hq + hq) * kHeadDim + 8 * hf;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+    for (int kk = 0; kk < 8; ++kk) {
+      qraw[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[8 * kk + e] = (float)v8[e];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 64; ++i) x[i] = 0.f;
+      for (int e = 0; e < 8; ++e) w[8 * kk + e] = qnorm_w[16 * kk + 8 * hf + e];
     }
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
-    ss += __shfl_xor(ss, 32);
-    const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
+    __builtin_amdgcn_sched_barrier(0);
+    // the first tile's copy overlaps the Q prologue
+    if (kt_lo < hi)
+      issue_tile(kimg + (size_t)kt_lo * 256, vimg + (size_t)kt_lo * 256, tid, wave_u, lds);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float x[64];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[8 * kk + e] *= inv * qnorm_w[16 * kk + 8 * hf + e];
+      for (int e = 0; e < 8; ++e) x[8 * kk + e] = tok_ok ? (float)qraw[kk][e] : 0.f;
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
+    ss = lane_pair_sum(ss);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] *= inv * w[i];
     if (use_rope && tok_ok) {
       const int p = tok - doc_start;
 #pragma unroll
@@ -285,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   // swizzled LDS byte offsets of this lane's operand reads inside a buffer
   int koff[8], voff[4];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) koff[kk] = col * 256 + (((2 * kk + hf) ^ (col & 15)) << 4);
+  for (int kk = 0; kk < 8; ++kk) koff[kk] = col * 256 + (((2 * kk + hf) ^ kswz(col)) << 4);
 #pragma unroll
   for (int j = 0; j < 4; ++j) voff[j] = col * 128 + (((2 * j + hf) ^ vswz(col)) << 4);
 
@@ -298,22 +327,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       // other buffer's readers (previous tile) are done too
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
-      if (kt + kKeyTile < hi) issue_tile(kbase, vbase, t_pad, kt + kKeyTile, tid, lds + (b ^ 1) * kBuf);
+      if (kt + kKeyTile < hi)
+        issue_tile(kimg + (size_t)(kt + kKeyTile) * 256, vimg + (size_t)(kt + kKeyTile) * 256, tid,
+                   wave_u, lds + (b ^ 1) * kBuf);
       const bool active = (tw0 < tw1) && (kt < tw1) && (kt + kKeyTile > wlo);
       if (active) {
         if (b == 0)
-          attend_tile<0>(lds, koff, voff, st, kt, col, hf, tok, tok_ok, tw0, tw1, doc_start,
-                         window, c_log2);
+          attend_tile<0>(lds, koff, voff, st, kt, hf, tok, tok_ok, tw0, tw1, doc_start, window,
+                         c_log2);
         else
-          attend_tile<1>(lds, koff, voff, st, kt, col, hf, tok, tok_ok, tw0, tw1, doc_start,
-                         window, c_log2);
+          attend_tile<1>(lds, koff, voff, st, kt, hf, tok, tok_ok, tw0, tw1, doc_start, window,
+                         c_log2);
       }
       kt += kKeyTile;
     }
   }
 
   // ---- epilogue: out = O / l in bf16, lse = ln2 * (m + log2 l) -------------
-  const float l = st.l_part + __shfl_xor(st.l_part, 32);
+  const float l = lane_pair_sum(st.l_part);
   if (tok_ok) {
     const float inv_l = 1.0f / l;
     bf16* op = out + ((size_t)tok * Hq + hq) * kHeadDim + 4 * hf;

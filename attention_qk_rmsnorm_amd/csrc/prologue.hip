@@ -5,13 +5,17 @@
 //     query blocks of every document, their exclusive prefix, and the table of
 //     (document, block) items the attention grid walks, longest-running
 //     (highest position) blocks first.
-//   * every other block takes 64 consecutive tokens of one kv head and
+//   * every other block takes 64 consecutive tokens (one key tile) of one kv
+//     head and
 //       - applies per-head RMSNorm and, when enabled, NeoX RoPE to K
 //         (flint.layers FlintAttention: q_norm / k_norm, _apply_rope; positions
 //         are document-local), writing k_hat bf16 [Hkv][t_pad][128];
-//       - copies V transposed to [Hkv][128][t_pad] (keys permuted inside
-//         groups of 16, see below) so the PV product reads its operand with
-//         one 16-byte LDS load.
+//       - writes V transposed, one [128][64] block per key tile (keys permuted
+//         inside groups of 16, see below) so the PV product reads its operand
+//         with one 16-byte LDS load.
+//     Both are written as the exact byte image the attention kernel keeps in
+//     LDS (16-byte chunks swizzled, see sa_device.h), so its tile copy is a
+//     straight 16 KiB memcpy.
 //     Padding keys [T, t_pad) are written as zeros.
 // fp32 debug path: RMSNorm (+RoPE) of K into k_hat fp32 [T][Hkv][d], and a
 // copy of V beside it, so the attention stage reads only the workspace.
@@ -160,9 +164,10 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
       lo[e] = (bf16)x[e];
       hi[e] = (bf16)x[8 + e];
     }
+    // row t of the tile image: chunk c at position c ^ kswz(t)
     bf16* kh = khat + ((size_t)g * t_pad + t) * kHeadDim;
-    *reinterpret_cast<bf16x8*>(kh + 8 * c) = lo;
-    *reinterpret_cast<bf16x8*>(kh + 64 + 8 * c) = hi;
+    *reinterpret_cast<bf16x8*>(kh + 8 * (c ^ kswz(t))) = lo;
+    *reinterpret_cast<bf16x8*>(kh + 8 * ((c + 8) ^ kswz(t))) = hi;
   }
 
   // V^T rows: lane (d, 8-position chunk) writes 16 contiguous bytes of row d.
@@ -177,7 +182,10 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
     bf16x8 col;
 #pragma unroll
     for (int e = 0; e < 8; ++e) col[e] = s_v[kbase16 + 8 * (e >> 2) + (e & 3)][d];
-    *reinterpret_cast<bf16x8*>(vt + ((size_t)g * kHeadDim + d) * t_pad + t0 + 8 * tc) = col;
+    // tile-major image: tile (g, tile) is 128 rows x 64 keys, chunk tc of
+    // row d at position tc ^ vswz(d)
+    bf16* vrow = vt + (((size_t)g * (t_pad / kKeyTile) + tile) * kHeadDim + d) * kKeyTile;
+    *reinterpret_cast<bf16x8*>(vrow + 8 * (tc ^ vswz(d))) = col;
   }
 }
 

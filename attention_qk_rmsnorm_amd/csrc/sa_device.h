@@ -42,4 +42,31 @@ __device__ inline void rope_sincos_rev(int p, double inv_freq_rev, float* s, flo
   *c = __builtin_amdgcn_cosf(rf);
 }
 
+// Layout of the key/value tiles the prologue writes and the attention kernel
+// copies verbatim into LDS (64 keys per tile, 16-byte chunks XOR-swizzled so
+// the MFMA operand reads, 32 lanes on 32 rows at one column, hit distinct
+// banks for a 32- or 64-bank LDS):
+//   k_hat tile: 64 rows (keys) x 256 B; chunk c (channels 8c..8c+7) of row r
+//               sits at chunk position c ^ kswz(r)
+//   V^T tile:   128 rows (channels) x 128 B; chunk c (8 keys) of row r sits at
+//               chunk position c ^ vswz(r)
+// vswz keeps positions distinct over any 8 consecutive rows and the pairs
+// (row parity, position) distinct over any 16.
+__device__ __forceinline__ int kswz(int r) { return r & 15; }
+__device__ __forceinline__ int vswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// max / sum of x over the lane pair (l, l ^ 32): v_permlane32_swap exchanges
+// the upper half of one operand with the lower half of the other, so with x
+// in both operands each lane ends up holding x[l] and x[l ^ 32].
+__device__ __forceinline__ float lane_pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float lane_pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 }  // namespace sa

@@ -1,0 +1,94 @@
+"""Properties of the generated gfx950 code that the kernels' performance and
+correctness rest on, checked on the CPU from hipcc's assembly output:
+
+* no scratch (private) memory in any kernel -- an early version staged the
+  key/value tiles through scratch and wrote ~40 GB per launch;
+* the attention kernel fits two waves per SIMD (<= 256 VGPRs);
+* no packed fp32 VALU instructions (v_pk_{add,mul,fma}_f32), which the build
+  disables;
+* in the attention kernel's key loop, the direct-to-LDS copy of the next tile
+  is not waited for (vmcnt) before the current tile's LDS reads: the only
+  vmcnt(0) waits sit right before the per-tile barrier.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    from attention_qk_rmsnorm_amd.build import CSRC, HIPCC_FLAGS, INCLUDE, sources
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    out = {}
+    d = tmp_path_factory.mktemp("asm")
+    flags = [f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")]
+    for src in sources():
+        name = os.path.basename(src)
+        dst = d / (name + ".s")
+        subprocess.run([hipcc, *flags, "-S", "--cuda-device-only", "-I", INCLUDE, "-I", CSRC,
+                        src, "-o", str(dst)], check=True, capture_output=True)
+        out[name] = dst.read_text()
+    return out
+
+
+def _kernels(text):
+    """(name, body) of every kernel in an assembly file."""
+    parts = re.split(r"^(_Z\S+):\s*;", text, flags=re.M)
+    return [(parts[i], parts[i + 1]) for i in range(1, len(parts) - 1, 2)]
+
+
+def test_no_scratch_in_bf16_kernels(asm):
+    # the fp32 debug kernels hold a whole head row per thread and may spill
+    for name, text in asm.items():
+        for kname, body in _kernels(text):
+            if "f32" in kname:
+                continue
+            sizes = re.findall(r"; ScratchSize: (\d+)", body)
+            assert sizes and all(int(x) == 0 for x in sizes), f"{kname} uses scratch: {sizes}"
+
+
+def test_attention_two_waves_per_simd(asm):
+    text = asm["attn_bf16.hip"]
+    vgprs = [int(x) for x in re.findall(r"; NumVgprs: (\d+)", text)]
+    assert vgprs and max(vgprs) <= 256, vgprs
+    occ = [int(x) for x in re.findall(r"; Occupancy: (\d+)", text)]
+    assert occ and min(occ) >= 2, occ
+
+
+def test_no_packed_fp32_valu(asm):
+    for name, text in asm.items():
+        assert not re.search(r"\bv_pk_(add|mul|fma)_f32\b", text), name
+
+
+def test_tile_copy_not_waited_before_reads(asm):
+    text = asm["attn_bf16.hip"]
+    lines = [l.strip() for l in text.splitlines()]
+    lds_dma = [i for i, l in enumerate(lines) if l.startswith("global_load_lds_dwordx4")]
+    assert lds_dma, "attention kernel copies tiles with global_load_lds_dwordx4"
+    # the in-loop copies follow the per-tile barrier; after each such group a
+    # vmcnt wait may only be the one right before the next barrier, never one
+    # ahead of an LDS read
+    groups = [i for j, i in enumerate(lds_dma) if j + 1 == len(lds_dma) or lds_dma[j + 1] - i > 8]
+    firsts = [i for j, i in enumerate(lds_dma) if j == 0 or i - lds_dma[j - 1] > 8]
+    in_loop = [last for first, last in zip(firsts, groups)
+               if any(l.startswith("s_barrier") for l in lines[max(0, first - 16):first])]
+    assert len(in_loop) >= 2, "expected the tile copies of both loop halves"
+    checked = 0
+    for i in in_loop:
+        pending_wait = None
+        for l in lines[i + 1:]:
+            if l.startswith("s_waitcnt") and "vmcnt" in l:
+                pending_wait = l
+            elif l.startswith("ds_read"):
+                assert pending_wait is None, f"vmcnt wait before the tile's LDS reads: {pending_wait}"
+                checked += 1
+                break
+            elif l.startswith("s_barrier") or l.startswith("s_endpgm"):
+                break
+    assert checked == len(in_loop)
