@@ -50,7 +50,9 @@ _lib = None
 
 
 def library_path() -> str:
-    return LIB_PATH
+    """The library this process loads: libsinkattn.so next to the package, or
+    another build of the same C ABI named by SINKATTN_LIBRARY."""
+    return os.environ.get("SINKATTN_LIBRARY") or LIB_PATH
 
 
 def load_library():
@@ -58,11 +60,12 @@ def load_library():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    path = library_path()
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{LIB_PATH} is missing: build it with attention_qk_rmsnorm_amd.build.build() "
+            f"{path} is missing: build it with attention_qk_rmsnorm_amd.build.build() "
             "(hipcc --offload-arch=gfx950); there is no fallback path")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I32 = ctypes.c_void_p, ctypes.c_int32
     DP = ctypes.POINTER(SinkAttnDesc)
     lib.sink_attn_workspace_bytes.argtypes = [DP]

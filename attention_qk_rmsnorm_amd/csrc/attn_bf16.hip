@@ -17,7 +17,10 @@
 // staging) into one of two buffers while the other is consumed; the tile is
 // shared by all 4 waves, i.e. by the 8 query heads of the group at 4 tokens
 // per wave.  Per tile and wave:
-//   S^T[key][col] = K Q^T      2 x 8 v_mfma_f32_32x32x16_bf16
+//   S^T[key][col] = K Q^T - m_ref   2 x (8 + 1) v_mfma_f32_32x32x16_bf16: Q is
+//   pre-scaled by scale * log2(e), and a ninth step with A = a column of ones
+//   and B = -m_ref subtracts the column's reference max inside the MFMA, so
+//   the weights need one v_exp_f32 each and no other VALU op
 //   online softmax in the log2 domain, the sink seeding the running max and
 //   denominator; band masks only on tiles that cross a document, causal or
 //   window edge; tiles outside the band are never visited
@@ -69,9 +72,21 @@ __device__ __forceinline__ void issue_tile(const char* __restrict__ ktile,
 struct ColState {
   bf16x8 qf[8];     // Q^T B operands, channels 16kk + 8hf .. +7
   f32x16 o[4];      // O^T accumulators, channels 32dd + ...
-  float m_run;      // reference max (log2 domain, scaled scores)
+  bf16x8 ones_a;    // A operand of the reference step: A[key][0] = 1
+  bf16x8 negm_b;    // B operand of the reference step: B[0][col] = -m_ref
+  float m_ref;      // reference max (log2 domain, bf16-representable, or -inf)
   float l_part;     // this lane's share of the denominator
 };
+
+// B operand that makes the reference MFMA step subtract m_ref from every
+// score of the column: lanes 0-31 hold k-slot 0 of their column.
+__device__ __forceinline__ bf16x8 neg_ref_operand(float m_ref, int hf) {
+  bf16x8 b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) b[e] = (bf16)0.f;
+  if (hf == 0 && m_ref != -INFINITY) b[0] = (bf16)(-m_ref);
+  return b;
+}
 
 // One 64-key tile for one wave: S^T = K Q^T, masked online softmax with the
 // sink-seeded state, O^T += V^T P^T.  LDS operand reads are issued one step
@@ -81,7 +96,7 @@ template <int BUF>
 __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8],
                                             const int (&voff)[4], ColState& st, int kt,
                                             int hf, int tok, bool tok_ok, int tw0, int tw1,
-                                            int doc_start, int window, float c_log2) {
+                                            int doc_start, int window) {
   const char* kbuf = lds + BUF * kBuf;
   const char* vbuf = kbuf + kTileK;
   auto rd = [](const char* p) { return *reinterpret_cast<const bf16x8*>(p); };
@@ -107,6 +122,10 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
     a0 = n0;
     a1 = n1;
   }
+  // reference step: every score of a column minus m_ref (exact: m_ref is a
+  // bf16 value), so the accumulators hold s * scale * log2e - m_ref
+  s0 = mfma32(st.ones_a, st.negm_b, s0);
+  s1 = mfma32(st.ones_a, st.negm_b, s1);
   // V fragments of the first PV step, read while the softmax runs
   bf16x8 va[4];
 #pragma unroll
@@ -135,24 +154,32 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
   for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s0[r]);
 #pragma unroll
   for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
-  mx = lane_pair_max(mx) * c_log2;
+  mx = lane_pair_max(mx);  // relative to the reference (or absolute while none)
 
   // Lazy rescale: the reference point m_run moves only when a score exceeds
   // it by more than kLazy (log2 units), so weights stay <= 2^kLazy and the
   // O / l rescale runs on the few tiles where the max jumps.  The result is
   // the same softmax; lse uses the reference actually kept.
-  const bool grow = mx > st.m_run + kLazy;
+  const bool no_ref = st.m_ref == -INFINITY;
+  const bool grow = no_ref ? mx > -INFINITY : mx > kLazy;
   if (__any(grow)) {
-    const float m_new = grow ? mx : st.m_run;
-    const float alpha = grow ? __builtin_amdgcn_exp2f(st.m_run - m_new) : 1.f;
-    st.m_run = m_new;
+    const float m_eff = no_ref ? 0.f : st.m_ref;         // what the step subtracted
+    const float m_new = grow ? (float)(bf16)(m_eff + mx) : st.m_ref;
+    const float delta = grow ? m_new - m_eff : 0.f;
+    const float alpha = grow ? (no_ref ? 0.f : __builtin_amdgcn_exp2f(st.m_ref - m_new)) : 1.f;
+    st.m_ref = m_new;
+    st.negm_b = neg_ref_operand(m_new, hf);
     st.l_part *= alpha;
 #pragma unroll
     for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.o[dd][r] *= alpha;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] -= delta;
+      s1[r] -= delta;
+    }
   }
-  const float m_use = st.m_run == -INFINITY ? 0.f : st.m_run;
 
   // ---- P = exp2(s * scale * log2e - m) into bf16 B operands; O^T += V^T P^T.
   // Step j covers keys 16j..16j+15 (j = 2 kb + sp): B operand k-slot 8hf + e
@@ -166,7 +193,7 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
     bf16x8 pb;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      pb[e] = (bf16)__builtin_amdgcn_exp2f(fmaf(sv[base + e], c_log2, -m_use));
+      pb[e] = (bf16)__builtin_amdgcn_exp2f(sv[base + e]);
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
       const bf16x2 pr = {pb[e], pb[e + 1]};
@@ -299,13 +326,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) st.qf[kk][e] = (bf16)x[8 * kk + e];
+      for (int e = 0; e < 8; ++e) st.qf[kk][e] = (bf16)(x[8 * kk + e] * c_log2);
   }
 
   // running state in the log2 domain: m = max(sink, scores) * log2(e) scaled,
   // l = partial denominator of this lane's keys (the sink's 1 in half 0 only)
-  st.m_run = sinks[hq] * kLog2e;
-  st.l_part = hf == 0 ? 1.f : 0.f;
+  {
+    const float sl = sinks[hq] * kLog2e;
+    st.m_ref = sl == -INFINITY ? -INFINITY : (float)(bf16)sl;
+    st.l_part = (hf == 0 && sl != -INFINITY) ? __builtin_amdgcn_exp2f(sl - st.m_ref) : 0.f;
+    st.negm_b = neg_ref_operand(st.m_ref, hf);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.ones_a[e] = (bf16)0.f;
+    if (hf == 0) st.ones_a[0] = (bf16)1.f;
+  }
 #pragma unroll
   for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
@@ -333,11 +367,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       const bool active = (tw0 < tw1) && (kt < tw1) && (kt + kKeyTile > wlo);
       if (active) {
         if (b == 0)
-          attend_tile<0>(lds, koff, voff, st, kt, hf, tok, tok_ok, tw0, tw1, doc_start, window,
-                         c_log2);
+          attend_tile<0>(lds, koff, voff, st, kt, hf, tok, tok_ok, tw0, tw1, doc_start, window);
         else
-          attend_tile<1>(lds, koff, voff, st, kt, hf, tok, tok_ok, tw0, tw1, doc_start, window,
-                         c_log2);
+          attend_tile<1>(lds, koff, voff, st, kt, hf, tok, tok_ok, tw0, tw1, doc_start, window);
       }
       kt += kKeyTile;
     }
@@ -357,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         for (int e = 0; e < 4; ++e) w[e] = (bf16)(st.o[dd][4 * rq + e] * inv_l);
         *reinterpret_cast<bf16x4*>(op + 32 * dd + 8 * rq) = w;
       }
-    if (lse != nullptr && hf == 0) lse[(size_t)hq * T + tok] = (st.m_run + __log2f(l)) * kLn2;
+    if (lse != nullptr && hf == 0) lse[(size_t)hq * T + tok] = (st.m_ref + __log2f(l)) * kLn2;
   }
 }
 

@@ -77,7 +77,7 @@ def test_tile_copy_not_waited_before_reads(asm):
     groups = [i for j, i in enumerate(lds_dma) if j + 1 == len(lds_dma) or lds_dma[j + 1] - i > 8]
     firsts = [i for j, i in enumerate(lds_dma) if j == 0 or i - lds_dma[j - 1] > 8]
     in_loop = [last for first, last in zip(firsts, groups)
-               if any(l.startswith("s_barrier") for l in lines[max(0, first - 16):first])]
+               if any(l.startswith("s_barrier") for l in lines[max(0, first - 48):first])]
     assert len(in_loop) >= 2, "expected the tile copies of both loop halves"
     checked = 0
     for i in in_loop:
