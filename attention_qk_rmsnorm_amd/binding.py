@@ -19,6 +19,11 @@ from .build import LIB_PATH
 SINK_ATTN_BF16 = 0
 SINK_ATTN_F32 = 1
 
+SINK_ATTN_TILE_AUTO = 0
+SINK_ATTN_TILE_NARROW = 1
+SINK_ATTN_TILE_WIDE = 2
+SINK_ATTN_TILE_WIDE_EXACT = 3
+
 _DTYPES = {torch.bfloat16: SINK_ATTN_BF16, torch.float32: SINK_ATTN_F32}
 
 
@@ -31,7 +36,7 @@ class SinkAttnDesc(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("max_seqlen", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("tile_config", ctypes.c_int32),
         ("rms_eps", ctypes.c_double),
         ("rope_theta", ctypes.c_double),
         ("softmax_scale", ctypes.c_double),
@@ -76,6 +81,8 @@ def load_library():
     lib.sink_attn_prologue.restype = ctypes.c_int
     lib.sink_attn_attention.argtypes = [DP, P, P, P, P, I32, I32, P, P, P]
     lib.sink_attn_attention.restype = ctypes.c_int
+    lib.sink_attn_tile_config.argtypes = [DP, I32]
+    lib.sink_attn_tile_config.restype = ctypes.c_int
     lib.sink_attn_status_string.argtypes = [ctypes.c_int]
     lib.sink_attn_status_string.restype = ctypes.c_char_p
     lib.sink_attn_version.argtypes = []
@@ -103,7 +110,7 @@ def _ptr(t):
 
 def make_desc(total_tokens, num_docs, num_q_heads, num_kv_heads, head_dim, dtype,
               rms_eps=1e-6, rope_theta=1e6, softmax_scale=0.0, workspace=None,
-              max_seqlen=0) -> SinkAttnDesc:
+              max_seqlen=0, tile_config=SINK_ATTN_TILE_AUTO) -> SinkAttnDesc:
     d = SinkAttnDesc()
     d.total_tokens = int(total_tokens)
     d.num_docs = int(num_docs)
@@ -112,7 +119,7 @@ def make_desc(total_tokens, num_docs, num_q_heads, num_kv_heads, head_dim, dtype
     d.head_dim = int(head_dim)
     d.dtype = _DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     d.max_seqlen = int(max_seqlen)
-    d.reserved = 0
+    d.tile_config = int(tile_config)
     d.rms_eps = float(rms_eps)
     d.rope_theta = float(rope_theta)
     d.softmax_scale = float(softmax_scale or 0.0)
@@ -124,6 +131,15 @@ def make_desc(total_tokens, num_docs, num_q_heads, num_kv_heads, head_dim, dtype
 
 def workspace_bytes(desc: SinkAttnDesc) -> int:
     return int(load_library().sink_attn_workspace_bytes(ctypes.byref(desc)))
+
+
+def tile_config(desc: SinkAttnDesc, window: int) -> int:
+    """The bf16 tile configuration the attention stage uses for this call
+    (SINK_ATTN_TILE_NARROW / _WIDE), 0 for fp32; raises on invalid input."""
+    rc = int(load_library().sink_attn_tile_config(ctypes.byref(desc), int(window)))
+    if rc < 0:
+        raise SinkAttnError(rc, "sink_attn_tile_config")
+    return rc
 
 
 def _check_tensor(name, t, dtype, device):
@@ -140,7 +156,7 @@ class Call:
 
     def __init__(self, q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope,
                  out=None, lse=None, *, rms_eps=1e-6, rope_theta=1e6, softmax_scale=None,
-                 workspace=None, stream=None, return_lse=True):
+                 workspace=None, stream=None, return_lse=True, tile_config=SINK_ATTN_TILE_AUTO):
         if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
             raise ValueError("q, k, v must be THD tensors [tokens, heads, head_dim]")
         dev = q.device
@@ -156,7 +172,7 @@ class Call:
         for name, t in (("sinks", sinks), ("qnorm_w", qnorm_w), ("knorm_w", knorm_w)):
             _check_tensor(name, t, torch.float32, dev)
         self.desc = make_desc(T, cu_seqlens.numel() - 1, Hq, Hkv, d, q.dtype, rms_eps,
-                              rope_theta, softmax_scale or 0.0)
+                              rope_theta, softmax_scale or 0.0, tile_config=tile_config)
         need = workspace_bytes(self.desc)
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -226,3 +242,11 @@ def sink_attn_workspace_bytes(total_tokens, num_docs, num_q_heads, num_kv_heads,
                               dtype=torch.bfloat16) -> int:
     return workspace_bytes(make_desc(total_tokens, num_docs, num_q_heads, num_kv_heads,
                                      head_dim, dtype))
+
+
+def sink_attn_tile_config(total_tokens, num_docs, num_q_heads, num_kv_heads, head_dim, window,
+                          dtype=torch.bfloat16, tile_config=SINK_ATTN_TILE_AUTO) -> int:
+    """Tile configuration the attention stage picks for these shapes and window."""
+    return globals()["tile_config"](
+        make_desc(total_tokens, num_docs, num_q_heads, num_kv_heads, head_dim, dtype,
+                  tile_config=tile_config), window)

@@ -25,6 +25,10 @@ HIPCC_FLAGS = [
     "-Wno-unused-function",
     # keep the compiler from forming packed fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA builtins write VGPRs: the wide attention kernel keeps its score
+    # accumulators in VGPRs for the softmax and its O accumulators in AGPRs
+    # through inline asm (code of the other kernels is unchanged by this)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -1,10 +1,11 @@
 // prologue.hip -- first stage of the forward pass.
 //
 // bf16 path, one launch:
-//   * block 0 builds the varlen work schedule from cu_seqlens: the number of
-//     query blocks of every document, their exclusive prefix, and the table of
-//     (document, block) items the attention grid walks, longest-running
-//     (highest position) blocks first.
+//   * blocks 0 and 1 build the varlen work schedules from cu_seqlens, one per
+//     attention tile configuration (query blocks of 128/G and 256/G tokens):
+//     the number of query blocks of every document, their exclusive prefix,
+//     and the table of (document, block) items the attention grid walks,
+//     longest-running (highest position) blocks first.
 //   * every other block takes 64 consecutive tokens (one key tile) of one kv
 //     head and
 //       - applies per-head RMSNorm and, when enabled, NeoX RoPE to K
@@ -83,18 +84,22 @@ __device__ void build_schedule(const int32_t* __restrict__ cu, int D, int m_tok,
 __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
     const bf16* __restrict__ k, const bf16* __restrict__ v,
     const int32_t* __restrict__ cu, const float* __restrict__ knorm_w, int T, int D,
-    int Hkv, int64_t t_pad, int m_tok, float eps, double theta, int use_rope,
-    bf16* __restrict__ khat, bf16* __restrict__ vt, int32_t* __restrict__ sched,
-    int64_t items_ub, int32_t* __restrict__ prefix_g) {
-  if (blockIdx.x == 0) {
-    build_schedule(cu, D, m_tok, sched, items_ub, prefix_g);
+    int Hkv, int64_t t_pad, int m_tok, int m_tok_wide, float eps, double theta,
+    int use_rope, bf16* __restrict__ khat, bf16* __restrict__ vt,
+    int32_t* __restrict__ sched, int32_t* __restrict__ sched_wide) {
+  if (blockIdx.x < 2) {
+    const bool wide = blockIdx.x == 1;
+    const int mt = wide ? m_tok_wide : m_tok;
+    const int64_t items_ub = T / mt + D;
+    int32_t* sc = wide ? sched_wide : sched;
+    build_schedule(cu, D, mt, sc, items_ub, sc + 4 + 2 * items_ub);
     return;
   }
   __shared__ double s_invf[64];
   __shared__ __attribute__((aligned(16))) bf16 s_v[kKeyTile][kHeadDim + 8];
 
   const int tid = threadIdx.x;
-  const int blk = blockIdx.x - 1;
+  const int blk = blockIdx.x - 2;
   const int tile = blk / Hkv;
   const int g = blk - tile * Hkv;
   const int t0 = tile * kKeyTile;
@@ -233,16 +238,14 @@ __global__ __launch_bounds__(kThreads) void prologue_f32_kernel(
 
 hipError_t launch_prologue_bf16(const bf16* k, const bf16* v, const int32_t* cu,
                                 const float* knorm_w, int T, int D, int Hkv,
-                                int64_t t_pad, int m_tok, double eps, double theta,
-                                int use_rope, bf16* khat, bf16* vt, int32_t* sched,
-                                hipStream_t stream) {
+                                int64_t t_pad, int m_tok, int m_tok_wide, double eps,
+                                double theta, int use_rope, bf16* khat, bf16* vt,
+                                int32_t* sched, int32_t* sched_wide, hipStream_t stream) {
   const int64_t n_tiles = t_pad / kKeyTile;
-  const int64_t items_ub = T / m_tok + D;
-  int32_t* prefix_g = sched + 4 + 2 * items_ub;
-  const int64_t grid = 1 + n_tiles * Hkv;
+  const int64_t grid = 2 + n_tiles * Hkv;
   prologue_bf16_kernel<<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-      k, v, cu, knorm_w, T, D, Hkv, t_pad, m_tok, (float)eps, theta, use_rope, khat, vt,
-      sched, items_ub, prefix_g);
+      k, v, cu, knorm_w, T, D, Hkv, t_pad, m_tok, m_tok_wide, (float)eps, theta, use_rope,
+      khat, vt, sched, sched_wide);
   return hipGetLastError();
 }
 

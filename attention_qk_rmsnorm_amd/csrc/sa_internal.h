@@ -17,25 +17,45 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kHeadDim = 128;     // head_dim of the bf16 MFMA path
 constexpr int kKeyTile = 64;      // keys per LDS tile; tiles start at multiples of 64
 constexpr int kWaves = 4;         // waves per attention workgroup
-constexpr int kColsPerWave = 32;  // (token, head) query columns per wave
+constexpr int kColsPerWave = 32;  // narrow tiles: (token, head) query columns per wave
+constexpr int kColsPerWaveWide = 64;  // wide tiles: columns per wave
 constexpr int kMaxGroup = 32;     // largest Hq / Hkv of the bf16 path
 constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
 
+// bf16 attention tile configurations (sink_attn_desc.tile_config).
+constexpr int kTileAuto = 0;
+constexpr int kTileNarrow = 1;  // 32 columns per wave, two workgroups per CU
+constexpr int kTileWide = 2;    // 64 columns per wave, one workgroup per CU
+constexpr int kTileWideExact = 3;  // wide, every block through the exact-max pass
+
 // Query tokens one attention workgroup covers for a GQA group size G:
-// kWaves * 32 columns = tokens * G.
+// kWaves * columns per wave = tokens * G.
 inline int tokens_per_block(int G) { return kWaves * kColsPerWave / G; }
+inline int tokens_per_block_wide(int G) { return kWaves * kColsPerWaveWide / G; }
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Workspace carve-up (all offsets 256-byte aligned).
 struct Workspace {
-  int64_t t_pad = 0;        // keys padded to a multiple of kKeyTile
-  int64_t items_ub = 0;     // upper bound on (document, query block) items
-  size_t khat_off = 0;      // bf16: [Hkv][t_pad][128]; f32: [T][Hkv][d]
-  size_t vt_off = 0;        // bf16: V transposed [Hkv][128][t_pad]; f32: V copy [T][Hkv][d]
-  size_t sched_off = 0;     // int32 n_items, then int2 items[items_ub]
+  int64_t t_pad = 0;         // keys padded to a multiple of kKeyTile
+  int64_t items_ub = 0;      // upper bound on (document, query block) items, narrow tiles
+  int64_t items_ub_wide = 0; // the same for wide tiles
+  size_t khat_off = 0;       // bf16: k_hat tile images [Hkv][t_pad/64][64][128]; f32: [T][Hkv][d]
+  size_t vt_off = 0;         // bf16: V^T tile images [Hkv][t_pad/64][128][64]; f32: V copy [T][Hkv][d]
+  size_t sched_off = 0;      // narrow schedule: int32 n_items, int2 items[items_ub], prefix
+  size_t sched_wide_off = 0; // wide schedule, same format
+  size_t redo_off = 0;       // int32 per wide workgroup: rerun with the exact row max
   size_t total = 0;
 };
+
+// Schedule table size in int32 for items_ub items and D documents.
+inline int64_t sched_ints(int64_t items_ub, int64_t D) { return 4 + 2 * items_ub + D + 1; }
+
+// Wide-tile grid size (also the redo table size) for items_ub items.
+inline int64_t wide_grid(int64_t items_ub, int Hkv) {
+  return (Hkv <= 8 && 8 % Hkv == 0) ? 8 * ((items_ub + 8 / Hkv - 1) / (8 / Hkv))
+                                    : items_ub * Hkv;
+}
 
 Workspace plan_workspace(int64_t T, int64_t D, int Hq, int Hkv, int d, int dtype);
 
@@ -43,9 +63,9 @@ Workspace plan_workspace(int64_t T, int64_t D, int Hq, int Hkv, int d, int dtype
 
 hipError_t launch_prologue_bf16(const bf16* k, const bf16* v, const int32_t* cu,
                                 const float* knorm_w, int T, int D, int Hkv,
-                                int64_t t_pad, int m_tok, double eps, double theta,
-                                int use_rope, bf16* khat, bf16* vt, int32_t* sched,
-                                hipStream_t stream);
+                                int64_t t_pad, int m_tok, int m_tok_wide, double eps,
+                                double theta, int use_rope, bf16* khat, bf16* vt,
+                                int32_t* sched, int32_t* sched_wide, hipStream_t stream);
 
 hipError_t launch_attention_bf16(const bf16* q, const bf16* khat, const bf16* vt,
                                  const int32_t* cu, const int32_t* sched,
@@ -54,6 +74,14 @@ hipError_t launch_attention_bf16(const bf16* q, const bf16* khat, const bf16* vt
                                  int64_t t_pad, int64_t items_ub, int window,
                                  int use_rope, double eps, double theta,
                                  double scale, hipStream_t stream);
+
+hipError_t launch_attention_bf16_wide(const bf16* q, const bf16* khat, const bf16* vt,
+                                      const int32_t* cu, const int32_t* sched,
+                                      const float* sinks, const float* qnorm_w, bf16* out,
+                                      float* lse, int32_t* redo, int T, int D, int Hq,
+                                      int Hkv, int64_t t_pad, int64_t items_ub, int window,
+                                      int use_rope, double eps, double theta, double scale,
+                                      bool exact_all, hipStream_t stream);
 
 hipError_t launch_prologue_f32(const float* k, const float* v, const int32_t* cu,
                                const float* knorm_w, int T, int D, int Hkv, int d,

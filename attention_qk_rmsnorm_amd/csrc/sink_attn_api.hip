@@ -19,6 +19,7 @@ Workspace plan_workspace(int64_t T, int64_t D, int Hq, int Hkv, int d, int dtype
   if (dtype == SINK_ATTN_BF16) {
     const int G = Hq / Hkv;
     w.items_ub = T / tokens_per_block(G) + D;
+    w.items_ub_wide = T / tokens_per_block_wide(G) + D;
     w.khat_off = off;
     off += (size_t)Hkv * w.t_pad * kHeadDim * sizeof(bf16);
     off = round_up(off, 256);
@@ -26,7 +27,13 @@ Workspace plan_workspace(int64_t T, int64_t D, int Hq, int Hkv, int d, int dtype
     off += (size_t)Hkv * kHeadDim * w.t_pad * sizeof(bf16);
     off = round_up(off, 256);
     w.sched_off = off;
-    off += sizeof(int32_t) * (4 + 2 * w.items_ub + D + 1);
+    off += sizeof(int32_t) * sched_ints(w.items_ub, D);
+    off = round_up(off, 256);
+    w.sched_wide_off = off;
+    off += sizeof(int32_t) * sched_ints(w.items_ub_wide, D);
+    off = round_up(off, 256);
+    w.redo_off = off;
+    off += sizeof(int32_t) * wide_grid(w.items_ub_wide, Hkv);
   } else {
     w.khat_off = off;
     off += (size_t)T * Hkv * d * sizeof(float);
@@ -48,7 +55,8 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 int check_desc(const sink_attn_desc* d) {
   if (d == nullptr) return SINK_ATTN_EINVAL;
   if (d->total_tokens < 0 || d->num_docs < 0 || d->num_q_heads <= 0 ||
-      d->num_kv_heads <= 0 || d->head_dim <= 0 || d->max_seqlen < 0 || d->reserved != 0)
+      d->num_kv_heads <= 0 || d->head_dim <= 0 || d->max_seqlen < 0 ||
+      d->tile_config < sa::kTileAuto || d->tile_config > sa::kTileWideExact)
     return SINK_ATTN_EINVAL;
   if (d->num_q_heads % d->num_kv_heads != 0) return SINK_ATTN_EINVAL;
   if (d->total_tokens > 0 && d->num_docs == 0) return SINK_ATTN_EINVAL;
@@ -80,6 +88,20 @@ uintptr_t io_align(const sink_attn_desc* d) { return d->dtype == SINK_ATTN_BF16 
 sa::Workspace plan(const sink_attn_desc* d) {
   return sa::plan_workspace(d->total_tokens, d->num_docs, d->num_q_heads, d->num_kv_heads,
                             d->head_dim, d->dtype);
+}
+
+// bf16 tile configuration of a call.  Wide tiles (64 columns per wave, one
+// workgroup per CU, half the LDS operand traffic per MFMA) win once a query
+// block visits many key tiles; narrow ones (32 columns, two workgroups per
+// CU, shorter blocks) win on short documents and narrow windows.  The
+// automatic choice estimates the keys a query sees: the window, capped by the
+// mean document length, or half that length when causal.
+int select_tile(const sink_attn_desc* d, int32_t window) {
+  if (d->tile_config != sa::kTileAuto) return d->tile_config;
+  if (d->num_docs <= 0) return sa::kTileNarrow;
+  const int64_t mean_len = (int64_t)d->total_tokens / d->num_docs;
+  const int64_t keys = window > 0 ? (window < mean_len ? window : mean_len) : mean_len / 2;
+  return keys >= 2048 ? sa::kTileWide : sa::kTileNarrow;
 }
 
 double softmax_scale(const sink_attn_desc* d) {
@@ -128,9 +150,10 @@ int launch_prologue(const sink_attn_desc* d, const void* k, const void* v,
     e = sa::launch_prologue_bf16(
         static_cast<const sa::bf16*>(k), static_cast<const sa::bf16*>(v), cu, knorm_w,
         d->total_tokens, d->num_docs, d->num_kv_heads, w.t_pad, sa::tokens_per_block(G),
-        d->rms_eps, d->rope_theta, use_rope, reinterpret_cast<sa::bf16*>(ws + w.khat_off),
-        reinterpret_cast<sa::bf16*>(ws + w.vt_off), reinterpret_cast<int32_t*>(ws + w.sched_off),
-        stream);
+        sa::tokens_per_block_wide(G), d->rms_eps, d->rope_theta, use_rope,
+        reinterpret_cast<sa::bf16*>(ws + w.khat_off), reinterpret_cast<sa::bf16*>(ws + w.vt_off),
+        reinterpret_cast<int32_t*>(ws + w.sched_off),
+        reinterpret_cast<int32_t*>(ws + w.sched_wide_off), stream);
   } else {
     e = sa::launch_prologue_f32(static_cast<const float*>(k), static_cast<const float*>(v), cu,
                                 knorm_w, d->total_tokens, d->num_docs, d->num_kv_heads,
@@ -147,7 +170,17 @@ int launch_attention(const sink_attn_desc* d, const void* q, const int32_t* cu, 
   const sa::Workspace w = plan(d);
   char* ws = static_cast<char*>(d->workspace);
   hipError_t e;
-  if (d->dtype == SINK_ATTN_BF16) {
+  const int tile = d->dtype == SINK_ATTN_BF16 ? select_tile(d, window) : 0;
+  if (tile == sa::kTileWide || tile == sa::kTileWideExact) {
+    e = sa::launch_attention_bf16_wide(
+        static_cast<const sa::bf16*>(q), reinterpret_cast<const sa::bf16*>(ws + w.khat_off),
+        reinterpret_cast<const sa::bf16*>(ws + w.vt_off), cu,
+        reinterpret_cast<const int32_t*>(ws + w.sched_wide_off), sinks, qnorm_w,
+        static_cast<sa::bf16*>(out), lse, reinterpret_cast<int32_t*>(ws + w.redo_off),
+        d->total_tokens, d->num_docs, d->num_q_heads, d->num_kv_heads, w.t_pad,
+        w.items_ub_wide, window, use_rope, d->rms_eps, d->rope_theta, softmax_scale(d),
+        tile == sa::kTileWideExact, stream);
+  } else if (d->dtype == SINK_ATTN_BF16) {
     e = sa::launch_attention_bf16(
         static_cast<const sa::bf16*>(q), reinterpret_cast<const sa::bf16*>(ws + w.khat_off),
         reinterpret_cast<const sa::bf16*>(ws + w.vt_off),
@@ -208,6 +241,14 @@ int sink_attn_fwd(const sink_attn_desc* desc, const void* q, const void* k, cons
   return launch_attention(desc, q, cu_seqlens, sinks, qnorm_w, window, use_rope, out, lse, s);
 }
 
+int sink_attn_tile_config(const sink_attn_desc* desc, int32_t window) {
+  const int rc = check_desc(desc);
+  if (rc != SINK_ATTN_OK) return rc;
+  if (window == 0) return SINK_ATTN_EINVAL;
+  if (desc->dtype != SINK_ATTN_BF16) return 0;
+  return select_tile(desc, window);
+}
+
 const char* sink_attn_status_string(int status) {
   switch (status) {
     case SINK_ATTN_OK: return "success";
@@ -219,6 +260,6 @@ const char* sink_attn_status_string(int status) {
   }
 }
 
-int sink_attn_version(void) { return 100; }
+int sink_attn_version(void) { return 200; }
 
 }  // extern "C"

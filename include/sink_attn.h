@@ -69,6 +69,25 @@ typedef enum {
   SINK_ATTN_F32 = 1    /* q, k, v, out fp32; fp32 arithmetic throughout (debug path) */
 } sink_attn_dtype;
 
+/* Attention tile configuration of the bf16 path.  Both compute the same
+ * function to the same tolerance; they differ in speed.  Narrow: each wave
+ * holds 32 (token, head) query columns, two workgroups share a compute unit;
+ * best for short documents and narrow windows.  Wide: 64 columns per wave,
+ * one workgroup per compute unit, half the LDS operand traffic per matrix
+ * instruction; best when every query sees thousands of keys (long causal
+ * documents, wide windows).  The fp32 path has a single configuration and
+ * ignores the setting. */
+typedef enum {
+  SINK_ATTN_TILE_AUTO = 0,
+  SINK_ATTN_TILE_NARROW = 1,
+  SINK_ATTN_TILE_WIDE = 2,
+  /* Wide tiles with every query block taking the path normally reserved for
+   * blocks whose scores rise more than 90 log2 units above the token's own
+   * score: a scores-only pass for the exact row max first.  Same results,
+   * slower; for testing that path. */
+  SINK_ATTN_TILE_WIDE_EXACT = 3
+} sink_attn_tile_config_t;
+
 /* Shapes and settings of one call.  Plain data; the library keeps no pointer
  * to it after a call returns. */
 typedef struct {
@@ -79,7 +98,7 @@ typedef struct {
   int32_t head_dim;       /* d: 128 (bf16 and fp32) or 64 (fp32 only) */
   int32_t dtype;          /* sink_attn_dtype of q, k, v and out */
   int32_t max_seqlen;     /* optional hint (0 = unknown); not needed, not trusted */
-  int32_t reserved;       /* must be 0 */
+  int32_t tile_config;    /* sink_attn_tile_config_t: 0 automatic (use this), 1-3 force */
   double rms_eps;         /* RMSNorm epsilon, added to mean(x^2); 1e-6 for Flint */
   double rope_theta;      /* RoPE base; inv_freq_i = theta^(-2i/d) */
   double softmax_scale;   /* <= 0 selects 1/sqrt(head_dim) */
@@ -88,7 +107,8 @@ typedef struct {
 } sink_attn_desc;
 
 /* Bytes of device workspace a call with this descriptor needs (0 when T == 0).
- * Depends only on total_tokens, num_docs, num_kv_heads, head_dim and dtype.
+ * Depends only on total_tokens, num_docs, num_q_heads, num_kv_heads, head_dim
+ * and dtype (not on tile_config).
  * Returns 0 for a NULL or invalid descriptor. */
 size_t sink_attn_workspace_bytes(const sink_attn_desc* desc);
 
@@ -123,6 +143,14 @@ int sink_attn_attention(const sink_attn_desc* desc, const void* q,
                         const int32_t* cu_seqlens, const float* sinks,
                         const float* qnorm_w, int32_t window, int32_t use_rope,
                         void* out, float* lse, void* stream);
+
+/* The tile configuration (SINK_ATTN_TILE_NARROW, _WIDE or _WIDE_EXACT) that
+ * sink_attn_attention would use for this descriptor and window, 0 for the fp32
+ * path, or a negative status for an invalid descriptor or window == 0.  The
+ * automatic choice takes the wide tiles when the window (capped by the mean
+ * document length T / D), or half the mean length when causal, is at least
+ * 2048 keys.  Reads no device memory. */
+int sink_attn_tile_config(const sink_attn_desc* desc, int32_t window);
 
 /* Static text for a status code (never NULL). */
 const char* sink_attn_status_string(int status);

@@ -26,7 +26,7 @@ def test_every_declared_symbol_is_exported(A):
     names = A.header_functions()
     assert set(names) >= {"sink_attn_fwd", "sink_attn_workspace_bytes",
                           "sink_attn_status_string", "sink_attn_prologue",
-                          "sink_attn_attention", "sink_attn_version"}
+                          "sink_attn_attention", "sink_attn_version", "sink_attn_tile_config"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -84,7 +84,8 @@ def _fwd(A, desc, window=-1, use_rope=0, q=FAKE, k=FAKE, v=FAKE, cu=FAKE, sinks=
     ("heads_not_divisible", EINVAL),
     ("negative_tokens", EINVAL),
     ("tokens_without_docs", EINVAL),
-    ("reserved_nonzero", EINVAL),
+    ("tile_config_4", EINVAL),
+    ("tile_config_negative", EINVAL),
     ("negative_eps", EINVAL),
     ("theta_zero", EINVAL),
     ("nan_scale", EINVAL),
@@ -118,8 +119,10 @@ def test_invalid_arguments_rejected_before_any_launch(A, case, expected):
         desc = _desc(A, T=-5)
     elif case == "tokens_without_docs":
         desc = _desc(A, D=0, ws_bytes=1 << 30)
-    elif case == "reserved_nonzero":
-        desc.reserved = 1
+    elif case == "tile_config_4":
+        desc.tile_config = 4
+    elif case == "tile_config_negative":
+        desc.tile_config = -1
     elif case == "negative_eps":
         desc.rms_eps = -1.0
     elif case == "theta_zero":
@@ -177,3 +180,28 @@ def test_empty_batch_is_a_no_op(A):
     assert _fwd(A, desc, q=0, k=0, v=0, sinks=0, qw=0, kw=0, out=0, lse=0) == OK
     desc = _desc(A, T=0, D=3)
     assert _fwd(A, desc, q=0, k=0, v=0, sinks=0, qw=0, kw=0, out=0, lse=0) == OK
+
+
+@pytest.mark.parametrize("T, D, window, expected", [
+    (32768, 1, -1, 2),      # one long causal document: wide tiles
+    (131072, 2, 4096, 2),   # long documents, 4096-key window: wide
+    (12450, 8, 1024, 1),    # 1024-key window: narrow
+    (111378, 512, -1, 1),   # short documents: narrow
+    (8192, 1, 1024, 1),     # long document, narrow window: narrow
+    (8192, 2, -1, 2),       # two 4096-token causal documents: wide (2048 keys)
+    (8190, 2, -1, 1),       # just under: narrow
+])
+def test_automatic_tile_choice(A, T, D, window, expected):
+    assert A.sink_attn_tile_config(T, D, 32, 4, 128, window) == expected
+
+
+def test_forced_tile_choice_and_fp32(A):
+    assert A.sink_attn_tile_config(100, 1, 32, 4, 128, -1, tile_config=A.SINK_ATTN_TILE_WIDE) == 2
+    assert A.sink_attn_tile_config(10 ** 6, 1, 32, 4, 128, -1,
+                                   tile_config=A.SINK_ATTN_TILE_NARROW) == 1
+    assert A.sink_attn_tile_config(128, 1, 4, 1, 64, -1, dtype=A.SINK_ATTN_F32) == 0
+    with pytest.raises(A.SinkAttnError):
+        A.sink_attn_tile_config(128, 1, 32, 4, 128, 0)
+    assert A.sink_attn_tile_config(100, 1, 32, 4, 128, -1, tile_config=3) == 3
+    with pytest.raises(A.SinkAttnError):
+        A.sink_attn_tile_config(128, 1, 32, 4, 128, -1, tile_config=5)

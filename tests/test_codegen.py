@@ -8,7 +8,12 @@ correctness rest on, checked on the CPU from hipcc's assembly output:
   disables;
 * in the attention kernel's key loop, the direct-to-LDS copy of the next tile
   is not waited for (vmcnt) before the current tile's LDS reads: the only
-  vmcnt(0) waits sit right before the per-tile barrier.
+  vmcnt(0) waits sit right before the per-tile barrier;
+* the wide attention kernel keeps its O accumulators in AGPRs through its
+  whole key loop (no accvgpr copies there), waits for tile copies only at the
+  per-tile barrier, and every MFMA it issues from inline asm has the two wait
+  states an MFMA needs after VALU code wrote one of its A/B operands (the
+  compiler does not insert them for inline asm).
 """
 import os
 import re
@@ -92,3 +97,82 @@ def test_tile_copy_not_waited_before_reads(asm):
             elif l.startswith("s_barrier") or l.startswith("s_endpgm"):
                 break
     assert checked == len(in_loop)
+
+
+def _kernel(text, marker):
+    for name, body in _kernels(text):
+        if marker in name:
+            return body
+    raise AssertionError(f"kernel {marker} not found")
+
+
+def _main_loop(body):
+    """Lines of the first loop (from its header label to the branch back)."""
+    lines = [l.strip() for l in body.splitlines()]
+    head = next(i for i, l in enumerate(lines) if "Loop Header" in l)
+    label = lines[head].split(":")[0]
+    back = max(i for i, l in enumerate(lines) if l.startswith("s_") and l.endswith(" " + label))
+    return lines[head:back + 1]
+
+
+def test_wide_kernel_registers(asm):
+    text = asm["attn_bf16_wide.hip"]
+    for key in ("NumVgprs", "NumAgprs"):
+        vals = [int(x) for x in re.findall(rf"; {key}: (\d+)", text)]
+        assert vals and max(vals) <= 256, (key, vals)
+    # O (128) and the Q operands (64) live in AGPRs
+    assert min(int(x) for x in re.findall(r"; NumAgprs: (\d+)", text)) >= 128
+
+
+def test_wide_kernel_loop_keeps_accumulators_in_agprs(asm):
+    loop = _main_loop(_kernel(asm["attn_bf16_wide.hip"], "wide_kernelILb0"))
+    assert sum(l.startswith("v_mfma") for l in loop) >= 64
+    moves = [l for l in loop if l.startswith("v_accvgpr_")]
+    assert not moves, moves[:4]
+
+
+def test_wide_kernel_waits_for_copies_only_at_barriers(asm):
+    loop = _main_loop(_kernel(asm["attn_bf16_wide.hip"], "wide_kernelILb0"))
+    code = [l for l in loop if l and not l.startswith(";")]
+    for i, l in enumerate(code):
+        if l.startswith("s_waitcnt") and "vmcnt" in l:
+            assert any(x.startswith("s_barrier") for x in code[i + 1:i + 3]), code[i:i + 4]
+
+
+def _regs(tok):
+    m = re.match(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([va])(\d+)$", tok)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
+def test_inline_asm_mfma_wait_states(asm):
+    text = asm["attn_bf16_wide.hip"]
+    lines = [l.strip() for l in text.splitlines()]
+    inasm, checked, bad = False, 0, []
+    for i, l in enumerate(lines):
+        if l.startswith(";;#ASMSTART"):
+            inasm = True
+        elif l.startswith(";;#ASMEND"):
+            inasm = False
+        elif inasm and l.startswith("v_mfma"):
+            checked += 1
+            ops = [t.strip() for t in l.split(None, 1)[1].split(",")]
+            srcs = _regs(ops[1]) | _regs(ops[2])
+            slots, j = 0, i - 1
+            while slots < 2 and j >= 0:
+                p = lines[j]
+                j -= 1
+                if not p or p.startswith(";") or p.endswith(":"):
+                    continue
+                op = p.split()[0]
+                if op == "s_nop":
+                    slots += int(p.split()[1]) + 1
+                    continue
+                if op.startswith("v_") and not op.startswith("v_mfma"):
+                    if _regs(p.split(None, 1)[1].split(",")[0].strip()) & srcs:
+                        bad.append((p, l))
+                slots += 1
+    assert checked >= 100
+    assert not bad, bad[:3]
