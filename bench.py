@@ -11,9 +11,12 @@ Throughput counts visible score entries only:
     N_vis = sum over documents of sum_{i < L} min(i + 1, W)   (W = inf when causal)
     FLOP  = 4 * head_dim * Hq * N_vis      (QK^T and PV, 2 * head_dim each)
 and is reported in TFLOP/s for the whole step.  The printed JSON line also
-carries the roofline of the dominant kernel (the attention kernel, timed with
+carries the roofline of the dominant kernel (the attention stage, timed with
 HIP events on the stream it is launched on) against the bf16 dense MFMA peak,
-and the fp64 CPU oracle timed on a bounded sample of the same workload.
+and the fp64 CPU oracle timed on a bounded sample of the same workload.  The
+attention stage is one launch of the narrow-tile kernel or, with wide tiles,
+the main launch plus the follow-up that reruns the (normally no) blocks whose
+fixed softmax reference proved too low; the events cover both.
 """
 from __future__ import annotations
 
@@ -33,7 +36,11 @@ if ROOT not in sys.path:
 METRIC = "sink-attn fwd TFLOP/s (visible entries) + % bf16 MFMA peak, 32q/4kv d128, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
-ATTN_SOURCE = os.path.join(ROOT, "attention_qk_rmsnorm_amd", "csrc", "attn_bf16.hip")
+CSRC = os.path.join(ROOT, "attention_qk_rmsnorm_amd", "csrc")
+# tile configuration -> (attention kernel, its source file)
+ATTN_KERNELS = {1: ("attn_fwd_bf16_kernel", "attn_bf16.hip"),
+                2: ("attn_fwd_bf16_wide_kernel", "attn_bf16_wide.hip"),
+                3: ("attn_fwd_bf16_wide_kernel", "attn_bf16_wide.hip")}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_traffic.json")
 
 
@@ -53,16 +60,17 @@ def source_digest(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, kernel: str, source: str):
     """HBM bytes per attention launch from the committed rocprofv3 PMC summary,
-    or None when it is missing, for another workload, or the kernel source has
-    changed since the counters were taken."""
+    or None when it is missing, for another workload or kernel, or the kernel
+    source has changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("workload") != workload or t.get("source_sha256") != source_digest(ATTN_SOURCE):
+    if (t.get("workload") != workload or t.get("kernel") != kernel
+            or t.get("source_sha256") != source_digest(os.path.join(CSRC, source))):
         return None
     return t.get("bytes_per_launch")
 
@@ -168,13 +176,15 @@ def main():
                   d_inp["qnorm_w"], d_inp["knorm_w"], w.window, w.use_rope,
                   rms_eps=w.rms_eps, rope_theta=w.rope_theta)
     stream = torch.cuda.current_stream(dev)
+    tile = A.tile_config(call.desc, w.window)
+    kernel, kernel_src = ATTN_KERNELS[tile]
 
     for _ in range(args.warmup):
         call.fwd()
     torch.cuda.synchronize()
 
     # timed region: K whole steps, each bracketed by events around the two
-    # stages on the launch stream (the attention stage launches one kernel)
+    # stages on the launch stream
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -215,17 +225,18 @@ def main():
             "tokens": T, "docs": w.num_docs, "q_heads": w.num_q_heads,
             "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "window": w.window,
             "rope": w.use_rope, "visible_entries": n_vis, "flop_per_step": flop,
+            "tile_config": {1: "narrow", 2: "wide", 3: "wide_exact"}[tile],
             "parallelism": "single GPU",
         },
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_bf16_kernel",
+            "kernel": kernel,
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": load_traffic(w.name),
+            "traffic": load_traffic(w.name, kernel, kernel_src),
             "avg_launch_ms": attn_ms,
         },
         "kernels": {
