@@ -279,6 +279,164 @@ int oracle_sink_attn_fwd(int T, int num_docs, const int32_t* cu, int Hq,
   return rc;
 }
 
+/* ------------------------------------------------------------------------
+ * Backward pass: gradients of L = sum(dout * out) with respect to q, k, v,
+ * the sinks and the two norm weights, for the forward above.  Each is the
+ * derivative of steps 1-5 by the chain rule, evaluated in double precision:
+ *   step 5, per (token t, query head h) with weights P_u = exp(s_u - lse) over
+ *   the visible set and p_sink = exp(sink - lse):
+ *     D       = dout_t . out_t
+ *     dv_u   += P_u dout_t                       (summed over the heads of u's group)
+ *     dS_u    = P_u (dout_t . v_u - D)
+ *     dsink_h -= p_sink D                        (the sink's value is zero)
+ *   step 4:  dq_hat_t += scale sum_u dS_u k_hat_u,  dk_hat_u += scale dS_u q_hat_t
+ *   step 2:  the transpose of the rotation: rotate each pair back by -angle
+ *   step 1:  y = w x r with r = (mean(x^2) + eps)^(-1/2):
+ *            dw += dy x r,  dx = w dy r - x r^3 (sum_c w_c dy_c x_c) / d
+ * The sinks are trainable fp32 logits ([L] _FlintSinkParameters) and the norm
+ * weights are the RMSNorm parameters ([L] q_norm / k_norm).
+ * ------------------------------------------------------------------------ */
+
+/* Transpose of step 2 for one head vector: turn each pair by -angle. */
+static void rope_neox_vec_t(int d, double p, double theta, double* y) {
+  int half = d / 2;
+  for (int i = 0; i < half; ++i) {
+    double inv_freq = pow(theta, -2.0 * (double)i / (double)d);
+    double ang = p * inv_freq;
+    double c = cos(ang), s = sin(ang);
+    double a = y[i], b = y[i + half];
+    y[i] = a * c + b * s;
+    y[i + half] = b * c - a * s;
+  }
+}
+
+/* Backward of step 1 for one head vector: dy -> dx, and dy * x * r added
+ * into dw. */
+static void rmsnorm_vec_bwd(int d, const double* x, const double* w, double eps,
+                            const double* dy, double* dx, double* dw) {
+  double ss = 0.0;
+  for (int i = 0; i < d; ++i) ss += x[i] * x[i];
+  double r = 1.0 / sqrt(ss / (double)d + eps);
+  double dot = 0.0;
+  for (int i = 0; i < d; ++i) dot += w[i] * dy[i] * x[i];
+  for (int i = 0; i < d; ++i) {
+    dx[i] = w[i] * dy[i] * r - x[i] * r * r * r * dot / (double)d;
+    dw[i] += dy[i] * x[i] * r;
+  }
+}
+
+/* Public: gradients of sum(dout * out) for the whole forward pass.
+ *   q, dout, dq [T, Hq, d]; k, v, dk, dv [T, Hkv, d]; dsinks [Hq];
+ *   dqnorm_w, dknorm_w [d].  Every output is overwritten.  Work is split
+ *   over (document, kv head) pairs, whose gradients do not overlap, and the
+ *   shared sums (sinks, norm weights) are added in a fixed order, so the
+ *   result does not depend on the thread count. */
+int oracle_sink_attn_bwd(int T, int num_docs, const int32_t* cu, int Hq, int Hkv,
+                         int d, const double* q, const double* k, const double* v,
+                         const double* sinks, const double* qnorm_w,
+                         const double* knorm_w, double eps, double theta,
+                         double scale, int window, int use_rope, const double* dout,
+                         double* dq, double* dk, double* dv, double* dsinks,
+                         double* dqnorm_w, double* dknorm_w, int nthreads) {
+  if (T < 0 || num_docs < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || (d & 1) ||
+      Hq % Hkv || window == 0)
+    return ORACLE_EINVAL;
+  if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+  int32_t* doc_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  int32_t* pos_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)(T > 0 ? T : 1));
+  int rc = doc_layout(T, num_docs, cu, doc_of, pos_of);
+  if (rc != ORACLE_OK) {
+    free(doc_of);
+    free(pos_of);
+    return rc;
+  }
+  const int group = Hq / Hkv;
+  const size_t nq = (size_t)T * Hq * d, nk = (size_t)T * Hkv * d;
+  double* qh = (double*)malloc(sizeof(double) * (nq + 1));
+  double* kh = (double*)malloc(sizeof(double) * (nk + 1));
+  double* dqh = (double*)calloc(nq + 1, sizeof(double));
+  double* dkh = (double*)calloc(nk + 1, sizeof(double));
+  double* sink_part = (double*)calloc((size_t)num_docs * Hq + 1, sizeof(double));
+  prologue_rows(T, pos_of, Hq, d, q, qnorm_w, eps, theta, use_rope, qh);
+  prologue_rows(T, pos_of, Hkv, d, k, knorm_w, eps, theta, use_rope, kh);
+  for (size_t i = 0; i < nk; ++i) dv[i] = 0.0;
+
+  const long items = (long)num_docs * Hkv;
+#ifdef _OPENMP
+  int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
+#pragma omp parallel num_threads(nt)
+#endif
+  {
+    double* scores = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    double* out_row = (double*)malloc(sizeof(double) * (size_t)d);
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+    for (long item = 0; item < items; ++item) {
+      const int n = (int)(item / Hkv), g = (int)(item % Hkv);
+      for (int t = cu[n]; t < cu[n + 1]; ++t)
+        for (int h = g * group; h < (g + 1) * group; ++h) {
+          const double* qrow = qh + ((size_t)t * Hq + h) * d;
+          const double* dorow = dout + ((size_t)t * Hq + h) * d;
+          double lse;
+          attend_row(t, T, Hkv, g, d, qrow, kh, v, sinks[h], scale, window, doc_of,
+                     pos_of, scores, out_row, &lse);
+          double D = 0.0;
+          for (int i = 0; i < d; ++i) D += dorow[i] * out_row[i];
+          sink_part[(size_t)n * Hq + h] -= exp(sinks[h] - lse) * D;
+          double* dqrow = dqh + ((size_t)t * Hq + h) * d;
+          for (int u = cu[n]; u <= t; ++u) {
+            if (scores[u] == -INFINITY) continue;
+            const double P = exp(scores[u] - lse);
+            const double* vu = v + ((size_t)u * Hkv + g) * d;
+            const double* ku = kh + ((size_t)u * Hkv + g) * d;
+            double dP = 0.0;
+            for (int i = 0; i < d; ++i) dP += dorow[i] * vu[i];
+            const double dS = P * (dP - D);
+            double* dku = dkh + ((size_t)u * Hkv + g) * d;
+            double* dvu = dv + ((size_t)u * Hkv + g) * d;
+            for (int i = 0; i < d; ++i) {
+              dqrow[i] += scale * dS * ku[i];
+              dku[i] += scale * dS * qrow[i];
+              dvu[i] += P * dorow[i];
+            }
+          }
+        }
+    }
+    free(scores);
+    free(out_row);
+  }
+  for (int h = 0; h < Hq; ++h) {
+    dsinks[h] = 0.0;
+    for (int n = 0; n < num_docs; ++n) dsinks[h] += sink_part[(size_t)n * Hq + h];
+  }
+  /* steps 2 and 1 backwards, token by token in order (fixed summation order
+   * for the norm weights) */
+  for (int i = 0; i < d; ++i) dqnorm_w[i] = dknorm_w[i] = 0.0;
+  for (int t = 0; t < T; ++t) {
+    for (int h = 0; h < Hq; ++h) {
+      double* dy = dqh + ((size_t)t * Hq + h) * d;
+      if (use_rope) rope_neox_vec_t(d, (double)pos_of[t], theta, dy);
+      rmsnorm_vec_bwd(d, q + ((size_t)t * Hq + h) * d, qnorm_w, eps, dy,
+                      dq + ((size_t)t * Hq + h) * d, dqnorm_w);
+    }
+    for (int g = 0; g < Hkv; ++g) {
+      double* dy = dkh + ((size_t)t * Hkv + g) * d;
+      if (use_rope) rope_neox_vec_t(d, (double)pos_of[t], theta, dy);
+      rmsnorm_vec_bwd(d, k + ((size_t)t * Hkv + g) * d, knorm_w, eps, dy,
+                      dk + ((size_t)t * Hkv + g) * d, dknorm_w);
+    }
+  }
+  free(qh);
+  free(kh);
+  free(dqh);
+  free(dkh);
+  free(sink_part);
+  free(doc_of);
+  free(pos_of);
+  return ORACLE_OK;
+}
+
 /* Number of OpenMP threads a call with nthreads <= 0 would use. */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

@@ -55,6 +55,9 @@ def _load():
     lib.oracle_sink_attn_fwd.argtypes = [I, I, P, I, I, I, P, P, P, P, P, P,
                                          D, D, D, I, I, P, I, P, P, I]
     lib.oracle_sink_attn_fwd.restype = I
+    lib.oracle_sink_attn_bwd.argtypes = [I, I, P, I, I, I, P, P, P, P, P, P,
+                                         D, D, D, I, I, P, P, P, P, P, P, P, I]
+    lib.oracle_sink_attn_bwd.restype = I
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = I
     _lib = lib
@@ -150,3 +153,30 @@ def sink_attn_fwd(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window,
     if rc:
         raise OracleError(f"oracle_sink_attn_fwd rejected its arguments ({rc})")
     return out, lse
+
+
+def sink_attn_bwd(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope,
+                  dout, eps=1e-6, theta=1e6, scale=None, nthreads=0):
+    """Gradients of sum(dout * out) of the whole forward pass, in fp64.
+
+    q, dout [T, Hq, d]; k, v [T, Hkv, d].  Returns a dict with dq, dk, dv (the
+    shapes of q, k, v), dsinks [Hq], dqnorm_w and dknorm_w [d], as float64.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    T, Hkv, d = k.shape
+    Hq = q.shape[1]
+    if q.shape[0] != T or dout.shape != q.shape:
+        raise OracleError("q and dout must be [T, Hq, d]")
+    cu = _i32(cu_seqlens)
+    res = {"dq": np.empty_like(q), "dk": np.empty_like(k), "dv": np.empty_like(v),
+           "dsinks": np.empty(Hq), "dqnorm_w": np.empty(d), "dknorm_w": np.empty(d)}
+    rc = _load().oracle_sink_attn_bwd(
+        T, len(cu) - 1, _ptr(cu), Hq, Hkv, d, _ptr(q), _ptr(k), _ptr(v),
+        _ptr(_f64(sinks)), _ptr(_f64(qnorm_w)), _ptr(_f64(knorm_w)),
+        float(eps), float(theta), float(scale) if scale else 0.0, int(window),
+        int(bool(use_rope)), _ptr(dout), _ptr(res["dq"]), _ptr(res["dk"]),
+        _ptr(res["dv"]), _ptr(res["dsinks"]), _ptr(res["dqnorm_w"]),
+        _ptr(res["dknorm_w"]), int(nthreads))
+    if rc:
+        raise OracleError(f"oracle_sink_attn_bwd rejected its arguments ({rc})")
+    return res

@@ -1,5 +1,7 @@
 """Each plausible mistake planted in a copy of the oracle (dropped term, wrong
-sign, wrong index, wrong operand) must make at least one pin fail.
+sign, wrong index, wrong operand) must make at least one pin fail: forward
+mistakes against the forward pins, backward mistakes against the backward
+pins.
 
 The mutants are compiled on the CPU from text substitutions of oracle.c into a
 temporary directory; the pins run against them in a subprocess through the
@@ -35,10 +37,24 @@ MUTANTS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_catch_planted_mistake(name, tmp_path):
+BWD_MUTANTS = {
+    "bwd_D_term_dropped": ("const double dS = P * (dP - D);", "const double dS = P * dP;"),
+    "bwd_sink_sign": ("sink_part[(size_t)n * Hq + h] -= exp(sinks[h] - lse) * D;",
+                      "sink_part[(size_t)n * Hq + h] += exp(sinks[h] - lse) * D;"),
+    "bwd_sink_not_normalised": ("exp(sinks[h] - lse) * D", "exp(sinks[h]) * D"),
+    "bwd_dq_scale_dropped": ("dqrow[i] += scale * dS * ku[i];", "dqrow[i] += dS * ku[i];"),
+    "bwd_dk_from_key": ("dku[i] += scale * dS * qrow[i];", "dku[i] += scale * dS * ku[i];"),
+    "bwd_dv_weight": ("dvu[i] += P * dorow[i];", "dvu[i] += dS * dorow[i];"),
+    "bwd_dP_against_key": ("dP += dorow[i] * vu[i];", "dP += dorow[i] * ku[i];"),
+    "bwd_rope_not_transposed": ("y[i] = a * c + b * s;", "y[i] = a * c - b * s;"),
+    "bwd_norm_second_term": ("dx[i] = w[i] * dy[i] * r - x[i] * r * r * r * dot / (double)d;",
+                             "dx[i] = w[i] * dy[i] * r;"),
+    "bwd_norm_weight_grad_unnormalised": ("dw[i] += dy[i] * x[i] * r;", "dw[i] += dy[i] * x[i];"),
+}
+
+
+def _run_mutant(name, old, new, pins, tmp_path):
     import oracle.oracle as O
-    old, new = MUTANTS[name]
     src = open(SRC).read()
     assert src.count(old) >= 1, f"mutation site for {name} not found"
     mutated = src.replace(old, new)
@@ -47,6 +63,16 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     lib = O.build(force=True, src=str(csrc), out=str(tmp_path / "liboracle_mutant.so"))
     env = dict(os.environ, SINKATTN_ORACLE_LIB=lib, OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} survived every pin:\n{r.stdout[-2000:]}"
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    _run_mutant(name, *MUTANTS[name], "test_oracle_pins.py", tmp_path)
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_pins_catch_planted_mistake(name, tmp_path):
+    _run_mutant(name, *BWD_MUTANTS[name], "test_oracle_bwd_pins.py", tmp_path)
