@@ -83,6 +83,10 @@ def load_library():
     lib.sink_attn_attention.restype = ctypes.c_int
     lib.sink_attn_tile_config.argtypes = [DP, I32]
     lib.sink_attn_tile_config.restype = ctypes.c_int
+    lib.sink_attn_bwd_workspace_bytes.argtypes = [DP]
+    lib.sink_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.sink_attn_bwd.argtypes = [DP, P, P, P, P, P, P, P, I32, I32, P, P, P, P, P, P, P, P, P, P]
+    lib.sink_attn_bwd.restype = ctypes.c_int
     lib.sink_attn_status_string.argtypes = [ctypes.c_int]
     lib.sink_attn_status_string.restype = ctypes.c_char_p
     lib.sink_attn_version.argtypes = []
@@ -250,3 +254,83 @@ def sink_attn_tile_config(total_tokens, num_docs, num_q_heads, num_kv_heads, hea
     return globals()["tile_config"](
         make_desc(total_tokens, num_docs, num_q_heads, num_kv_heads, head_dim, dtype,
                   tile_config=tile_config), window)
+
+
+def bwd_workspace_bytes(desc: SinkAttnDesc) -> int:
+    return int(load_library().sink_attn_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+class BwdCall:
+    """Marshalled arguments of one backward call (sink_attn_bwd)."""
+
+    def __init__(self, q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope, out,
+                 lse, dout, *, rms_eps=1e-6, rope_theta=1e6, softmax_scale=None,
+                 workspace=None, stream=None, grads=None):
+        if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+            raise ValueError("q, k, v must be THD tensors [tokens, heads, head_dim]")
+        if q.dtype != torch.bfloat16:
+            raise ValueError("the backward takes bf16 q, k, v, out and dout")
+        dev = q.device
+        T, Hq, d = q.shape
+        Hkv = k.shape[1]
+        if k.shape != (T, Hkv, d) or v.shape != k.shape:
+            raise ValueError("k and v must be [T, Hkv, head_dim] with q's T and head_dim")
+        if out.shape != q.shape or dout.shape != q.shape:
+            raise ValueError("out and dout must have q's shape")
+        for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+            _check_tensor(name, t, q.dtype, dev)
+        _check_tensor("cu_seqlens", cu_seqlens, torch.int32, dev)
+        for name, t in (("sinks", sinks), ("qnorm_w", qnorm_w), ("knorm_w", knorm_w),
+                        ("lse", lse)):
+            _check_tensor(name, t, torch.float32, dev)
+        if lse.shape != (Hq, T):
+            raise ValueError("lse must be [Hq, T]")
+        self.desc = make_desc(T, cu_seqlens.numel() - 1, Hq, Hkv, d, q.dtype, rms_eps,
+                              rope_theta, softmax_scale or 0.0)
+        need = bwd_workspace_bytes(self.desc)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if workspace is not None:
+            self.desc.workspace = workspace.data_ptr()
+            self.desc.workspace_bytes = workspace.numel() * workspace.element_size()
+        if grads is None:
+            grads = {"dq": torch.empty_like(q), "dk": torch.empty_like(k),
+                     "dv": torch.empty_like(v),
+                     "dsinks": torch.empty(Hq, dtype=torch.float32, device=dev),
+                     "dqnorm_w": torch.empty(d, dtype=torch.float32, device=dev),
+                     "dknorm_w": torch.empty(d, dtype=torch.float32, device=dev)}
+        if stream is None:
+            stream = torch.cuda.current_stream(dev).cuda_stream
+        elif isinstance(stream, torch.cuda.Stream):
+            stream = stream.cuda_stream
+        self.args = (q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w)
+        self.window, self.use_rope = int(window), int(bool(use_rope))
+        self.out, self.lse, self.dout = out, lse, dout
+        self.grads, self.workspace = grads, workspace
+        self.stream = ctypes.c_void_p(stream)
+
+    def run(self):
+        g = self.grads
+        rc = load_library().sink_attn_bwd(
+            ctypes.byref(self.desc), *(_ptr(t) for t in self.args), self.window, self.use_rope,
+            _ptr(self.out), _ptr(self.lse), _ptr(self.dout), _ptr(g["dq"]), _ptr(g["dk"]),
+            _ptr(g["dv"]), _ptr(g["dsinks"]), _ptr(g["dqnorm_w"]), _ptr(g["dknorm_w"]),
+            self.stream)
+        if rc:
+            raise SinkAttnError(rc, "sink_attn_bwd")
+        return g
+
+
+def sink_attn_bwd(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope, out, lse,
+                  dout, **kw) -> dict:
+    """Backward pass on the current stream: gradients of sum(dout * out) as a
+    dict with dq, dk, dv (bf16, shapes of q, k, v), dsinks [Hq], dqnorm_w and
+    dknorm_w [d] (fp32).  out and lse are what the forward returned."""
+    return BwdCall(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope, out, lse,
+                   dout, **kw).run()
+
+
+def sink_attn_bwd_workspace_bytes(total_tokens, num_docs, num_q_heads, num_kv_heads, head_dim,
+                                  dtype=torch.bfloat16) -> int:
+    return bwd_workspace_bytes(make_desc(total_tokens, num_docs, num_q_heads, num_kv_heads,
+                                         head_dim, dtype))

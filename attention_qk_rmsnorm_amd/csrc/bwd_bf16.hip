@@ -1,0 +1,825 @@
+// bwd_bf16.hip -- backward pass of the sink-aware GQA attention, bf16 in/out,
+// gfx950 MFMA.
+//
+// Gradients of L = sum(dout * out) for the forward of attn_bf16*.hip
+// (flint.layers FlintAttention: the sinks are trainable fp32 logits,
+// _FlintSinkParameters, and the q_norm / k_norm weights are RMSNorm
+// parameters).  Per (token t, query head h) with weights P_u = exp(s_u - lse)
+// and p_sink = exp(sink_h - lse) (lse saved by the forward):
+//   D = dout . out,  dS_u = P_u (dout . v_u - D),  dsink_h = -sum_t p_sink D
+//   dv_u = sum P_u dout,  dk_hat_u = scale sum dS_u q_hat,  dq_hat = scale sum dS_u k_hat_u
+// then the transposed NeoX rotation and the RMSNorm backward
+//   dx = w dy r - x r^3 (sum_c w_c dy_c x_c) / d,  dw += dy x r,  r = (mean(x^2)+eps)^-1/2.
+//
+// Kernels (one launch each, in this order):
+//   bwd_keys_kernel    per 64-key tile: k_hat, the raw V rows and K^T as LDS
+//                      tile images (the forward prologue's formats)
+//   bwd_cols_kernel    per 32-column tile (32/G tokens x the G heads of one kv
+//                      head): q_hat * scale * log2(e) and dout as row images
+//                      and transposed images, -lse*log2(e) and -D per column,
+//                      and the tile's share of dsink
+//   bwd_dkdv_kernel    per 128-key block (a wave holds 32 keys' K and V rows
+//                      as MFMA operands): walks the column tiles that see the
+//                      keys; S = q K^T, P, dP - D = dout V^T - D, dS; dV^T +=
+//                      dout^T P, dK^T += q^T dS (AGPR accumulators); epilogue:
+//                      dv, and dk through the rotation and norm backward
+//   bwd_dq_kernel      per 256-column block (8 waves of 32 columns): walks the
+//                      key tiles the columns see; S^T = K q^T, P^T, dP^T - D,
+//                      dS^T; dq^T += K^T dS^T; epilogue: dq through the
+//                      rotation and norm backward
+//   bwd_reduce_kernel  dsinks and both norm-weight gradients from per-tile and
+//                      per-block partial sums, in a fixed order
+// MFMA operand layouts (32x32x16, wave64): A lane l holds A[l%32][8(l/32)..+7],
+// B lane l holds B[8(l/32)..+7][l%32], accumulator register r of lane l is
+// C[8(r/4) + 4(l/32) + r%4][l%32].  A 16-step of an accumulator taken as an
+// operand (registers 8j..8j+7) covers rows 16j + 8(e/4) + 4(l/32) + e%4; the
+// transposed images store their 16-groups in that order, so every operand is
+// one 16-byte LDS read.
+#include "sa_device.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ---- workspace images ------------------------------------------------------
+// key tile (64 keys of one kv head), 48 KiB: k_hat rows | V rows | K^T
+constexpr int kKT = 16384;                 // one 64 x 256 B or 128 x 128 B image
+constexpr int kKeyTileBytes = 3 * kKT;
+// column tile (32 columns of one kv head), 36 KiB: q rows | dout rows | q^T |
+// dout^T | (-lse*log2e)[32], (-D)[32]
+constexpr int kCT = 8192;                  // one 32 x 256 B or 128 x 64 B image
+constexpr int kColTileBytes = 4 * kCT + 4096;
+constexpr int kColLd = 4 * kCT;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// accumulation into AGPR-resident accumulators (see attn_bf16_wide.hip)
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// The same with the two wait states a VALU write of a or b needs before an
+// MFMA reads it (the first use of an operand just converted from scores).
+__device__ __forceinline__ void mfma32_acc_nop(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void zero_acc(f32x16& acc, bf16x8 zero) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero));
+}
+__device__ __forceinline__ void agpr_fence() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+__device__ __forceinline__ bf16x8 rd(const char* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// chunk swizzle of the 64-byte rows of the column tiles' transposed images
+__device__ __forceinline__ int cswz(int r) { return r & 3; }
+
+// Copy nbytes (a multiple of 4096) from global to LDS with global_load_lds.
+__device__ __forceinline__ void copy_lds(const char* __restrict__ src, int nbytes, int tid,
+                                         int nthreads, char* dst) {
+  for (int off = 0; off < nbytes; off += 16 * nthreads) {
+    const int w = tid >> 6;
+    __builtin_amdgcn_global_load_lds(src + off + 16 * tid,
+                                     (lds_void*)(dst + off + 1024 * w), 16, 0, 0);
+  }
+}
+
+// Latest token that key u is visible to: min(document end, u + W) - 1.
+__device__ __forceinline__ int last_viewer(const int32_t* __restrict__ cu, int D, int u,
+                                           int window) {
+  const int n = doc_of_token(cu, D, u);
+  int e = cu[n + 1];
+  if (window > 0 && u + window < e) e = u + window;
+  return e - 1;
+}
+
+// Earliest key visible to token t: max(document start, t - W + 1).
+__device__ __forceinline__ int first_key(const int32_t* __restrict__ cu, int D, int t,
+                                         int window) {
+  const int s = cu[doc_of_token(cu, D, t)];
+  return window > 0 ? max(s, t - window + 1) : s;
+}
+
+// Backward of the rotation and the RMSNorm for one head vector held by a lane
+// pair: lane half hf holds the gradient w.r.t. the normalised, rotated vector
+// for channels 32dd + 8rq + 4hf + e at dy[16dd + 4rq + e] (dd, rq, e < 4).
+// xp points at the raw input row (+ 4hf), w at the norm weight; pos is the
+// document position (rope only).  Writes dx to dxp when ok, and dy x r per
+// channel (zero when !ok) to red[channel].
+__device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const bf16* __restrict__ xp,
+                                              const float* __restrict__ w, bool ok, bool rope,
+                                              int pos, const double* s_invf, float eps, int hf,
+                                              bf16* __restrict__ dxp, float* red) {
+  if (rope && ok) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {  // channel 32dd + 8rq + 4hf + e (dd < 2), partner + 64
+      const int dd = i >> 4, rq = (i >> 2) & 3, e = i & 3;
+      float sn, cs;
+      rope_sincos_rev(pos, s_invf[32 * dd + 8 * rq + 4 * hf + e], &sn, &cs);
+      const float a = dy[i], b = dy[i + 32];
+      dy[i] = a * cs + b * sn;
+      dy[i + 32] = b * cs - a * sn;
+    }
+  }
+  float ss = 0.f, wdx = 0.f;
+#pragma unroll
+  for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const bf16x4 xv = *reinterpret_cast<const bf16x4*>(xp + 32 * dd + 8 * rq);
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(w + 32 * dd + 8 * rq + 4 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = (float)xv[e];
+        ss += x * x;
+        wdx += wv[e] * dy[16 * dd + 4 * rq + e] * x;
+      }
+    }
+  ss = lane_pair_sum(ss);
+  wdx = lane_pair_sum(wdx);
+  const float r = ok ? 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps) : 0.f;
+  const float coef = r * r * r * wdx * (1.0f / kHeadDim);
+#pragma unroll
+  for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const bf16x4 xv = *reinterpret_cast<const bf16x4*>(xp + 32 * dd + 8 * rq);
+      const f32x4 wv = *reinterpret_cast<const f32x4*>(w + 32 * dd + 8 * rq + 4 * hf);
+      bf16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = (float)xv[e], g = dy[16 * dd + 4 * rq + e];
+        o[e] = (bf16)(wv[e] * g * r - x * coef);
+        red[32 * dd + 8 * rq + 4 * hf + e] = g * x * r;
+      }
+      if (ok) *reinterpret_cast<bf16x4*>(dxp + 32 * dd + 8 * rq) = o;
+    }
+}
+
+// ============================================================================
+// bwd_keys_kernel: one block per (64-key tile, kv head)
+// ============================================================================
+__global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
+    const bf16* __restrict__ k, const bf16* __restrict__ v, const int32_t* __restrict__ cu,
+    const float* __restrict__ knorm_w, int T, int D, int Hkv, int n_kt, float eps,
+    double theta, int use_rope, char* __restrict__ keys) {
+  __shared__ double s_invf[64];
+  __shared__ __attribute__((aligned(16))) bf16 s_k[kKeyTile][kHeadDim + 8];
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x / Hkv, g = blockIdx.x - tile * Hkv;
+  const int t0 = tile * kKeyTile;
+  char* img = keys + ((size_t)g * n_kt + tile) * kKeyTileBytes;
+  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
+  __syncthreads();
+  // V rows straight into the V image (row r chunk c at c ^ kswz(r))
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid + kThreads * i;
+    const int r = idx >> 4, c = idx & 15;
+    const int t = t0 + r;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (t < T) val = *reinterpret_cast<const uint4*>(v + ((size_t)t * Hkv + g) * kHeadDim + 8 * c);
+    *reinterpret_cast<uint4*>(img + kKT + r * 256 + 16 * (c ^ kswz(r))) = val;
+  }
+  // K rows: RMSNorm (+RoPE), 8 lanes per token (channels 8c.. and 64+8c..)
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int r = (tid >> 3) + 32 * it;
+    const int c = tid & 7;
+    const int t = t0 + r;
+    float x[16];
+    if (t < T) {
+      const bf16* kp = k + ((size_t)t * Hkv + g) * kHeadDim;
+      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(kp + 8 * c);
+      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(kp + 64 + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = (float)lo[e];
+        x[8 + e] = (float)hi[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[e] = 0.f;
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ss += x[e] * x[e];
+    ss += __shfl_xor(ss, 1, 8);
+    ss += __shfl_xor(ss, 2, 8);
+    ss += __shfl_xor(ss, 4, 8);
+    const float inv = t < T ? 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps) : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] *= inv * knorm_w[8 * c + e];
+      x[8 + e] *= inv * knorm_w[64 + 8 * c + e];
+    }
+    if (use_rope && t < T) {
+      const int p = t - cu[doc_of_token(cu, D, t)];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float sn, cs;
+        rope_sincos_rev(p, s_invf[8 * c + e], &sn, &cs);
+        const float a = x[e], b = x[8 + e];
+        x[e] = a * cs - b * sn;
+        x[8 + e] = b * cs + a * sn;
+      }
+    }
+    bf16x8 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      lo[e] = (bf16)x[e];
+      hi[e] = (bf16)x[8 + e];
+    }
+    *reinterpret_cast<bf16x8*>(img + r * 256 + 16 * (c ^ kswz(r))) = lo;
+    *reinterpret_cast<bf16x8*>(img + r * 256 + 16 * ((c + 8) ^ kswz(r))) = hi;
+    *reinterpret_cast<bf16x8*>(&s_k[r][8 * c]) = lo;
+    *reinterpret_cast<bf16x8*>(&s_k[r][64 + 8 * c]) = hi;
+  }
+  __syncthreads();
+  // K^T: 128 channel rows x 64 keys, keys in the group order of the header,
+  // chunk tc of row d at position tc ^ vswz(d) (the forward's V^T format)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int pidx = tid + kThreads * i;
+    const int tc = pidx & 7, d = pidx >> 3;
+    const int kbase16 = 16 * (tc >> 1) + 4 * (tc & 1);
+    bf16x8 col;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) col[e] = s_k[kbase16 + 8 * (e >> 2) + (e & 3)][d];
+    *reinterpret_cast<bf16x8*>(img + 2 * kKT + d * 128 + 16 * (tc ^ vswz(d))) = col;
+  }
+}
+
+// ============================================================================
+// bwd_cols_kernel: one block per (32-column tile, kv head)
+// ============================================================================
+__global__ __launch_bounds__(kThreads) void bwd_cols_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ out, const bf16* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ sinks,
+    const int32_t* __restrict__ cu, const float* __restrict__ qnorm_w, int T, int D, int Hq,
+    int Hkv, int G, int log2G, int n_ct, float eps, double theta, int use_rope, float c_log2,
+    char* __restrict__ cols, float* __restrict__ dsink_part) {
+  __shared__ double s_invf[64];
+  __shared__ __attribute__((aligned(16))) bf16 s_q[32][kHeadDim + 8];
+  __shared__ __attribute__((aligned(16))) bf16 s_do[32][kHeadDim + 8];
+  __shared__ float s_sink[32];
+  const int tid = threadIdx.x;
+  const int ct = blockIdx.x / Hkv, g = blockIdx.x - ct * Hkv;
+  const int tpt = 32 >> log2G;
+  char* img = cols + ((size_t)g * n_ct + ct) * kColTileBytes;
+  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
+  __syncthreads();
+
+  // column col = 8 lanes: lane c holds channels 8c.. and 64+8c..
+  const int col = tid >> 3, c = tid & 7;
+  const int t = ct * tpt + (col >> log2G);
+  const int h = g * G + (col & (G - 1));
+  const bool ok = t < T;
+  float x[16], y[16], o[16];
+  if (ok) {
+    const size_t row = ((size_t)t * Hq + h) * kHeadDim;
+    const bf16x8 ql = *reinterpret_cast<const bf16x8*>(q + row + 8 * c);
+    const bf16x8 qh = *reinterpret_cast<const bf16x8*>(q + row + 64 + 8 * c);
+    const bf16x8 dl = *reinterpret_cast<const bf16x8*>(dout + row + 8 * c);
+    const bf16x8 dh = *reinterpret_cast<const bf16x8*>(dout + row + 64 + 8 * c);
+    const bf16x8 ol = *reinterpret_cast<const bf16x8*>(out + row + 8 * c);
+    const bf16x8 oh = *reinterpret_cast<const bf16x8*>(out + row + 64 + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = (float)ql[e];
+      x[8 + e] = (float)qh[e];
+      y[e] = (float)dl[e];
+      y[8 + e] = (float)dh[e];
+      o[e] = (float)ol[e];
+      o[8 + e] = (float)oh[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = y[e] = o[e] = 0.f;
+  }
+  // q_hat: RMSNorm (+RoPE), then * scale * log2(e) for the exp2 softmax
+  float ss = 0.f, dot = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    ss += x[e] * x[e];
+    dot += y[e] * o[e];
+  }
+#pragma unroll
+  for (int m = 1; m < 8; m <<= 1) {
+    ss += __shfl_xor(ss, m, 8);
+    dot += __shfl_xor(dot, m, 8);
+  }
+  const float inv = ok ? 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps) : 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[e] *= inv * qnorm_w[8 * c + e];
+    x[8 + e] *= inv * qnorm_w[64 + 8 * c + e];
+  }
+  if (use_rope && ok) {
+    const int p = t - cu[doc_of_token(cu, D, t)];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float sn, cs;
+      rope_sincos_rev(p, s_invf[8 * c + e], &sn, &cs);
+      const float a = x[e], b = x[8 + e];
+      x[e] = a * cs - b * sn;
+      x[8 + e] = b * cs + a * sn;
+    }
+  }
+  bf16x8 ql, qh, dl, dh;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ql[e] = (bf16)(x[e] * c_log2);
+    qh[e] = (bf16)(x[8 + e] * c_log2);
+    dl[e] = (bf16)y[e];
+    dh[e] = (bf16)y[8 + e];
+  }
+  // row images (row col, chunk c at c ^ kswz(col))
+  *reinterpret_cast<bf16x8*>(img + col * 256 + 16 * (c ^ kswz(col))) = ql;
+  *reinterpret_cast<bf16x8*>(img + col * 256 + 16 * ((c + 8) ^ kswz(col))) = qh;
+  *reinterpret_cast<bf16x8*>(img + kCT + col * 256 + 16 * (c ^ kswz(col))) = dl;
+  *reinterpret_cast<bf16x8*>(img + kCT + col * 256 + 16 * ((c + 8) ^ kswz(col))) = dh;
+  *reinterpret_cast<bf16x8*>(&s_q[col][8 * c]) = ql;
+  *reinterpret_cast<bf16x8*>(&s_q[col][64 + 8 * c]) = qh;
+  *reinterpret_cast<bf16x8*>(&s_do[col][8 * c]) = dl;
+  *reinterpret_cast<bf16x8*>(&s_do[col][64 + 8 * c]) = dh;
+  // per column: -lse*log2e, -D, and the sink's share -p_sink * D
+  if (c == 0) {
+    float* ld = reinterpret_cast<float*>(img + kColLd);
+    const float l = ok ? lse[(size_t)h * T + t] : INFINITY;
+    ld[col] = -l * kLog2e;
+    ld[32 + col] = -dot;
+    s_sink[col] = ok ? -__expf(sinks[h] - l) * dot : 0.f;
+  }
+  __syncthreads();
+  // transposed images: 128 channel rows x 32 columns (64 B), column groups in
+  // the header's order, chunk cc of row d at cc ^ cswz(d)
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int pidx = tid + kThreads * i;
+    const int cc = pidx & 3, d = pidx >> 2;
+    const int base = 16 * (cc >> 1) + 4 * (cc & 1);
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = s_q[base + 8 * (e >> 2) + (e & 3)][d];
+      b[e] = s_do[base + 8 * (e >> 2) + (e & 3)][d];
+    }
+    *reinterpret_cast<bf16x8*>(img + 2 * kCT + d * 64 + 16 * (cc ^ cswz(d))) = a;
+    *reinterpret_cast<bf16x8*>(img + 3 * kCT + d * 64 + 16 * (cc ^ cswz(d))) = b;
+  }
+  // dsink share of this tile per head of the group (tokens in order)
+  if (tid < G) {
+    float acc = 0.f;
+    for (int j = 0; j < tpt; ++j) acc += s_sink[j * G + tid];
+    dsink_part[((size_t)g * n_ct + ct) * G + tid] = acc;
+  }
+}
+
+// ============================================================================
+// bwd_dkdv_kernel: one block per (128-key block, kv head); 4 waves, one per SIMD
+// ============================================================================
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
+    const bf16* __restrict__ k, const char* __restrict__ keys, const char* __restrict__ cols,
+    const int32_t* __restrict__ cu, const float* __restrict__ knorm_w, int T, int D, int Hkv,
+    int log2G, int n_kt, int n_ct, int window, int use_rope, float eps, double theta,
+    bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ dwk_part) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * kColTileBytes];
+  __shared__ double s_invf[64];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, hf = lane >> 5;
+  const int kb = blockIdx.x / Hkv, g = blockIdx.x - kb * Hkv;
+  const int kb0 = kb * 128;
+  const int tpt = 32 >> log2G;
+  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
+
+  // this lane's key (column of S) and the wave's key range
+  const int u = kb0 + 32 * wave + col;
+  const bool u_ok = u < T;
+  const int uc = u_ok ? u : T - 1;
+  const int ua = kb0 + 32 * wave, ub = min(ua + 31, T - 1);
+  const int u_last = u_ok ? last_viewer(cu, D, u, window) : -1;  // visible tokens [u, u_last]
+  const int ua_last = ua < T ? last_viewer(cu, D, ua, window) : -1;
+  const int ub_last = ua < T ? last_viewer(cu, D, ub, window) : -1;
+  // the block's column tiles: tokens [kb0, last viewer of its last key]
+  const int kmax = min(kb0 + 127, T - 1);
+  const int t_hi = kb0 < T ? last_viewer(cu, D, kmax, window) : -1;
+  const int c_lo = kb0 / tpt, c_hi = t_hi >= 0 ? t_hi / tpt : c_lo - 1;
+  const char* ctiles = cols + (size_t)g * n_ct * kColTileBytes;
+
+  // K and V rows of this lane's key as B operands (channels 16kk + 8hf ..)
+  bf16x8 kB[8], vB[8];
+  {
+    const char* kimg = keys + ((size_t)g * n_kt + (uc >> 6)) * kKeyTileBytes;
+    const int r = uc & 63;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int pos = ((2 * kk + hf) ^ kswz(r)) << 4;
+      kB[kk] = rd(kimg + r * 256 + pos);
+      vB[kk] = rd(kimg + kKT + r * 256 + pos);
+    }
+  }
+  f32x16 acc_dv[4], acc_dk[4];
+  {
+    bf16x8 zero;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zero[e] = (bf16)0.f;
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd) {
+      zero_acc(acc_dv[dd], zero);
+      zero_acc(acc_dk[dd], zero);
+    }
+  }
+  // LDS read offsets: row images (rows = columns) and transposed images
+  // (rows = channels 32dd + col)
+  int roff[8], toff[4][2];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) roff[kk] = col * 256 + (((2 * kk + hf) ^ kswz(col)) << 4);
+#pragma unroll
+  for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int d = 32 * dd + col;
+      toff[dd][j] = d * 64 + (((2 * j + hf) ^ cswz(d)) << 4);
+    }
+
+  // The walk runs from the last tile down: the key blocks of a causal
+  // document all end at the document's last token, so blocks running at the
+  // same time read the same tiles and share them in L2.
+  if (c_lo <= c_hi) copy_lds(ctiles + (size_t)c_hi * kColTileBytes, kColTileBytes, tid, kThreads, lds);
+  for (int c = c_hi; c >= c_lo; --c) {
+    const int b = (c_hi - c) & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (c > c_lo)
+      copy_lds(ctiles + (size_t)(c - 1) * kColTileBytes, kColTileBytes, tid, kThreads,
+               lds + (b ^ 1) * kColTileBytes);
+    const int ta = c * tpt, tb = ta + tpt - 1;
+    // tiles the wave's keys cannot see: skip (wave-uniform)
+    if (ua > T - 1 || tb < ua || ta > ub_last) continue;
+    const bool full = ta >= ub && tb <= ua_last;
+    const char* buf = lds + b * kColTileBytes;
+    const float* ld = reinterpret_cast<const float*>(buf + kColLd);
+    // -lse*log2e and -D of the 16 columns this lane's accumulator rows hold
+    f32x16 nl, nd;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(ld + 8 * a + 4 * hf);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(ld + 32 + 8 * a + 4 * hf);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        nl[4 * a + e] = l4[e];
+        nd[4 * a + e] = d4[e];
+      }
+    }
+    // S[col][key] * log2e - lse*log2e, and dP[col][key] - D
+    f32x16 s = nl, dp = nd;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      s = mfma32(rd(buf + roff[kk]), kB[kk], s);
+      dp = mfma32(rd(buf + kCT + roff[kk]), vB[kk], dp);
+    }
+    if (!full) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = ta + ((8 * (r >> 2) + 4 * hf + (r & 3)) >> log2G);
+        s[r] += (u_ok && t >= u && t <= u_last) ? 0.f : -INFINITY;
+      }
+    }
+    // P and dS = P (dP - D), packed as B operands (16 columns per step)
+    bf16x8 pb[2], sb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float p = __builtin_amdgcn_exp2f(s[8 * j + e]);
+        pb[j][e] = (bf16)p;
+        sb[j][e] = (bf16)(p * dp[8 * j + e]);
+      }
+    // dV^T[ch][key] += dout^T P,  dK^T[ch][key] += q^T dS
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (dd == 0) {
+          mfma32_acc_nop(acc_dv[dd], rd(buf + 3 * kCT + toff[dd][j]), pb[j]);
+          mfma32_acc_nop(acc_dk[dd], rd(buf + 2 * kCT + toff[dd][j]), sb[j]);
+        } else {
+          mfma32_acc(acc_dv[dd], rd(buf + 3 * kCT + toff[dd][j]), pb[j]);
+          mfma32_acc(acc_dk[dd], rd(buf + 2 * kCT + toff[dd][j]), sb[j]);
+        }
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  agpr_fence();
+
+  // ---- epilogue: lane holds channels 32dd + 8(r/4) + 4hf + r%4 of key u ----
+  // dv: the accumulation is the gradient
+  if (u_ok) {
+    bf16* vp = dv + ((size_t)u * Hkv + g) * kHeadDim + 4 * hf;
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (bf16)acc_dv[dd][4 * rq + e];
+        *reinterpret_cast<bf16x4*>(vp + 32 * dd + 8 * rq) = w;
+      }
+  }
+  // dk_hat = ln2 * acc (q was scaled by scale*log2e); rotate back; RMSNorm
+  // bwd; dy x r per channel into LDS rows [key][channel] for the weight sum
+  {
+    float dy[64];
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dy[16 * dd + r] = acc_dk[dd][r] * kLn2;
+    const int pos = u_ok && use_rope ? u - cu[doc_of_token(cu, D, u)] : 0;
+    float* red = reinterpret_cast<float*>(lds) + (32 * wave + col) * 129;
+    norm_rope_bwd(dy, k + ((size_t)uc * Hkv + g) * kHeadDim + 4 * hf, knorm_w, u_ok,
+                  use_rope != 0, pos, s_invf, eps, hf,
+                  dk + ((size_t)uc * Hkv + g) * kHeadDim + 4 * hf, red);
+  }
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float acc = 0.f;
+    const float* red = reinterpret_cast<const float*>(lds);
+    for (int kr = 0; kr < 128; ++kr) acc += red[kr * 129 + tid];
+    dwk_part[(size_t)blockIdx.x * kHeadDim + tid] = acc;
+  }
+}
+
+// ============================================================================
+// bwd_dq_kernel: one block per (256-column block, kv head); 8 waves
+// ============================================================================
+constexpr int kDqWaves = 8;
+constexpr int kDqThreads = kDqWaves * 64;
+
+__global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
+    const bf16* __restrict__ q, const char* __restrict__ keys, const char* __restrict__ cols,
+    const int32_t* __restrict__ cu, const float* __restrict__ qnorm_w, int T, int D, int Hq,
+    int Hkv, int G, int log2G, int n_kt, int n_ct, int window, int use_rope, float eps,
+    double theta, float scale, bf16* __restrict__ dq, float* __restrict__ dwq_part) {
+  // two key tiles while walking, 256 x 129 floats in the epilogue
+  constexpr int kLdsBytes = 2 * kKeyTileBytes > 32 * kDqWaves * 129 * 4
+                                ? 2 * kKeyTileBytes : 32 * kDqWaves * 129 * 4;
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  __shared__ double s_invf[64];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, hf = lane >> 5;
+  const int n_qb = (n_ct + kDqWaves - 1) / kDqWaves;
+  // longest blocks (latest tokens) first
+  const int qb = n_qb - 1 - (int)(blockIdx.x / Hkv), g = blockIdx.x % Hkv;
+  const int tpt = 32 >> log2G;
+  const int ct = qb * kDqWaves + wave;  // this wave's column tile
+  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
+
+  // this lane's column: token t, head h
+  const int t = ct * tpt + (col >> log2G);
+  const int h = g * G + (col & (G - 1));
+  const bool t_ok = ct < n_ct && t < T;
+  const int tcl = t_ok ? t : 0;
+  const int t_lo = t_ok ? first_key(cu, D, t, window) : 1 << 30;  // visible keys [t_lo, t]
+  // the wave's tokens and the block's key range
+  const int ta = ct * tpt, tb = min(ta + tpt - 1, T - 1);
+  const bool wave_ok = ct < n_ct && ta < T;
+  const int a0 = qb * kDqWaves * tpt;
+  const int a1 = min((qb + 1) * kDqWaves * tpt, T);
+  const int lo = a0 < T ? first_key(cu, D, a0, window) : 0;
+  const int kt_lo = lo & ~(kKeyTile - 1);
+  const int n_tiles = a0 < a1 ? (a1 - kt_lo + kKeyTile - 1) / kKeyTile : 0;
+  const int wa_lo = wave_ok ? first_key(cu, D, ta, window) : 0;
+  const int wb_lo = wave_ok ? first_key(cu, D, tb, window) : 0;
+  const char* ktiles = keys + (size_t)g * n_kt * kKeyTileBytes;
+
+  // q (scaled) and dout rows of this lane's column as B operands, -lse*log2e, -D
+  bf16x8 qB[8], dB[8];
+  float nlse = -INFINITY, nD = 0.f;
+  {
+    const int ctc = min(ct, n_ct - 1);
+    const char* cimg = cols + ((size_t)g * n_ct + ctc) * kColTileBytes;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int off = col * 256 + (((2 * kk + hf) ^ kswz(col)) << 4);
+      qB[kk] = rd(cimg + off);
+      dB[kk] = rd(cimg + kCT + off);
+    }
+    if (t_ok) {
+      nlse = reinterpret_cast<const float*>(cimg + kColLd)[col];
+      nD = reinterpret_cast<const float*>(cimg + kColLd)[32 + col];
+    }
+  }
+  f32x16 acc[4];
+  {
+    bf16x8 zero;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zero[e] = (bf16)0.f;
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd) zero_acc(acc[dd], zero);
+  }
+  int koff[8], voff[4];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) koff[kk] = col * 256 + (((2 * kk + hf) ^ kswz(col)) << 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) voff[j] = col * 128 + (((2 * j + hf) ^ vswz(col)) << 4);
+  f32x16 nl16, nd16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    nl16[r] = nlse;
+    nd16[r] = nD;
+  }
+
+  if (n_tiles > 0)
+    copy_lds(ktiles + (size_t)(kt_lo >> 6) * kKeyTileBytes, kKeyTileBytes, tid, kDqThreads, lds);
+  for (int j = 0; j < n_tiles; ++j) {
+    const int b = j & 1;
+    const int kt = kt_lo + j * kKeyTile;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (j + 1 < n_tiles)
+      copy_lds(ktiles + (size_t)((kt >> 6) + 1) * kKeyTileBytes, kKeyTileBytes, tid,
+               kDqThreads, lds + (b ^ 1) * kKeyTileBytes);
+    // keys of the tile this wave's tokens cannot see: skip (wave-uniform)
+    if (!wave_ok || kt > tb || kt + kKeyTile - 1 < wa_lo) continue;
+    const bool full = kt + kKeyTile - 1 <= ta && kt >= wb_lo;
+    const char* buf = lds + b * kKeyTileBytes;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      // S^T[key][col] * log2e - lse*log2e and dP^T - D for 32 keys
+      f32x16 s = nl16, dp = nd16;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        s = mfma32(rd(buf + kh * 8192 + koff[kk]), qB[kk], s);
+        dp = mfma32(rd(buf + kKT + kh * 8192 + koff[kk]), dB[kk], dp);
+      }
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
+          s[r] += (key >= t_lo && key <= t) ? 0.f : -INFINITY;
+        }
+      }
+      bf16x8 sb[2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sb[jj][e] = (bf16)(__builtin_amdgcn_exp2f(s[8 * jj + e]) * dp[8 * jj + e]);
+      // dq^T[ch][col] += K^T[ch][key] dS^T[key][col]
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          if (dd == 0)
+            mfma32_acc_nop(acc[dd], rd(buf + 2 * kKT + dd * 4096 + voff[2 * kh + jj]), sb[jj]);
+          else
+            mfma32_acc(acc[dd], rd(buf + 2 * kKT + dd * 4096 + voff[2 * kh + jj]), sb[jj]);
+        }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  agpr_fence();
+
+  // ---- epilogue: dq_hat = scale * acc; rotate back; RMSNorm bwd; dy x r per
+  // channel into LDS rows [column][channel], summed over the 256 columns ----
+  {
+    float dy[64];
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dy[16 * dd + r] = acc[dd][r] * scale;
+    const int pos = t_ok && use_rope ? t - cu[doc_of_token(cu, D, t)] : 0;
+    float* red = reinterpret_cast<float*>(lds) + (32 * wave + col) * 129;
+    norm_rope_bwd(dy, q + ((size_t)tcl * Hq + h) * kHeadDim + 4 * hf, qnorm_w, t_ok,
+                  use_rope != 0, pos, s_invf, eps, hf,
+                  dq + ((size_t)tcl * Hq + h) * kHeadDim + 4 * hf, red);
+  }
+  __syncthreads();
+  float part = 0.f;
+  if (tid < kHeadDim) {
+    const float* red = reinterpret_cast<const float*>(lds);
+    for (int cr = 0; cr < 32 * kDqWaves; ++cr) part += red[cr * 129 + tid];
+  }
+  if (tid < kHeadDim) dwq_part[(size_t)blockIdx.x * kHeadDim + tid] = part;
+}
+
+// ============================================================================
+// bwd_reduce_kernel: one block per output (Hq sinks, then 128 + 128 norm
+// weight channels); thread i sums partials i, i + 256, ... and a tree in LDS
+// adds the 256 sums, so the order is fixed and the result deterministic
+// ============================================================================
+__global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(
+    const float* __restrict__ dsink_part, const float* __restrict__ dwq_part,
+    const float* __restrict__ dwk_part, int Hq, int G, int n_ct, int n_qblk, int n_kblk,
+    float* __restrict__ dsinks, float* __restrict__ dqnorm_w, float* __restrict__ dknorm_w) {
+  __shared__ float s_red[kThreads];
+  const int tid = threadIdx.x;
+  const int o = blockIdx.x;
+  const float* src;
+  size_t stride;
+  int n;
+  float* dst;
+  if (o < Hq) {
+    const int g = o / G;
+    src = dsink_part + (size_t)g * n_ct * G + (o - g * G);
+    stride = G;
+    n = n_ct;
+    dst = dsinks + o;
+  } else if (o < Hq + kHeadDim) {
+    src = dwq_part + (o - Hq);
+    stride = kHeadDim;
+    n = n_qblk;
+    dst = dqnorm_w + (o - Hq);
+  } else {
+    src = dwk_part + (o - Hq - kHeadDim);
+    stride = kHeadDim;
+    n = n_kblk;
+    dst = dknorm_w + (o - Hq - kHeadDim);
+  }
+  float acc = 0.f;
+  for (int i = tid; i < n; i += kThreads) acc += src[(size_t)i * stride];
+  s_red[tid] = acc;
+  __syncthreads();
+#pragma unroll
+  for (int m = kThreads / 2; m > 0; m >>= 1) {
+    if (tid < m) s_red[tid] += s_red[tid + m];
+    __syncthreads();
+  }
+  if (tid == 0) *dst = s_red[0];
+}
+
+}  // namespace
+
+BwdWorkspace plan_bwd_workspace(int64_t T, int Hq, int Hkv) {
+  BwdWorkspace w;
+  if (T <= 0) return w;
+  const int G = Hq / Hkv;
+  const int tpt = 32 / G;
+  w.n_kt = (T + kKeyTile - 1) / kKeyTile;
+  w.n_ct = (T + tpt - 1) / tpt;
+  w.n_kblk = (int64_t)((T + 127) / 128) * Hkv;
+  w.n_qblk = (int64_t)((w.n_ct + kDqWaves - 1) / kDqWaves) * Hkv;
+  size_t off = 0;
+  w.keys_off = off;
+  off += (size_t)Hkv * w.n_kt * kKeyTileBytes;
+  w.cols_off = off = round_up(off, 256);
+  off += (size_t)Hkv * w.n_ct * kColTileBytes;
+  w.dsink_off = off = round_up(off, 256);
+  off += sizeof(float) * (size_t)Hkv * w.n_ct * G;
+  w.dwq_off = off = round_up(off, 256);
+  off += sizeof(float) * (size_t)w.n_qblk * kHeadDim;
+  w.dwk_off = off = round_up(off, 256);
+  off += sizeof(float) * (size_t)w.n_kblk * kHeadDim;
+  w.total = round_up(off, 256);
+  return w;
+}
+
+hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const int32_t* cu,
+                           const float* sinks, const float* qnorm_w, const float* knorm_w,
+                           const bf16* out, const float* lse, const bf16* dout, bf16* dq,
+                           bf16* dk, bf16* dv, float* dsinks, float* dqnorm_w,
+                           float* dknorm_w, int T, int D, int Hq, int Hkv, int window,
+                           int use_rope, double eps, double theta, double scale, char* ws,
+                           const BwdWorkspace& w, hipStream_t stream) {
+  const int G = Hq / Hkv;
+  int log2G = 0;
+  while ((1 << log2G) < G) ++log2G;
+  char* keys = ws + w.keys_off;
+  char* cols = ws + w.cols_off;
+  float* dsink_part = reinterpret_cast<float*>(ws + w.dsink_off);
+  float* dwq_part = reinterpret_cast<float*>(ws + w.dwq_off);
+  float* dwk_part = reinterpret_cast<float*>(ws + w.dwk_off);
+  const float c_log2 = (float)(scale * 1.4426950408889634);
+  bwd_keys_kernel<<<dim3((unsigned)(w.n_kt * Hkv)), dim3(kThreads), 0, stream>>>(
+      k, v, cu, knorm_w, T, D, Hkv, (int)w.n_kt, (float)eps, theta, use_rope, keys);
+  bwd_cols_kernel<<<dim3((unsigned)(w.n_ct * Hkv)), dim3(kThreads), 0, stream>>>(
+      q, out, dout, lse, sinks, cu, qnorm_w, T, D, Hq, Hkv, G, log2G, (int)w.n_ct, (float)eps,
+      theta, use_rope, c_log2, cols, dsink_part);
+  bwd_dkdv_kernel<<<dim3((unsigned)w.n_kblk), dim3(kThreads), 0, stream>>>(
+      k, keys, cols, cu, knorm_w, T, D, Hkv, log2G, (int)w.n_kt, (int)w.n_ct, window, use_rope,
+      (float)eps, theta, dk, dv, dwk_part);
+  bwd_dq_kernel<<<dim3((unsigned)w.n_qblk), dim3(kDqThreads), 0, stream>>>(
+      q, keys, cols, cu, qnorm_w, T, D, Hq, Hkv, G, log2G, (int)w.n_kt, (int)w.n_ct, window,
+      use_rope, (float)eps, theta, (float)scale, dq, dwq_part);
+  bwd_reduce_kernel<<<dim3(Hq + 2 * kHeadDim), dim3(kThreads), 0, stream>>>(
+      dsink_part, dwq_part, dwk_part, Hq, G, (int)w.n_ct, (int)w.n_qblk, (int)w.n_kblk,
+      dsinks, dqnorm_w, dknorm_w);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -59,6 +59,22 @@ inline int64_t wide_grid(int64_t items_ub, int Hkv) {
 
 Workspace plan_workspace(int64_t T, int64_t D, int Hq, int Hkv, int d, int dtype);
 
+// Backward workspace (bf16): per kv head, 48 KiB key-tile images (64 keys:
+// k_hat rows, V rows, K^T) and 36 KiB column-tile images (32 query columns:
+// scaled q_hat rows, dout rows, their transposes, -lse and -D), then fp32
+// partial sums of dsink (per column tile and head) and of the two norm-weight
+// gradients (per dK/dV and dQ workgroup).
+struct BwdWorkspace {
+  int64_t n_kt = 0;    // 64-key tiles per kv head
+  int64_t n_ct = 0;    // 32-column tiles per kv head (32 / G tokens each)
+  int64_t n_kblk = 0;  // dK/dV workgroups (128 keys x kv head)
+  int64_t n_qblk = 0;  // dQ workgroups (256 columns x kv head)
+  size_t keys_off = 0, cols_off = 0, dsink_off = 0, dwq_off = 0, dwk_off = 0;
+  size_t total = 0;
+};
+
+BwdWorkspace plan_bwd_workspace(int64_t T, int Hq, int Hkv);
+
 // ---- launch wrappers (return hipGetLastError after the launches) ----------
 
 hipError_t launch_prologue_bf16(const bf16* k, const bf16* v, const int32_t* cu,
@@ -82,6 +98,14 @@ hipError_t launch_attention_bf16_wide(const bf16* q, const bf16* khat, const bf1
                                       int Hkv, int64_t t_pad, int64_t items_ub, int window,
                                       int use_rope, double eps, double theta, double scale,
                                       bool exact_all, hipStream_t stream);
+
+hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const int32_t* cu,
+                           const float* sinks, const float* qnorm_w, const float* knorm_w,
+                           const bf16* out, const float* lse, const bf16* dout, bf16* dq,
+                           bf16* dk, bf16* dv, float* dsinks, float* dqnorm_w,
+                           float* dknorm_w, int T, int D, int Hq, int Hkv, int window,
+                           int use_rope, double eps, double theta, double scale, char* ws,
+                           const BwdWorkspace& w, hipStream_t stream);
 
 hipError_t launch_prologue_f32(const float* k, const float* v, const int32_t* cu,
                                const float* knorm_w, int T, int D, int Hkv, int d,

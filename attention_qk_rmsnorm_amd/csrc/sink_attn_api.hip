@@ -198,6 +198,47 @@ int launch_attention(const sink_attn_desc* d, const void* q, const int32_t* cu, 
   return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;
 }
 
+sa::BwdWorkspace plan_bwd(const sink_attn_desc* d) {
+  return sa::plan_bwd_workspace(d->total_tokens, d->num_q_heads, d->num_kv_heads);
+}
+
+int check_bwd(const sink_attn_desc* d, const void* q, const void* k, const void* v,
+              const int32_t* cu, const float* sinks, const float* qnorm_w,
+              const float* knorm_w, int32_t window, int32_t use_rope, const void* out,
+              const float* lse, const void* dout, const void* dq, const void* dk,
+              const void* dv, const float* dsinks, const float* dqnorm_w,
+              const float* dknorm_w) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (d->dtype != SINK_ATTN_BF16) return SINK_ATTN_EUNSUPPORTED;
+  if (window == 0) return SINK_ATTN_EINVAL;
+  if (use_rope != 0 && use_rope != 1) return SINK_ATTN_EINVAL;
+  if (cu == nullptr || !aligned(cu, 4)) return SINK_ATTN_EINVAL;
+  if (sinks == nullptr || qnorm_w == nullptr || knorm_w == nullptr || dsinks == nullptr ||
+      dqnorm_w == nullptr || dknorm_w == nullptr)
+    return SINK_ATTN_EINVAL;
+  const float* f32s[] = {sinks, qnorm_w, knorm_w, dsinks, dqnorm_w, dknorm_w};
+  for (const float* p : f32s)
+    if (!aligned(p, 4)) return SINK_ATTN_EINVAL;
+  if (d->total_tokens == 0) return SINK_ATTN_OK;
+  const void* io[] = {q, k, v, out, dout, dq, dk, dv};
+  for (const void* p : io)
+    if (p == nullptr || !aligned(p, 16)) return SINK_ATTN_EINVAL;
+  if (lse == nullptr || !aligned(lse, 4)) return SINK_ATTN_EINVAL;
+  const sa::BwdWorkspace w = plan_bwd(d);
+  if (d->workspace == nullptr || d->workspace_bytes < w.total || !aligned(d->workspace, 256))
+    return SINK_ATTN_EWORKSPACE;
+  return SINK_ATTN_OK;
+}
+
+// Zero-token calls still define the parameter gradients: zero them.
+__global__ void zero_f32_kernel(float* a, int na, float* b, int nb, float* c, int nc) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < na) a[i] = 0.f;
+  if (i < nb) b[i] = 0.f;
+  if (i < nc) c[i] = 0.f;
+}
+
 }  // namespace
 
 extern "C" {
@@ -241,6 +282,38 @@ int sink_attn_fwd(const sink_attn_desc* desc, const void* q, const void* k, cons
   return launch_attention(desc, q, cu_seqlens, sinks, qnorm_w, window, use_rope, out, lse, s);
 }
 
+size_t sink_attn_bwd_workspace_bytes(const sink_attn_desc* desc) {
+  if (check_desc(desc) != SINK_ATTN_OK || desc->dtype != SINK_ATTN_BF16) return 0;
+  return plan_bwd(desc).total;
+}
+
+int sink_attn_bwd(const sink_attn_desc* desc, const void* q, const void* k, const void* v,
+                  const int32_t* cu_seqlens, const float* sinks, const float* qnorm_w,
+                  const float* knorm_w, int32_t window, int32_t use_rope, const void* out,
+                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                  float* dsinks, float* dqnorm_w, float* dknorm_w, void* stream) {
+  const int rc = check_bwd(desc, q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window,
+                           use_rope, out, lse, dout, dq, dk, dv, dsinks, dqnorm_w, dknorm_w);
+  if (rc != SINK_ATTN_OK) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int Hq = desc->num_q_heads, dh = desc->head_dim;
+  if (desc->total_tokens == 0) {
+    const int n = Hq > dh ? Hq : dh;
+    zero_f32_kernel<<<dim3((n + 255) / 256), dim3(256), 0, s>>>(dsinks, Hq, dqnorm_w, dh,
+                                                                 dknorm_w, dh);
+    return hipGetLastError() == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;
+  }
+  using sa::bf16;
+  const hipError_t e = sa::launch_bwd_bf16(
+      static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+      cu_seqlens, sinks, qnorm_w, knorm_w, static_cast<const bf16*>(out), lse,
+      static_cast<const bf16*>(dout), static_cast<bf16*>(dq), static_cast<bf16*>(dk),
+      static_cast<bf16*>(dv), dsinks, dqnorm_w, dknorm_w, desc->total_tokens, desc->num_docs,
+      Hq, desc->num_kv_heads, window, use_rope, desc->rms_eps, desc->rope_theta,
+      softmax_scale(desc), static_cast<char*>(desc->workspace), plan_bwd(desc), s);
+  return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;
+}
+
 int sink_attn_tile_config(const sink_attn_desc* desc, int32_t window) {
   const int rc = check_desc(desc);
   if (rc != SINK_ATTN_OK) return rc;
@@ -260,6 +333,6 @@ const char* sink_attn_status_string(int status) {
   }
 }
 
-int sink_attn_version(void) { return 200; }
+int sink_attn_version(void) { return 300; }
 
 }  // extern "C"

@@ -1,6 +1,6 @@
 """Benchmark of the sink-aware GQA attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload full] [--pass fwd|bwd]
 
 A step is one sink_attn_fwd call (K prologue + varlen schedule, then attention
 with the fused Q prologue) over one synthetic batch already resident in HBM.
@@ -17,6 +17,11 @@ and the fp64 CPU oracle timed on a bounded sample of the same workload.  The
 attention stage is one launch of the narrow-tile kernel or, with wide tiles,
 the main launch plus the follow-up that reruns the (normally no) blocks whose
 fixed softmax reference proved too low; the events cover both.
+
+--pass bwd times the backward instead: a step is one sink_attn_bwd call (key
+and column tile preparation, the dK/dV and dQ kernels, the final sums) on the
+out and lse of one forward, counted as 2.5 forward passes
+(FLOP = 10 * head_dim * Hq * N_vis: recomputed scores, dP, dV, dK and dQ).
 """
 from __future__ import annotations
 
@@ -34,6 +39,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "sink-attn fwd TFLOP/s (visible entries) + % bf16 MFMA peak, 32q/4kv d128, 1 GPU"
+METRIC_BWD = ("sink-attn bwd TFLOP/s (visible entries, 10*d*Hq per entry) + % bf16 MFMA peak, "
+              "32q/4kv d128, 1 GPU")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 CSRC = os.path.join(ROOT, "attention_qk_rmsnorm_amd", "csrc")
@@ -125,6 +132,110 @@ def cpu_baseline(inp, w, out_gpu, lse_gpu, target_seconds: float):
     }
 
 
+def cpu_baseline_bwd(w, target_seconds: float):
+    """The fp64 backward oracle as it stands on a prefix of the workload's first
+    document, taken as a document of its own, sized to about target_seconds."""
+    import oracle.oracle as O
+    import workloads
+
+    def run(L):
+        sub = workloads.custom_workload([L], w.num_q_heads, w.num_kv_heads, w.head_dim, w.dtype,
+                                        w.window, w.use_rope, w.sink_mean)
+        inp = workloads.make_inputs(sub, seed=0)
+        dout = workloads.make_grad_output(sub, seed=0)
+        f = lambda t: t.double().numpy()  # noqa: E731
+        t0 = time.perf_counter()
+        O.sink_attn_bwd(f(inp["q"]), f(inp["k"]), f(inp["v"]), inp["cu_seqlens"].numpy(),
+                        f(inp["sinks"]), f(inp["qnorm_w"]), f(inp["knorm_w"]), w.window,
+                        w.use_rope, f(dout), eps=w.rms_eps, theta=w.rope_theta)
+        return time.perf_counter() - t0
+
+    L = min(256, w.lengths[0])
+    dt = run(L)                                   # calibration run (not reported)
+    rate = visible_entries([L], w.window) / max(dt, 1e-6)
+    L = max(L, min(w.lengths[0], 8192))
+    while L > 256 and visible_entries([L], w.window) / rate > target_seconds:
+        L = int(L * 0.8)
+    dt = run(L)
+    n_vis = visible_entries([L], w.window)
+    flop = 10.0 * w.head_dim * w.num_q_heads * n_vis
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": O.max_threads(),
+        "kind": "oracle",
+        "sample": (f"backward of the first {L} tokens of the workload's first document as a "
+                   f"document of its own, all {w.num_q_heads} heads ({n_vis} visible entries "
+                   f"per head, {flop:.3e} FLOP), fp64, {dt:.1f} s"),
+        "seconds": dt,
+    }
+
+
+def run_bwd(args, A, w, d_inp, call, dev):
+    import torch
+    import workloads
+
+    call.fwd()
+    dout = workloads.make_grad_output(w, seed=0).to(dev)
+    torch.cuda.synchronize()
+    bc = A.BwdCall(d_inp["q"], d_inp["k"], d_inp["v"], d_inp["cu_seqlens"], d_inp["sinks"],
+                   d_inp["qnorm_w"], d_inp["knorm_w"], w.window, w.use_rope, call.out, call.lse,
+                   dout, rms_eps=w.rms_eps, rope_theta=w.rope_theta)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        bc.run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        bc.run()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    n_vis = visible_entries(w.lengths, w.window)
+    flop = 10.0 * w.head_dim * w.num_q_heads * n_vis
+    value = flop / (ms_step * 1e-3) / 1e12
+    achieved = flop / (call_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC_BWD,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name} backward: {w.description}",
+            "tokens": w.total_tokens, "docs": w.num_docs, "q_heads": w.num_q_heads,
+            "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "window": w.window,
+            "rope": w.use_rope, "visible_entries": n_vis, "flop_per_step": flop,
+            "parallelism": "single GPU",
+        },
+        "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "sink_attn_bwd (all five launches)",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "avg_launch_ms": call_ms,
+        },
+    }
+    result["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_seconds) if args.cpu_seconds > 0
+                              else None)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -135,6 +246,8 @@ def main():
                     choices=["full", "sliding", "long", "mixed_sliding", "mixed_causal"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target host time of the oracle sample (0 skips the CPU baseline)")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
+                    help="time the forward (default) or the backward pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -175,6 +288,9 @@ def main():
     call = A.Call(d_inp["q"], d_inp["k"], d_inp["v"], d_inp["cu_seqlens"], d_inp["sinks"],
                   d_inp["qnorm_w"], d_inp["knorm_w"], w.window, w.use_rope,
                   rms_eps=w.rms_eps, rope_theta=w.rope_theta)
+    if args.which == "bwd":
+        run_bwd(args, A, w, d_inp, call, dev)
+        return
     stream = torch.cuda.current_stream(dev)
     tile = A.tile_config(call.desc, w.window)
     kernel, kernel_src = ATTN_KERNELS[tile]

@@ -2,7 +2,7 @@
  * sink_attn.h -- C ABI of the MI355X (gfx950) sink-aware grouped-query
  * attention forward pass: per-head RMSNorm and NeoX RoPE on Q and K, then
  * causal or sliding-window attention over packed variable-length documents
- * with one learned fp32 sink logit per query head.
+ * with one learned fp32 sink logit per query head -- and its backward pass.
  *
  * Sources (NeMo AutoModel API reference pages):
  *   "flint.layers"     FlintAttention: separate Q/K/V, per-head RMSNorm,
@@ -16,6 +16,10 @@
  *                      rms_norm_eps 1e-6; full layers have no RoPE, sliding
  *                      layers rotate all channels; the window counts the
  *                      current token.
+ *   "flint.layers"     (backward) the sinks are trainable parameters
+ *                      (_FlintSinkParameters) and q_norm / k_norm are RMSNorm
+ *                      modules with weights, so a training step needs the
+ *                      gradients of q, k, v, the sinks and both weights.
  *   "attention.utils"  preprocess_args_and_kwargs_for_attn: THD tensors
  *                      [tokens, heads, head_dim], K and V share a layout,
  *                      int32 cu_seqlens [documents + 1], a positive left
@@ -151,6 +155,35 @@ int sink_attn_attention(const sink_attn_desc* desc, const void* q,
  * document length T / D), or half the mean length when causal, is at least
  * 2048 keys.  Reads no device memory. */
 int sink_attn_tile_config(const sink_attn_desc* desc, int32_t window);
+
+/* Bytes of device workspace sink_attn_bwd needs for this descriptor (0 when
+ * T == 0, for the fp32 path, or for an invalid descriptor).  The forward's
+ * workspace can be reused once the forward has completed; the backward does
+ * not read what the forward left there. */
+size_t sink_attn_bwd_workspace_bytes(const sink_attn_desc* desc);
+
+/* Backward pass of sink_attn_fwd (bf16 only): the gradients of
+ * L = sum(dout * out) with respect to every input of the forward.
+ *   q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope
+ *               exactly as passed to the forward
+ *   out [T,Hq,d] bf16 and lse fp32 [Hq,T]: what that forward wrote (lse is
+ *               required here)
+ *   dout        [T,Hq,d] bf16, the gradient of the loss with respect to out
+ *   dq [T,Hq,d], dk [T,Hkv,d], dv [T,Hkv,d]   bf16, fully overwritten
+ *   dsinks fp32 [Hq], dqnorm_w fp32 [d], dknorm_w fp32 [d]   overwritten, not
+ *               accumulated (zero when T == 0)
+ * desc->workspace must hold sink_attn_bwd_workspace_bytes(desc) bytes
+ * (256-byte aligned); every bf16 tensor 16-byte aligned.  Gradients through
+ * the softmax use D = dout . out per (token, head) with the bf16 out.  The
+ * sums over tokens (dsinks, norm weights) are added in a fixed order: equal
+ * inputs give bitwise equal outputs.  fp32 descriptors return
+ * SINK_ATTN_EUNSUPPORTED. */
+int sink_attn_bwd(const sink_attn_desc* desc, const void* q, const void* k,
+                  const void* v, const int32_t* cu_seqlens, const float* sinks,
+                  const float* qnorm_w, const float* knorm_w, int32_t window,
+                  int32_t use_rope, const void* out, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, float* dsinks,
+                  float* dqnorm_w, float* dknorm_w, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* sink_attn_status_string(int status);

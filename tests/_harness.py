@@ -94,3 +94,76 @@ def check_parity(inp: dict, window: int, use_rope: bool, rows=None, label="", **
 def custom_inputs(lengths, Hq=32, Hkv=4, d=128, dtype="bf16", sink_mean=0.0, seed=0):
     w = workloads.custom_workload(lengths, Hq, Hkv, d, dtype, sink_mean=sink_mean)
     return workloads.make_inputs(w, seed=seed)
+
+
+# ---- backward ----------------------------------------------------------------
+# Gradient tensors scale with the number of terms they collect (a key early in
+# a long causal document gathers P * dout from every later token and head), so
+# the bf16 bound is taken relative to each reference tensor's largest entry:
+# max |got - ref| <= BWD_REL_MAX * max|ref| and
+# mean |got - ref| <= BWD_REL_MEAN * mean|ref|.
+BWD_REL_MAX, BWD_REL_MEAN = 2e-2, 1e-2
+GRAD_KEYS = ("dq", "dk", "dv", "dsinks", "dqnorm_w", "dknorm_w")
+
+
+def gpu_backward(inp_dev: dict, window: int, use_rope: bool, dout=None, seed=0,
+                 return_forward=False, **kw):
+    """Forward then backward through the C ABI; dout from the seeded generator
+    unless given."""
+    import attention_qk_rmsnorm_amd as A
+    if dout is None:
+        T, Hq, d = inp_dev["q"].shape
+        w = workloads.Workload("g", (T,), Hq, inp_dev["k"].shape[1], d, "bf16")
+        dout = workloads.make_grad_output(w, seed).to(inp_dev["q"].device)
+    fkw = {k: v for k, v in kw.items() if k in ("rms_eps", "rope_theta", "softmax_scale")}
+    out, lse = A.sink_attn_fwd(inp_dev["q"], inp_dev["k"], inp_dev["v"], inp_dev["cu_seqlens"],
+                               inp_dev["sinks"], inp_dev["qnorm_w"], inp_dev["knorm_w"],
+                               window, use_rope, **kw)
+    g = A.sink_attn_bwd(inp_dev["q"], inp_dev["k"], inp_dev["v"], inp_dev["cu_seqlens"],
+                        inp_dev["sinks"], inp_dev["qnorm_w"], inp_dev["knorm_w"], window,
+                        use_rope, out, lse, dout, **fkw)
+    torch.cuda.synchronize()
+    if return_forward:
+        return g, out, dout
+    return g
+
+
+def oracle_backward(inp: dict, window: int, use_rope: bool, dout, eps=1e-6, theta=1e6,
+                    scale=None):
+    import oracle.oracle as O
+    f = lambda t: t.double().numpy()  # noqa: E731
+    return O.sink_attn_bwd(f(inp["q"]), f(inp["k"]), f(inp["v"]), inp["cu_seqlens"].numpy(),
+                           f(inp["sinks"]), f(inp["qnorm_w"]), f(inp["knorm_w"]), window,
+                           use_rope, f(dout), eps=eps, theta=theta, scale=scale)
+
+
+def check_bwd_parity(inp: dict, window: int, use_rope: bool, label="", seed=0, **kw):
+    """Backward on the GPU and in the oracle on the same bits; assert the
+    relative bound on every gradient tensor.  Returns the GPU gradients."""
+    T, Hq, d = inp["q"].shape
+    w = workloads.Workload("g", (T,), Hq, inp["k"].shape[1], d, "bf16")
+    dout = workloads.make_grad_output(w, seed)
+    dev = to_device(inp)
+    g = gpu_backward(dev, window, use_rope, dout=dout.to("cuda:0"), **kw)
+    ref = oracle_backward(inp, window, use_rope, dout, eps=kw.get("rms_eps", 1e-6),
+                          theta=kw.get("rope_theta", 1e6), scale=kw.get("softmax_scale"))
+    msg = []
+    bad = []
+    for key in GRAD_KEYS:
+        got = g[key].float().cpu().numpy().astype(np.float64)
+        r = ref[key]
+        assert np.all(np.isfinite(got)), f"{label}: non-finite {key}"
+        if r.size == 0:
+            continue
+        emax, emean = errors(got, r)
+        smax = float(np.abs(r).max())
+        smean = float(np.abs(r).mean())
+        rel_max = emax / smax if smax > 0 else emax
+        rel_mean = emean / smean if smean > 0 else emean
+        msg.append(f"{key} {rel_max:.2e}/{rel_mean:.2e}")
+        if rel_max > BWD_REL_MAX or rel_mean > BWD_REL_MEAN:
+            bad.append(f"{key}: max {emax:.3e} (scale {smax:.3e}) mean {emean:.3e} "
+                       f"(scale {smean:.3e})")
+    print(f"  {label}: rel max/mean " + ", ".join(msg), flush=True)
+    assert not bad, f"{label}: " + "; ".join(bad)
+    return g

@@ -26,7 +26,8 @@ def test_every_declared_symbol_is_exported(A):
     names = A.header_functions()
     assert set(names) >= {"sink_attn_fwd", "sink_attn_workspace_bytes",
                           "sink_attn_status_string", "sink_attn_prologue",
-                          "sink_attn_attention", "sink_attn_version", "sink_attn_tile_config"}
+                          "sink_attn_attention", "sink_attn_version", "sink_attn_tile_config",
+                          "sink_attn_bwd", "sink_attn_bwd_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -205,3 +206,71 @@ def test_forced_tile_choice_and_fp32(A):
     assert A.sink_attn_tile_config(100, 1, 32, 4, 128, -1, tile_config=3) == 3
     with pytest.raises(A.SinkAttnError):
         A.sink_attn_tile_config(128, 1, 32, 4, 128, -1, tile_config=5)
+
+
+def test_bwd_workspace_bytes(A):
+    assert A.sink_attn_bwd_workspace_bytes(0, 0, 32, 4, 128) == 0
+    assert A.sink_attn_bwd_workspace_bytes(128, 1, 4, 1, 64, A.SINK_ATTN_F32) == 0
+    assert A.sink_attn_bwd_workspace_bytes(100, 1, 32, 5, 128) == 0     # invalid: 32 % 5
+    assert A.load_library().sink_attn_bwd_workspace_bytes(None) == 0
+    a = A.sink_attn_bwd_workspace_bytes(1000, 3, 32, 4, 128)
+    T = 32768
+    b = A.sink_attn_bwd_workspace_bytes(T, 1, 32, 4, 128)
+    assert 0 < a < b and a % 256 == 0 and b % 256 == 0
+    # per kv head: 48 KiB per 64 keys, 36 KiB per 32 query columns (4 tokens at G = 8)
+    assert b >= 4 * (T // 64) * 48 * 1024 + 4 * (T // 4) * 36 * 1024
+    assert b < 1.05 * (4 * (T // 64) * 48 * 1024 + 4 * (T // 4) * 36 * 1024)
+
+
+def _bwd(A, desc, window=-1, use_rope=0, **ptrs):
+    names = ["q", "k", "v", "cu", "sinks", "qw", "kw", "out", "lse", "dout", "dq", "dk", "dv",
+             "dsinks", "dqw", "dkw"]
+    p = {n: FAKE for n in names}
+    p.update(ptrs)
+    P = ctypes.c_void_p
+    a = [P(p[n]) for n in names]
+    return A.load_library().sink_attn_bwd(ctypes.byref(desc) if desc is not None else None,
+                                          *a[:7], window, use_rope, *a[7:], None)
+
+
+def _bwd_desc(A, **kw):
+    desc = _desc(A, **kw)
+    need = A.bwd_workspace_bytes(desc)
+    desc.workspace = 0x10000000 if need else None
+    desc.workspace_bytes = need
+    return desc
+
+
+@pytest.mark.parametrize("case, expected", [
+    ("null_desc", EINVAL), ("window_zero", EINVAL), ("use_rope_two", EINVAL),
+    ("null_lse", EINVAL), ("null_dout", EINVAL), ("null_dq", EINVAL), ("null_dsinks", EINVAL),
+    ("null_dknorm_w", EINVAL), ("misaligned_dk", EINVAL), ("misaligned_lse", EINVAL),
+    ("fp32", EUNSUPPORTED), ("group_3", EUNSUPPORTED), ("no_workspace", EWORKSPACE),
+    ("fwd_sized_workspace", EWORKSPACE), ("misaligned_workspace", EWORKSPACE),
+])
+def test_bwd_invalid_arguments_rejected(A, case, expected):
+    desc = _bwd_desc(A)
+    kw = {}
+    if case == "null_desc":
+        desc = None
+    elif case == "window_zero":
+        kw["window"] = 0
+    elif case == "use_rope_two":
+        kw["use_rope"] = 2
+    elif case.startswith("null_"):
+        kw[{"null_dknorm_w": "dkw"}.get(case, case[5:])] = 0
+    elif case == "misaligned_dk":
+        kw["dk"] = FAKE + 4
+    elif case == "misaligned_lse":
+        kw["lse"] = FAKE + 2
+    elif case == "fp32":
+        desc = _desc(A, dtype=1, ws_bytes=1 << 30)
+    elif case == "group_3":
+        desc = _desc(A, Hq=12, Hkv=4, ws_bytes=1 << 30)
+    elif case == "no_workspace":
+        desc.workspace = None
+    elif case == "fwd_sized_workspace":
+        desc.workspace_bytes = A.workspace_bytes(desc)
+    elif case == "misaligned_workspace":
+        desc.workspace = 0x10000000 + 64
+    assert _bwd(A, desc, **kw) == expected

@@ -1,0 +1,94 @@
+"""GPU parity of the backward pass (sink_attn_bwd) against the fp64 backward
+oracle on the same bf16 inputs, output gradient and forward results.
+
+Every gradient tensor is compared element by element; the tolerance is
+relative to the tensor's own scale because gradient magnitudes grow with the
+number of (token, head) terms a key collects (see _harness.BWD_REL_MAX)."""
+import numpy as np
+import pytest
+import torch
+
+from _harness import check_bwd_parity, custom_inputs, gpu_backward, require_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 2, 3, 17, 63, 64, 65, 127, 128, 129, 200, 0, 31, 300]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    return require_gpu()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("window,use_rope", [(-1, False), (1, True), (65, False), (100, True),
+                                             (512, True)])
+def test_ragged_documents(window, use_rope):
+    _say(f"case bwd ragged W={window} rope={use_rope}")
+    check_bwd_parity(custom_inputs(RAGGED), window, use_rope, label=f"W={window}")
+
+
+@pytest.mark.parametrize("heads", [(32, 4), (8, 8), (32, 1), (4, 2), (16, 16)])
+def test_group_sizes(heads):
+    _say(f"case bwd heads={heads}")
+    inp = custom_inputs([150, 33, 290], Hq=heads[0], Hkv=heads[1])
+    check_bwd_parity(inp, 100, True, label=f"{heads} W=100")
+    check_bwd_parity(inp, -1, False, label=f"{heads} causal")
+
+
+def test_long_document():
+    _say("case bwd one doc 1500")
+    inp = custom_inputs([1500])
+    check_bwd_parity(inp, -1, False, label="causal 1500")
+    check_bwd_parity(inp, 700, True, label="W=700 1500")
+
+
+def test_sinks():
+    _say("case bwd sinks")
+    inp = custom_inputs([70, 130])
+    g = check_bwd_parity(dict(inp, sinks=torch.full((32,), float("-inf"))), 40, True,
+                         label="sink -inf")
+    assert torch.all(g["dsinks"] == 0)
+    check_bwd_parity(custom_inputs([70, 130], sink_mean=3.0), -1, False, label="sinks N(3,1)")
+
+
+def test_norm_weights_and_scale():
+    _say("case bwd norm weights, softmax scale, eps")
+    inp = custom_inputs([90, 200], seed=3)
+    g = torch.Generator().manual_seed(11)
+    inp = dict(inp, qnorm_w=1 + 0.3 * torch.randn(128, generator=g),
+               knorm_w=1 + 0.3 * torch.randn(128, generator=g))
+    check_bwd_parity(inp, 50, True, label="weights N(1,0.3)")
+    check_bwd_parity(inp, -1, True, label="scale 0.05", softmax_scale=0.05)
+    check_bwd_parity(inp, -1, False, label="eps 1e-2", rms_eps=1e-2)
+
+
+def test_determinism_and_empty_batch():
+    _say("case bwd determinism + T=0")
+    import attention_qk_rmsnorm_amd as A
+    inp = to_device(custom_inputs([333, 1, 900]))
+    a = gpu_backward(inp, 64, True)
+    b = gpu_backward(inp, 64, True)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+    e = to_device(custom_inputs([0]))
+    z = {k: torch.full_like(v, 7.0) for k, v in a.items() if k.startswith("ds") or "norm" in k}
+    dq = torch.empty_like(e["q"])
+    out = torch.empty_like(e["q"])
+    lse = torch.empty((32, 0), dtype=torch.float32, device="cuda:0")
+    grads = dict(z, dq=dq, dk=torch.empty_like(e["k"]), dv=torch.empty_like(e["v"]))
+    A.sink_attn_bwd(e["q"], e["k"], e["v"], e["cu_seqlens"], e["sinks"], e["qnorm_w"],
+                    e["knorm_w"], -1, False, out, lse, out, grads=grads)
+    torch.cuda.synchronize()
+    for key in ("dsinks", "dqnorm_w", "dknorm_w"):
+        assert torch.all(grads[key] == 0), key
+
+
+def test_sliding_layer_scale():
+    # two documents of 2500 and 3500 tokens with the sliding layers' 1024-key
+    # window and RoPE: many key blocks and column tiles per document
+    _say("case bwd T=6000 W=1024 rope")
+    check_bwd_parity(custom_inputs([2500, 3500], seed=5), 1024, True, label="T=6000 W=1024")

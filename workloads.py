@@ -11,7 +11,9 @@ Recipe (the same for every configuration):
     once (round-to-nearest-even) to the storage dtype;
   * Q/K/V ~ N(0, 1); sinks ~ N(sink_mean, 1) fp32; RMSNorm weights
     1 + N(0, 0.02) fp32 with one weight vector of head_dim entries per
-    projection.
+    projection;
+  * for the backward, the output gradient dout ~ N(0, 1) [T, Hq, d] from a
+    second generator seeded with seed + 1, rounded to the storage dtype.
 """
 from __future__ import annotations
 
@@ -103,6 +105,14 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
         "cu_seqlens": torch.from_numpy(cu_seqlens(w.lengths)),
         "sinks": sinks, "qnorm_w": qnorm_w, "knorm_w": knorm_w,
     }
+
+
+def make_grad_output(w: Workload, seed: int = 0) -> torch.Tensor:
+    """dout [T, Hq, d] in w.dtype for the backward of workload ``w``."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed + 1)
+    return torch.randn((w.total_tokens, w.num_q_heads, w.head_dim), generator=gen,
+                       dtype=torch.float32).to(_TORCH_DTYPES[w.dtype])
 
 
 def custom_workload(lengths, num_q_heads=32, num_kv_heads=4, head_dim=128,
