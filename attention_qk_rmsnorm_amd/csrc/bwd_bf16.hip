@@ -57,6 +57,26 @@ constexpr int kKeyTileBytes = 3 * kKT;
 constexpr int kCT = 8192;                  // one 32 x 256 B or 128 x 64 B image
 constexpr int kColTileBytes = 4 * kCT + 4096;
 constexpr int kColLd = 4 * kCT;
+// dK/dV workgroups keep a ring of this many column tiles in LDS; one tile
+// copy is this many global_load_lds instructions per wave
+constexpr int kColBufs = 4;
+constexpr int kColCopyOps = kColTileBytes / (16 * kThreads);
+static_assert(kColCopyOps * 2 < 64, "vmcnt holds 6 bits");
+
+// Workgroup barrier that leaves outstanding global loads (the LDS copies of
+// later tiles) in flight.  The LDS reads of the finished tile have all been
+// consumed by MFMAs before it is reached; lgkmcnt(0) makes that explicit.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_keep_copies() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) (other counters untouched); N < 64
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -114,12 +134,12 @@ __device__ __forceinline__ int first_key(const int32_t* __restrict__ cu, int D, 
 // pair: lane half hf holds the gradient w.r.t. the normalised, rotated vector
 // for channels 32dd + 8rq + 4hf + e at dy[16dd + 4rq + e] (dd, rq, e < 4).
 // xp points at the raw input row (+ 4hf), w at the norm weight; pos is the
-// document position (rope only).  Writes dx to dxp when ok, and dy x r per
-// channel (zero when !ok) to red[channel].
+// document position (rope only).  Writes dx to dxp when ok, and dy x r (zero
+// when !ok) to wsum in dy's order.
 __device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const bf16* __restrict__ xp,
                                               const float* __restrict__ w, bool ok, bool rope,
                                               int pos, const double* s_invf, float eps, int hf,
-                                              bf16* __restrict__ dxp, float* red) {
+                                              bf16* __restrict__ dxp, float (&wsum)[64]) {
   if (rope && ok) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {  // channel 32dd + 8rq + 4hf + e (dd < 2), partner + 64
@@ -160,7 +180,7 @@ __device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const bf16* __res
       for (int e = 0; e < 4; ++e) {
         const float x = (float)xv[e], g = dy[16 * dd + 4 * rq + e];
         o[e] = (bf16)(wv[e] * g * r - x * coef);
-        red[32 * dd + 8 * rq + 4 * hf + e] = g * x * r;
+        wsum[16 * dd + 4 * rq + e] = g * x * r;
       }
       if (ok) *reinterpret_cast<bf16x4*>(dxp + 32 * dd + 8 * rq) = o;
     }
@@ -394,7 +414,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int32_t* __restrict__ cu, const float* __restrict__ knorm_w, int T, int D, int Hkv,
     int log2G, int n_kt, int n_ct, int window, int use_rope, float eps, double theta,
     bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ dwk_part) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * kColTileBytes];
+  // the ring: one array per slot, so that the compiler can tell a copy into
+  // one slot from reads of another (with one array and computed offsets it
+  // waits for every copy in flight before reading)
+  __shared__ __attribute__((aligned(1024))) char ring0[kColTileBytes];
+  __shared__ __attribute__((aligned(1024))) char ring1[kColTileBytes];
+  __shared__ __attribute__((aligned(1024))) char ring2[kColTileBytes];
+  __shared__ __attribute__((aligned(1024))) char ring3[kColTileBytes];
+  static_assert(kColBufs == 4, "one array per ring slot");
+  auto slot = [&](int b) -> char* { return b == 0 ? ring0 : b == 1 ? ring1 : b == 2 ? ring2 : ring3; };
   __shared__ double s_invf[64];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -456,40 +484,60 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   // The walk runs from the last tile down: the key blocks of a causal
   // document all end at the document's last token, so blocks running at the
-  // same time read the same tiles and share them in L2.
-  if (c_lo <= c_hi) copy_lds(ctiles + (size_t)c_hi * kColTileBytes, kColTileBytes, tid, kThreads, lds);
-  for (int c = c_hi; c >= c_lo; --c) {
-    const int b = (c_hi - c) & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    if (c > c_lo)
-      copy_lds(ctiles + (size_t)(c - 1) * kColTileBytes, kColTileBytes, tid, kThreads,
-               lds + (b ^ 1) * kColTileBytes);
+  // same time read the same tiles and share them in L2.  Tiles are copied
+  // kColBufs - 1 ahead into a ring of kColBufs LDS buffers.
+  const int n_tiles = c_hi - c_lo + 1;
+#pragma unroll
+  for (int i = 0; i < kColBufs - 1; ++i)
+    if (i < n_tiles)
+      copy_lds(ctiles + (size_t)(c_hi - i) * kColTileBytes, kColTileBytes, tid, kThreads,
+               slot(i));
+  // One tile; buf is a ring slot fixed at compile time at each call.
+  auto tile = [&](const char* buf, int c) {
     const int ta = c * tpt, tb = ta + tpt - 1;
     // tiles the wave's keys cannot see: skip (wave-uniform)
-    if (ua > T - 1 || tb < ua || ta > ub_last) continue;
+    if (ua > T - 1 || tb < ua || ta > ub_last) return;
     const bool full = ta >= ub && tb <= ua_last;
-    const char* buf = lds + b * kColTileBytes;
     const float* ld = reinterpret_cast<const float*>(buf + kColLd);
+    // Every LDS operand of the tile is read ahead of the MFMA that takes it
+    // (the scheduling barriers keep the compiler from sinking the reads next
+    // to their uses, which would expose the LDS latency once per MFMA).
     // -lse*log2e and -D of the 16 columns this lane's accumulator rows hold
-    f32x16 nl, nd;
+    f32x16 s, dp;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(ld + 8 * a + 4 * hf);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(ld + 32 + 8 * a + 4 * hf);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        nl[4 * a + e] = l4[e];
-        nd[4 * a + e] = d4[e];
+        s[4 * a + e] = l4[e];
+        dp[4 * a + e] = d4[e];
       }
     }
-    // S[col][key] * log2e - lse*log2e, and dP[col][key] - D
-    f32x16 s = nl, dp = nd;
+    bf16x8 aq[8], ado[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      s = mfma32(rd(buf + roff[kk]), kB[kk], s);
-      dp = mfma32(rd(buf + kCT + roff[kk]), vB[kk], dp);
+      aq[kk] = rd(buf + roff[kk]);
+      ado[kk] = rd(buf + kCT + roff[kk]);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // S[col][key] * log2e - lse*log2e, and dP[col][key] - D
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      s = mfma32(aq[kk], kB[kk], s);
+      dp = mfma32(ado[kk], vB[kk], dp);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // operands of the accumulations, read while the scores complete
+    bf16x8 tdo[4][2], tq[4][2];
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        tdo[dd][j] = rd(buf + 3 * kCT + toff[dd][j]);
+        tq[dd][j] = rd(buf + 2 * kCT + toff[dd][j]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
     if (!full) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -513,13 +561,37 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         if (dd == 0) {
-          mfma32_acc_nop(acc_dv[dd], rd(buf + 3 * kCT + toff[dd][j]), pb[j]);
-          mfma32_acc_nop(acc_dk[dd], rd(buf + 2 * kCT + toff[dd][j]), sb[j]);
+          mfma32_acc_nop(acc_dv[dd], tdo[dd][j], pb[j]);
+          mfma32_acc_nop(acc_dk[dd], tq[dd][j], sb[j]);
         } else {
-          mfma32_acc(acc_dv[dd], rd(buf + 3 * kCT + toff[dd][j]), pb[j]);
-          mfma32_acc(acc_dk[dd], rd(buf + 2 * kCT + toff[dd][j]), sb[j]);
+          mfma32_acc(acc_dv[dd], tdo[dd][j], pb[j]);
+          mfma32_acc(acc_dk[dd], tq[dd][j], sb[j]);
         }
       }
+  };
+  for (int i = 0; i < n_tiles;) {
+#pragma unroll
+    for (int b = 0; b < kColBufs; ++b) {  // i % kColBufs == b
+      if (i >= n_tiles) break;
+      const int c = c_hi - i;
+      // this wave's copies of tile i are done once at most the copies of the
+      // tiles after it are outstanding
+      const int ahead = min(n_tiles - 1 - i, kColBufs - 2);
+      if (ahead >= 2)
+        wait_vmcnt<2 * kColCopyOps>();
+      else if (ahead == 1)
+        wait_vmcnt<kColCopyOps>();
+      else
+        wait_vmcnt<0>();
+      // a bare barrier: __syncthreads() would also drain the copies still
+      // in flight for the next tiles
+      barrier_keep_copies();
+      if (i + kColBufs - 1 < n_tiles)
+        copy_lds(ctiles + (size_t)(c - (kColBufs - 1)) * kColTileBytes, kColTileBytes, tid,
+                 kThreads, slot((b + kColBufs - 1) % kColBufs));
+      tile(slot(b), c);
+      ++i;
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
@@ -548,17 +620,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) dy[16 * dd + r] = acc_dk[dd][r] * kLn2;
     const int pos = u_ok && use_rope ? u - cu[doc_of_token(cu, D, u)] : 0;
-    float* red = reinterpret_cast<float*>(lds) + (32 * wave + col) * 129;
+    float wsum[64];
     norm_rope_bwd(dy, k + ((size_t)uc * Hkv + g) * kHeadDim + 4 * hf, knorm_w, u_ok,
                   use_rope != 0, pos, s_invf, eps, hf,
-                  dk + ((size_t)uc * Hkv + g) * kHeadDim + 4 * hf, red);
-  }
-  __syncthreads();
-  if (tid < kHeadDim) {
+                  dk + ((size_t)uc * Hkv + g) * kHeadDim + 4 * hf, wsum);
+    // the weight gradient sums dy x r over the block's keys in a fixed order,
+    // two waves (64 keys) at a time through LDS rows [key][channel]
+    float* red = reinterpret_cast<float*>(ring0);
     float acc = 0.f;
-    const float* red = reinterpret_cast<const float*>(lds);
-    for (int kr = 0; kr < 128; ++kr) acc += red[kr * 129 + tid];
-    dwk_part[(size_t)blockIdx.x * kHeadDim + tid] = acc;
+#pragma unroll
+    for (int round = 0; round < 2; ++round) {
+      if ((wave >> 1) == round) {
+        float* row = red + (32 * (wave & 1) + col) * 129;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) row[32 * (i >> 4) + 8 * ((i >> 2) & 3) + 4 * hf + (i & 3)] = wsum[i];
+      }
+      __syncthreads();
+      if (tid < kHeadDim)
+        for (int kr = 0; kr < 64; ++kr) acc += red[kr * 129 + tid];
+      __syncthreads();
+    }
+    if (tid < kHeadDim) dwk_part[(size_t)blockIdx.x * kHeadDim + tid] = acc;
   }
 }
 
@@ -567,16 +649,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 // ============================================================================
 constexpr int kDqWaves = 8;
 constexpr int kDqThreads = kDqWaves * 64;
+constexpr int kKeyBufs = 3;  // ring of key tiles in LDS
+constexpr int kKeyCopyOps = kKeyTileBytes / (16 * kDqThreads);  // copies per wave per tile
+static_assert(kKeyBufs == 3, "the waits below assume two copies in flight at most");
 
 __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
     const bf16* __restrict__ q, const char* __restrict__ keys, const char* __restrict__ cols,
     const int32_t* __restrict__ cu, const float* __restrict__ qnorm_w, int T, int D, int Hq,
     int Hkv, int G, int log2G, int n_kt, int n_ct, int window, int use_rope, float eps,
     double theta, float scale, bf16* __restrict__ dq, float* __restrict__ dwq_part) {
-  // two key tiles while walking, 256 x 129 floats in the epilogue
-  constexpr int kLdsBytes = 2 * kKeyTileBytes > 32 * kDqWaves * 129 * 4
-                                ? 2 * kKeyTileBytes : 32 * kDqWaves * 129 * 4;
-  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  // the ring of key tiles, one array per slot (see the dK/dV kernel)
+  __shared__ __attribute__((aligned(1024))) char ring0[kKeyTileBytes];
+  __shared__ __attribute__((aligned(1024))) char ring1[kKeyTileBytes];
+  __shared__ __attribute__((aligned(1024))) char ring2[kKeyTileBytes];
+  auto slot = [&](int b) -> char* { return b == 0 ? ring0 : b == 1 ? ring1 : ring2; };
   __shared__ double s_invf[64];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -643,20 +729,18 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
     nd16[r] = nD;
   }
 
-  if (n_tiles > 0)
-    copy_lds(ktiles + (size_t)(kt_lo >> 6) * kKeyTileBytes, kKeyTileBytes, tid, kDqThreads, lds);
-  for (int j = 0; j < n_tiles; ++j) {
-    const int b = j & 1;
-    const int kt = kt_lo + j * kKeyTile;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (j + 1 < n_tiles)
-      copy_lds(ktiles + (size_t)((kt >> 6) + 1) * kKeyTileBytes, kKeyTileBytes, tid,
-               kDqThreads, lds + (b ^ 1) * kKeyTileBytes);
+  // Key tiles are copied kKeyBufs - 1 ahead into a ring of kKeyBufs LDS
+  // slots; the slot of each unrolled step is a compile-time constant (see the
+  // dK/dV kernel).
+#pragma unroll
+  for (int j = 0; j < kKeyBufs - 1; ++j)
+    if (j < n_tiles)
+      copy_lds(ktiles + (size_t)((kt_lo >> 6) + j) * kKeyTileBytes, kKeyTileBytes, tid,
+               kDqThreads, slot(j));
+  auto tile = [&](const char* buf, int kt) {
     // keys of the tile this wave's tokens cannot see: skip (wave-uniform)
-    if (!wave_ok || kt > tb || kt + kKeyTile - 1 < wa_lo) continue;
+    if (!wave_ok || kt > tb || kt + kKeyTile - 1 < wa_lo) return;
     const bool full = kt + kKeyTile - 1 <= ta && kt >= wb_lo;
-    const char* buf = lds + b * kKeyTileBytes;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       // S^T[key][col] * log2e - lse*log2e and dP^T - D for 32 keys
@@ -690,13 +774,29 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
             mfma32_acc(acc[dd], rd(buf + 2 * kKT + dd * 4096 + voff[2 * kh + jj]), sb[jj]);
         }
     }
+  };
+  for (int j = 0; j < n_tiles;) {
+#pragma unroll
+    for (int b = 0; b < kKeyBufs; ++b) {  // j % kKeyBufs == b
+      if (j >= n_tiles) break;
+      if (j + 1 < n_tiles)
+        wait_vmcnt<kKeyCopyOps>();  // only the copy of tile j + 1 may be outstanding
+      else
+        wait_vmcnt<0>();
+      barrier_keep_copies();
+      if (j + kKeyBufs - 1 < n_tiles)
+        copy_lds(ktiles + (size_t)((kt_lo >> 6) + j + kKeyBufs - 1) * kKeyTileBytes,
+                 kKeyTileBytes, tid, kDqThreads, slot((b + kKeyBufs - 1) % kKeyBufs));
+      tile(slot(b), kt_lo + j * kKeyTile);
+      ++j;
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   agpr_fence();
 
-  // ---- epilogue: dq_hat = scale * acc; rotate back; RMSNorm bwd; dy x r per
-  // channel into LDS rows [column][channel], summed over the 256 columns ----
+  // ---- epilogue: dq_hat = scale * acc; rotate back; RMSNorm bwd ------------
+  float part = 0.f;
   {
     float dy[64];
 #pragma unroll
@@ -704,16 +804,25 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) dy[16 * dd + r] = acc[dd][r] * scale;
     const int pos = t_ok && use_rope ? t - cu[doc_of_token(cu, D, t)] : 0;
-    float* red = reinterpret_cast<float*>(lds) + (32 * wave + col) * 129;
+    float wsum[64];
     norm_rope_bwd(dy, q + ((size_t)tcl * Hq + h) * kHeadDim + 4 * hf, qnorm_w, t_ok,
                   use_rope != 0, pos, s_invf, eps, hf,
-                  dq + ((size_t)tcl * Hq + h) * kHeadDim + 4 * hf, red);
-  }
-  __syncthreads();
-  float part = 0.f;
-  if (tid < kHeadDim) {
-    const float* red = reinterpret_cast<const float*>(lds);
-    for (int cr = 0; cr < 32 * kDqWaves; ++cr) part += red[cr * 129 + tid];
+                  dq + ((size_t)tcl * Hq + h) * kHeadDim + 4 * hf, wsum);
+    // the weight gradient sums dy x r over the block's 256 columns in a fixed
+    // order, two waves (64 columns) at a time through LDS rows
+    float* red = reinterpret_cast<float*>(ring0);
+#pragma unroll
+    for (int round = 0; round < kDqWaves / 2; ++round) {
+      if ((wave >> 1) == round) {
+        float* row = red + (32 * (wave & 1) + col) * 129;
+#pragma unroll
+        for (int i = 0; i < 64; ++i) row[32 * (i >> 4) + 8 * ((i >> 2) & 3) + 4 * hf + (i & 3)] = wsum[i];
+      }
+      __syncthreads();
+      if (tid < kHeadDim)
+        for (int cr = 0; cr < 64; ++cr) part += red[cr * 129 + tid];
+      __syncthreads();
+    }
   }
   if (tid < kHeadDim) dwq_part[(size_t)blockIdx.x * kHeadDim + tid] = part;
 }
