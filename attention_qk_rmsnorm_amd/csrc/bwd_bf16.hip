@@ -101,8 +101,12 @@ __device__ __forceinline__ bf16x8 rd(const char* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// chunk swizzle of the 64-byte rows of the column tiles' transposed images
-__device__ __forceinline__ int cswz(int r) { return r & 3; }
+// Chunk swizzle of the 64-byte rows of the column tiles' transposed images.
+// An operand read takes 16 B from each of 32 consecutive rows; in every group
+// of 16 rows, rows r and r + 4 start on the same LDS bank, so the chunk
+// position must differ between them: (r >> 2) & 3 gives the 16 rows 16
+// distinct 4-bank groups.
+__device__ __forceinline__ int cswz(int r) { return (r >> 2) & 3; }
 
 // Copy nbytes (a multiple of 4096) from global to LDS with global_load_lds.
 __device__ __forceinline__ void copy_lds(const char* __restrict__ src, int nbytes, int tid,
@@ -486,24 +490,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // document all end at the document's last token, so blocks running at the
   // same time read the same tiles and share them in L2.  Tiles are copied
   // kColBufs - 1 ahead into a ring of kColBufs LDS buffers.
+  // The walk is software-pipelined by one tile: while the scores of tile i + 1
+  // run on the matrix cores, the vector units turn tile i's scores into P and
+  // dS, two elements per score step; then tile i's dV and dK products follow.
+  // Every LDS operand is read one step ahead of its MFMA, and scheduling
+  // fences keep that order (left alone, the compiler reads each operand just
+  // before its use and waits out the LDS latency at every MFMA).
+  // Tiles are copied three ahead of the one being scored into a ring of four
+  // LDS slots (tile i in slot i % 4).  Past the last tile the copies repeat
+  // tile c_lo into the slot no later step reads, so every step waits for the
+  // same count.  Tiles this wave's keys cannot see are not skipped: the
+  // element mask zeroes them (the waves of a block share every step).
   const int n_tiles = c_hi - c_lo + 1;
-#pragma unroll
-  for (int i = 0; i < kColBufs - 1; ++i)
-    if (i < n_tiles)
-      copy_lds(ctiles + (size_t)(c_hi - i) * kColTileBytes, kColTileBytes, tid, kThreads,
-               slot(i));
-  // One tile; buf is a ring slot fixed at compile time at each call.
-  auto tile = [&](const char* buf, int c) {
-    const int ta = c * tpt, tb = ta + tpt - 1;
-    // tiles the wave's keys cannot see: skip (wave-uniform)
-    if (ua > T - 1 || tb < ua || ta > ub_last) return;
-    const bool full = ta >= ub && tb <= ua_last;
+  auto copy_tile = [&](int i, char* dst) {
+    const int c = i < n_tiles ? c_hi - i : c_lo;
+    copy_lds(ctiles + (size_t)c * kColTileBytes, kColTileBytes, tid, kThreads, dst);
+  };
+  // -lse*log2e and -D of the 16 columns this lane's accumulator rows hold:
+  // the starting values of the score accumulators
+  auto init_scores = [&](const char* buf, f32x16& s, f32x16& dp) {
     const float* ld = reinterpret_cast<const float*>(buf + kColLd);
-    // Every LDS operand of the tile is read ahead of the MFMA that takes it
-    // (the scheduling barriers keep the compiler from sinking the reads next
-    // to their uses, which would expose the LDS latency once per MFMA).
-    // -lse*log2e and -D of the 16 columns this lane's accumulator rows hold
-    f32x16 s, dp;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(ld + 8 * a + 4 * hf);
@@ -514,84 +520,130 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         dp[4 * a + e] = d4[e];
       }
     }
-    bf16x8 aq[8], ado[8];
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      aq[kk] = rd(buf + roff[kk]);
-      ado[kk] = rd(buf + kCT + roff[kk]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // S[col][key] * log2e - lse*log2e, and dP[col][key] - D
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      s = mfma32(aq[kk], kB[kk], s);
-      dp = mfma32(ado[kk], vB[kk], dp);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // operands of the accumulations, read while the scores complete
-    bf16x8 tdo[4][2], tq[4][2];
-#pragma unroll
-    for (int dd = 0; dd < 4; ++dd)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        tdo[dd][j] = rd(buf + 3 * kCT + toff[dd][j]);
-        tq[dd][j] = rd(buf + 2 * kCT + toff[dd][j]);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-    if (!full) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = ta + ((8 * (r >> 2) + 4 * hf + (r & 3)) >> log2G);
-        s[r] += (u_ok && t >= u && t <= u_last) ? 0.f : -INFINITY;
-      }
-    }
-    // P and dS = P (dP - D), packed as B operands (16 columns per step)
-    bf16x8 pb[2], sb[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = __builtin_amdgcn_exp2f(s[8 * j + e]);
-        pb[j][e] = (bf16)p;
-        sb[j][e] = (bf16)(p * dp[8 * j + e]);
-      }
-    // dV^T[ch][key] += dout^T P,  dK^T[ch][key] += q^T dS
-#pragma unroll
-    for (int dd = 0; dd < 4; ++dd)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (dd == 0) {
-          mfma32_acc_nop(acc_dv[dd], tdo[dd][j], pb[j]);
-          mfma32_acc_nop(acc_dk[dd], tq[dd][j], sb[j]);
-        } else {
-          mfma32_acc(acc_dv[dd], tdo[dd][j], pb[j]);
-          mfma32_acc(acc_dk[dd], tq[dd][j], sb[j]);
-        }
-      }
   };
-  for (int i = 0; i < n_tiles;) {
+  // the element mask of tile c when some (column, key) pair is not visible
+  auto mask = [&](int c, f32x16& s) {
+    const int ta = c * tpt, tb = ta + tpt - 1;
+    if (ta >= ub && tb <= ua_last) return;  // all visible (wave-uniform)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = ta + ((8 * (r >> 2) + 4 * hf + (r & 3)) >> log2G);
+      s[r] += (u_ok && t >= u && t <= u_last) ? 0.f : -INFINITY;
+    }
+  };
+  // elements 2m, 2m + 1 of P and dS = P (dP - D), packed as B operands
+  auto grads2 = [&](int m, const f32x16& s, const f32x16& dp, bf16x8 (&pb)[2],
+                    bf16x8 (&sb)[2]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int e = 2 * m + h;
+      const float p = __builtin_amdgcn_exp2f(s[e]);
+      pb[e >> 3][e & 7] = (bf16)p;
+      sb[e >> 3][e & 7] = (bf16)(p * dp[e]);
+    }
+  };
+  // scores of the tile in nbuf (into s_n, dp_n) while P and dS of the
+  // finished scores (s_c, dp_c) are formed; then dV^T += dout^T P and
+  // dK^T += q^T dS for the finished tile in cbuf.  has_next == false: no next
+  // tile (nbuf unused).  Both are compile-time at every call.
+  auto step = [&](bool has_next, const char* nbuf, const char* cbuf, const f32x16& s_c,
+                  const f32x16& dp_c, f32x16& s_n, f32x16& dp_n) {
+    bf16x8 pb[2], sb[2];
+    bf16x8 qa[8], da[8];
+    if (has_next) {
+      init_scores(nbuf, s_n, dp_n);
+      qa[0] = rd(nbuf + roff[0]);
+      da[0] = rd(nbuf + kCT + roff[0]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      if (has_next && kk < 7) {
+        qa[kk + 1] = rd(nbuf + roff[kk + 1]);
+        da[kk + 1] = rd(nbuf + kCT + roff[kk + 1]);
+      }
+      grads2(kk, s_c, dp_c, pb, sb);
+      // pin the two new elements here (otherwise they sink to their use)
+      asm volatile("" : "+v"(pb[kk >> 2]), "+v"(sb[kk >> 2]));
+      __builtin_amdgcn_sched_barrier(0);
+      if (has_next) {
+        s_n = mfma32(qa[kk], kB[kk], s_n);
+        dp_n = mfma32(da[kk], vB[kk], dp_n);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bf16x8 tdo[8], tq[8];  // step m = 2 dd + j
+    tdo[0] = rd(cbuf + 3 * kCT + toff[0][0]);
+    tq[0] = rd(cbuf + 2 * kCT + toff[0][0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int dd = m >> 1, j = m & 1;
+      if (m < 7) {
+        tdo[m + 1] = rd(cbuf + 3 * kCT + toff[(m + 1) >> 1][(m + 1) & 1]);
+        tq[m + 1] = rd(cbuf + 2 * kCT + toff[(m + 1) >> 1][(m + 1) & 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (dd == 0) {
+        mfma32_acc_nop(acc_dv[dd], tdo[m], pb[j]);
+        mfma32_acc_nop(acc_dk[dd], tq[m], sb[j]);
+      } else {
+        mfma32_acc(acc_dv[dd], tdo[m], pb[j]);
+        mfma32_acc(acc_dk[dd], tq[m], sb[j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  f32x16 sx[2], dpx[2];  // scores of the tile being finished / being formed
+#pragma unroll
+  for (int i = 0; i < kColBufs - 1; ++i) copy_tile(i, slot(i));
+  wait_vmcnt<2 * kColCopyOps>();  // tile 0 landed
+  barrier_keep_copies();
+  {
+    bf16x8 qa[8], da[8];
+    init_scores(slot(0), sx[0], dpx[0]);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      qa[kk] = rd(slot(0) + roff[kk]);
+      da[kk] = rd(slot(0) + kCT + roff[kk]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      sx[0] = mfma32(qa[kk], kB[kk], sx[0]);
+      dpx[0] = mfma32(da[kk], vB[kk], dpx[0]);
+    }
+  }
+  // steady state, unrolled by the ring size (slots are compile-time) and by
+  // two for the score registers
+  int i = 0;
+  for (; i + 1 < n_tiles;) {
 #pragma unroll
     for (int b = 0; b < kColBufs; ++b) {  // i % kColBufs == b
-      if (i >= n_tiles) break;
-      const int c = c_hi - i;
-      // this wave's copies of tile i are done once at most the copies of the
-      // tiles after it are outstanding
-      const int ahead = min(n_tiles - 1 - i, kColBufs - 2);
-      if (ahead >= 2)
-        wait_vmcnt<2 * kColCopyOps>();
-      else if (ahead == 1)
-        wait_vmcnt<kColCopyOps>();
-      else
-        wait_vmcnt<0>();
-      // a bare barrier: __syncthreads() would also drain the copies still
-      // in flight for the next tiles
+      if (i + 1 >= n_tiles) break;
+      const int x = b & 1;  // scores of tile i in sx[x]
+      mask(c_hi - i, sx[x]);
+      wait_vmcnt<kColCopyOps>();  // tile i + 1 landed; tile i + 2 may be in flight
       barrier_keep_copies();
-      if (i + kColBufs - 1 < n_tiles)
-        copy_lds(ctiles + (size_t)(c - (kColBufs - 1)) * kColTileBytes, kColTileBytes, tid,
-                 kThreads, slot((b + kColBufs - 1) % kColBufs));
-      tile(slot(b), c);
+      copy_tile(i + kColBufs - 1, slot((b + kColBufs - 1) % kColBufs));
+      step(true, slot((b + 1) % kColBufs), slot(b), sx[x], dpx[x], sx[x ^ 1], dpx[x ^ 1]);
       ++i;
     }
+  }
+  // the last tile (i == n_tiles - 1); its scores sit in sx[i & 1]
+  {
+    f32x16 dummy_s, dummy_dp;
+    const int x = i & 1;
+#define SA_LAST_TILE(B, X)                                    \
+  mask(c_hi - i, sx[X]);                                      \
+  step(false, slot(0), slot(B), sx[X], dpx[X], dummy_s, dummy_dp);
+    switch (i % kColBufs) {
+      case 0: if (x) { SA_LAST_TILE(0, 1) } else { SA_LAST_TILE(0, 0) } break;
+      case 1: if (x) { SA_LAST_TILE(1, 1) } else { SA_LAST_TILE(1, 0) } break;
+      case 2: if (x) { SA_LAST_TILE(2, 1) } else { SA_LAST_TILE(2, 0) } break;
+      default: if (x) { SA_LAST_TILE(3, 1) } else { SA_LAST_TILE(3, 0) } break;
+    }
+#undef SA_LAST_TILE
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
