@@ -109,12 +109,19 @@ __device__ __forceinline__ bf16x8 rd(const char* p) {
 __device__ __forceinline__ int cswz(int r) { return (r >> 2) & 3; }
 
 // Copy nbytes (a multiple of 4096) from global to LDS with global_load_lds.
+// The LDS destination goes through readfirstlane as a plain 32-bit address,
+// so the compiler keeps no alias information for the copy and adds no waits
+// of its own for it: every reader of a copied tile waits with an explicit
+// vmcnt and a barrier (with alias information the compiler, unable to follow
+// the ring across loop iterations, waits for all copies in flight).
 __device__ __forceinline__ void copy_lds(const char* __restrict__ src, int nbytes, int tid,
                                          int nthreads, char* dst) {
+  typedef __attribute__((address_space(3))) char lds_char;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_char*)dst;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int off = 0; off < nbytes; off += 16 * nthreads) {
-    const int w = tid >> 6;
-    __builtin_amdgcn_global_load_lds(src + off + 16 * tid,
-                                     (lds_void*)(dst + off + 1024 * w), 16, 0, 0);
+    const uint32_t a = __builtin_amdgcn_readfirstlane(base + off + 1024 * w);
+    __builtin_amdgcn_global_load_lds(src + off + 16 * tid, (lds_void*)(uintptr_t)a, 16, 0, 0);
   }
 }
 
@@ -548,48 +555,51 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // tile (nbuf unused).  Both are compile-time at every call.
   auto step = [&](bool has_next, const char* nbuf, const char* cbuf, const f32x16& s_c,
                   const f32x16& dp_c, f32x16& s_n, f32x16& dp_n) {
-    bf16x8 pb[2], sb[2];
-    bf16x8 qa[8], da[8];
-    if (has_next) {
-      init_scores(nbuf, s_n, dp_n);
-      qa[0] = rd(nbuf + roff[0]);
-      da[0] = rd(nbuf + kCT + roff[0]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      if (has_next && kk < 7) {
-        qa[kk + 1] = rd(nbuf + roff[kk + 1]);
-        da[kk + 1] = rd(nbuf + kCT + roff[kk + 1]);
-      }
-      grads2(kk, s_c, dp_c, pb, sb);
-      // pin the two new elements here (otherwise they sink to their use)
-      asm volatile("" : "+v"(pb[kk >> 2]), "+v"(sb[kk >> 2]));
-      __builtin_amdgcn_sched_barrier(0);
-      if (has_next) {
-        s_n = mfma32(qa[kk], kB[kk], s_n);
-        dp_n = mfma32(da[kk], vB[kk], dp_n);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    bf16x8 tdo[8], tq[8];  // step m = 2 dd + j
-    tdo[0] = rd(cbuf + 3 * kCT + toff[0][0]);
-    tq[0] = rd(cbuf + 2 * kCT + toff[0][0]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int dd = m >> 1, j = m & 1;
-      if (m < 7) {
-        tdo[m + 1] = rd(cbuf + 3 * kCT + toff[(m + 1) >> 1][(m + 1) & 1]);
-        tq[m + 1] = rd(cbuf + 2 * kCT + toff[(m + 1) >> 1][(m + 1) & 1]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (dd == 0) {
-        mfma32_acc_nop(acc_dv[dd], tdo[m], pb[j]);
-        mfma32_acc_nop(acc_dk[dd], tq[m], sb[j]);
+    // 16 MFMA pairs: k < 8 scores of the next tile (q and dout rows of
+    // nbuf), k >= 8 the products of the finished tile (dout^T and q^T of
+    // cbuf); the operands of pair k are read kReadAhead pairs earlier
+    constexpr int kReadAhead = 3;
+    auto operands = [&](int k, bf16x8& x, bf16x8& y) {
+      if (k < 8) {
+        x = rd(nbuf + roff[k]);
+        y = rd(nbuf + kCT + roff[k]);
       } else {
-        mfma32_acc(acc_dv[dd], tdo[m], pb[j]);
-        mfma32_acc(acc_dk[dd], tq[m], sb[j]);
+        const int m = k - 8;
+        x = rd(cbuf + 3 * kCT + toff[m >> 1][m & 1]);
+        y = rd(cbuf + 2 * kCT + toff[m >> 1][m & 1]);
+      }
+    };
+    bf16x8 pb[2], sb[2];
+    bf16x8 ox[16], oy[16];
+    if (has_next) init_scores(nbuf, s_n, dp_n);
+#pragma unroll
+    for (int k = 0; k < kReadAhead; ++k)
+      if (has_next || k >= 8) operands(k, ox[k], oy[k]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int kn = k + kReadAhead;
+      if (kn < 16 && (has_next || kn >= 8)) operands(kn, ox[kn], oy[kn]);
+      if (k < 8) {
+        grads2(k, s_c, dp_c, pb, sb);
+        // pin the two new elements here (otherwise they sink to their use)
+        asm volatile("" : "+v"(pb[k >> 2]), "+v"(sb[k >> 2]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (k < 8) {
+        if (has_next) {
+          s_n = mfma32(ox[k], kB[k], s_n);
+          dp_n = mfma32(oy[k], vB[k], dp_n);
+        }
+      } else {
+        const int m = k - 8, dd = m >> 1, j = m & 1;
+        if (dd == 0) {
+          mfma32_acc_nop(acc_dv[dd], ox[k], pb[j]);
+          mfma32_acc_nop(acc_dk[dd], oy[k], sb[j]);
+        } else {
+          mfma32_acc(acc_dv[dd], ox[k], pb[j]);
+          mfma32_acc(acc_dk[dd], oy[k], sb[j]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
