@@ -49,19 +49,24 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 // ---- workspace images ------------------------------------------------------
-// key tile (64 keys of one kv head), 48 KiB: k_hat rows | V rows | K^T
-constexpr int kKT = 16384;                 // one 64 x 256 B or 128 x 128 B image
-constexpr int kKeyTileBytes = 3 * kKT;
-// column tile (32 columns of one kv head), 36 KiB: q rows | dout rows | q^T |
-// dout^T | (-lse*log2e)[32], (-D)[32]
-constexpr int kCT = 8192;                  // one 32 x 256 B or 128 x 64 B image
-constexpr int kColTileBytes = 4 * kCT + 4096;
-constexpr int kColLd = 4 * kCT;
+// Row images only: 256-byte rows of 128 bf16 channels, 16-byte chunk c of
+// row r at chunk position c ^ bswz(r).  MFMA operands that run over the rows
+// (the transposed products) come from the same images through the LDS
+// transpose read.
+// key tile (64 keys of one kv head), 32 KiB: k_hat rows | V rows
+constexpr int kKT = 16384;                 // one 64-row image
+constexpr int kKeyTileBytes = 2 * kKT;
+// column tile (32 columns of one kv head), 16.25 KiB: q rows | dout rows |
+// (-lse*log2e)[32], (-D)[32]
+constexpr int kCT = 8192;                  // one 32-row image
+constexpr int kColLd = 2 * kCT;
+constexpr int kColTileBytes = 2 * kCT + 256;
 // dK/dV workgroups keep a ring of this many column tiles in LDS; one tile
-// copy is this many global_load_lds instructions per wave
-constexpr int kColBufs = 4;
-constexpr int kColCopyOps = kColTileBytes / (16 * kThreads);
-static_assert(kColCopyOps * 2 < 64, "vmcnt holds 6 bits");
+// copy is this many global_load_lds instructions per wave (four of the two
+// row images, one of the -lse / -D block)
+constexpr int kColBufs = 8;
+constexpr int kColCopyOps = 2 * kCT / (16 * kThreads) + 1;
+static_assert(kColCopyOps * (kColBufs - 2) < 64, "vmcnt holds 6 bits");
 
 // Workgroup barrier that leaves outstanding global loads (the LDS copies of
 // later tiles) in flight.  The LDS reads of the finished tile have all been
@@ -101,12 +106,42 @@ __device__ __forceinline__ bf16x8 rd(const char* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// Chunk swizzle of the 64-byte rows of the column tiles' transposed images.
-// An operand read takes 16 B from each of 32 consecutive rows; in every group
-// of 16 rows, rows r and r + 4 start on the same LDS bank, so the chunk
-// position must differ between them: (r >> 2) & 3 gives the 16 rows 16
-// distinct 4-bank groups.
-__device__ __forceinline__ int cswz(int r) { return (r >> 2) & 3; }
+// Chunk swizzle of the backward's row images.  Rows are 256 B, so every row
+// starts on LDS bank 0 and only the chunk position decides the banks.  The
+// MFMA operand read takes one chunk from each of 16 aligned rows: bswz is a
+// permutation of 0..15 over them.  The transpose read takes 4 consecutive
+// chunks from each of 4 aligned rows: bits 2-3 of bswz differ across those
+// rows.  Both reads are therefore free of bank conflicts.
+__device__ __forceinline__ int bswz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// LDS transpose read (ds_read_b64_tr_b16): in every group of 16 lanes, lane
+// 4a + b receives, as its elements 0..3, element b of the 8 bytes read by
+// lanes a, a + 4, a + 8 and a + 12 of the group.  Two such reads make one
+// MFMA operand of 8 bf16.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+__device__ __forceinline__ bf16x8 rd_tr(const char* p0, const char* p1) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_char*)p0);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_char*)p1);
+  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Per-lane offsets of the transpose reads for an A operand A[m][k] with
+// m = 32 dd + (lane % 32) a channel and k running over 16 rows 16 j .. of a
+// row image, in the order the accumulator layout hands out its rows: slot
+// 4h + e of lane half hf is row 16 j + 8 h + 4 hf + e.  Reading lane l (in
+// its 16-lane group: e = (l % 16) / 4, a = l % 4, G = (l / 16) % 2) fetches
+// row 16 j + 8 h + 4 hf + e, channels 32 dd + 16 G + 4a .. + 3, i.e. 8 bytes
+// of chunk 4 dd + 2 G + a / 2.  The offset is 4096 j + tr_off(dd, h).
+__device__ __forceinline__ int tr_off(int lane, int dd, int h) {
+  const int hf = lane >> 5, e = (lane >> 2) & 3, a = lane & 3, G = (lane >> 4) & 1;
+  const int r = 8 * h + 4 * hf + e;  // row within the 16-row step (bswz only sees bits 0-3)
+  const int c = 4 * dd + 2 * G + (a >> 1);
+  return r * 256 + ((c ^ bswz(r)) << 4) + 8 * (a & 1);
+}
 
 // Copy nbytes (a multiple of 4096) from global to LDS with global_load_lds.
 // The LDS destination goes through readfirstlane as a plain 32-bit address,
@@ -123,6 +158,18 @@ __device__ __forceinline__ void copy_lds(const char* __restrict__ src, int nbyte
     const uint32_t a = __builtin_amdgcn_readfirstlane(base + off + 1024 * w);
     __builtin_amdgcn_global_load_lds(src + off + 16 * tid, (lds_void*)(uintptr_t)a, 16, 0, 0);
   }
+}
+
+// Copy one column tile: the two row images with every lane, then the 256-byte
+// -lse / -D block with lanes 0-3 of every wave (64 bytes per wave).
+__device__ __forceinline__ void copy_col_tile(const char* __restrict__ src, int tid, char* dst) {
+  copy_lds(src, 2 * kCT, tid, kThreads, dst);
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_char*)dst;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t a = __builtin_amdgcn_readfirstlane(base + kColLd + 64 * w);
+  if ((tid & 63) < 4)
+    __builtin_amdgcn_global_load_lds(src + kColLd + 64 * w + 16 * (tid & 63),
+                                     (lds_void*)(uintptr_t)a, 16, 0, 0);
 }
 
 // Latest token that key u is visible to: min(document end, u + W) - 1.
@@ -205,14 +252,13 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
     const float* __restrict__ knorm_w, int T, int D, int Hkv, int n_kt, float eps,
     double theta, int use_rope, char* __restrict__ keys) {
   __shared__ double s_invf[64];
-  __shared__ __attribute__((aligned(16))) bf16 s_k[kKeyTile][kHeadDim + 8];
   const int tid = threadIdx.x;
   const int tile = blockIdx.x / Hkv, g = blockIdx.x - tile * Hkv;
   const int t0 = tile * kKeyTile;
   char* img = keys + ((size_t)g * n_kt + tile) * kKeyTileBytes;
   if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
   __syncthreads();
-  // V rows straight into the V image (row r chunk c at c ^ kswz(r))
+  // V rows straight into the V image
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int idx = tid + kThreads * i;
@@ -220,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
     const int t = t0 + r;
     uint4 val = make_uint4(0, 0, 0, 0);
     if (t < T) val = *reinterpret_cast<const uint4*>(v + ((size_t)t * Hkv + g) * kHeadDim + 8 * c);
-    *reinterpret_cast<uint4*>(img + kKT + r * 256 + 16 * (c ^ kswz(r))) = val;
+    *reinterpret_cast<uint4*>(img + kKT + r * 256 + 16 * (c ^ bswz(r))) = val;
   }
   // K rows: RMSNorm (+RoPE), 8 lanes per token (channels 8c.. and 64+8c..)
 #pragma unroll
@@ -271,23 +317,8 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
       lo[e] = (bf16)x[e];
       hi[e] = (bf16)x[8 + e];
     }
-    *reinterpret_cast<bf16x8*>(img + r * 256 + 16 * (c ^ kswz(r))) = lo;
-    *reinterpret_cast<bf16x8*>(img + r * 256 + 16 * ((c + 8) ^ kswz(r))) = hi;
-    *reinterpret_cast<bf16x8*>(&s_k[r][8 * c]) = lo;
-    *reinterpret_cast<bf16x8*>(&s_k[r][64 + 8 * c]) = hi;
-  }
-  __syncthreads();
-  // K^T: 128 channel rows x 64 keys, keys in the group order of the header,
-  // chunk tc of row d at position tc ^ vswz(d) (the forward's V^T format)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int pidx = tid + kThreads * i;
-    const int tc = pidx & 7, d = pidx >> 3;
-    const int kbase16 = 16 * (tc >> 1) + 4 * (tc & 1);
-    bf16x8 col;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) col[e] = s_k[kbase16 + 8 * (e >> 2) + (e & 3)][d];
-    *reinterpret_cast<bf16x8*>(img + 2 * kKT + d * 128 + 16 * (tc ^ vswz(d))) = col;
+    *reinterpret_cast<bf16x8*>(img + r * 256 + 16 * (c ^ bswz(r))) = lo;
+    *reinterpret_cast<bf16x8*>(img + r * 256 + 16 * ((c + 8) ^ bswz(r))) = hi;
   }
 }
 
@@ -301,8 +332,6 @@ __global__ __launch_bounds__(kThreads) void bwd_cols_kernel(
     int Hkv, int G, int log2G, int n_ct, float eps, double theta, int use_rope, float c_log2,
     char* __restrict__ cols, float* __restrict__ dsink_part) {
   __shared__ double s_invf[64];
-  __shared__ __attribute__((aligned(16))) bf16 s_q[32][kHeadDim + 8];
-  __shared__ __attribute__((aligned(16))) bf16 s_do[32][kHeadDim + 8];
   __shared__ float s_sink[32];
   const int tid = threadIdx.x;
   const int ct = blockIdx.x / Hkv, g = blockIdx.x - ct * Hkv;
@@ -375,15 +404,11 @@ __global__ __launch_bounds__(kThreads) void bwd_cols_kernel(
     dl[e] = (bf16)y[e];
     dh[e] = (bf16)y[8 + e];
   }
-  // row images (row col, chunk c at c ^ kswz(col))
-  *reinterpret_cast<bf16x8*>(img + col * 256 + 16 * (c ^ kswz(col))) = ql;
-  *reinterpret_cast<bf16x8*>(img + col * 256 + 16 * ((c + 8) ^ kswz(col))) = qh;
-  *reinterpret_cast<bf16x8*>(img + kCT + col * 256 + 16 * (c ^ kswz(col))) = dl;
-  *reinterpret_cast<bf16x8*>(img + kCT + col * 256 + 16 * ((c + 8) ^ kswz(col))) = dh;
-  *reinterpret_cast<bf16x8*>(&s_q[col][8 * c]) = ql;
-  *reinterpret_cast<bf16x8*>(&s_q[col][64 + 8 * c]) = qh;
-  *reinterpret_cast<bf16x8*>(&s_do[col][8 * c]) = dl;
-  *reinterpret_cast<bf16x8*>(&s_do[col][64 + 8 * c]) = dh;
+  // row images
+  *reinterpret_cast<bf16x8*>(img + col * 256 + 16 * (c ^ bswz(col))) = ql;
+  *reinterpret_cast<bf16x8*>(img + col * 256 + 16 * ((c + 8) ^ bswz(col))) = qh;
+  *reinterpret_cast<bf16x8*>(img + kCT + col * 256 + 16 * (c ^ bswz(col))) = dl;
+  *reinterpret_cast<bf16x8*>(img + kCT + col * 256 + 16 * ((c + 8) ^ bswz(col))) = dh;
   // per column: -lse*log2e, -D, and the sink's share -p_sink * D
   if (c == 0) {
     float* ld = reinterpret_cast<float*>(img + kColLd);
@@ -393,22 +418,6 @@ __global__ __launch_bounds__(kThreads) void bwd_cols_kernel(
     s_sink[col] = ok ? -__expf(sinks[h] - l) * dot : 0.f;
   }
   __syncthreads();
-  // transposed images: 128 channel rows x 32 columns (64 B), column groups in
-  // the header's order, chunk cc of row d at cc ^ cswz(d)
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int pidx = tid + kThreads * i;
-    const int cc = pidx & 3, d = pidx >> 2;
-    const int base = 16 * (cc >> 1) + 4 * (cc & 1);
-    bf16x8 a, b;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      a[e] = s_q[base + 8 * (e >> 2) + (e & 3)][d];
-      b[e] = s_do[base + 8 * (e >> 2) + (e & 3)][d];
-    }
-    *reinterpret_cast<bf16x8*>(img + 2 * kCT + d * 64 + 16 * (cc ^ cswz(d))) = a;
-    *reinterpret_cast<bf16x8*>(img + 3 * kCT + d * 64 + 16 * (cc ^ cswz(d))) = b;
-  }
   // dsink share of this tile per head of the group (tokens in order)
   if (tid < G) {
     float acc = 0.f;
@@ -428,12 +437,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // the ring: one array per slot, so that the compiler can tell a copy into
   // one slot from reads of another (with one array and computed offsets it
   // waits for every copy in flight before reading)
-  __shared__ __attribute__((aligned(1024))) char ring0[kColTileBytes];
-  __shared__ __attribute__((aligned(1024))) char ring1[kColTileBytes];
-  __shared__ __attribute__((aligned(1024))) char ring2[kColTileBytes];
-  __shared__ __attribute__((aligned(1024))) char ring3[kColTileBytes];
-  static_assert(kColBufs == 4, "one array per ring slot");
-  auto slot = [&](int b) -> char* { return b == 0 ? ring0 : b == 1 ? ring1 : b == 2 ? ring2 : ring3; };
+  __shared__ __attribute__((aligned(256))) char ring0[kColTileBytes];
+  __shared__ __attribute__((aligned(256))) char ring1[kColTileBytes];
+  __shared__ __attribute__((aligned(256))) char ring2[kColTileBytes];
+  __shared__ __attribute__((aligned(256))) char ring3[kColTileBytes];
+  __shared__ __attribute__((aligned(256))) char ring4[kColTileBytes];
+  __shared__ __attribute__((aligned(256))) char ring5[kColTileBytes];
+  __shared__ __attribute__((aligned(256))) char ring6[kColTileBytes];
+  __shared__ __attribute__((aligned(256))) char ring7[kColTileBytes];
+  static_assert(kColBufs == 8, "one array per ring slot");
+  auto slot = [&](int b) -> char* {
+    switch (b) {
+      case 0: return ring0;
+      case 1: return ring1;
+      case 2: return ring2;
+      case 3: return ring3;
+      case 4: return ring4;
+      case 5: return ring5;
+      case 6: return ring6;
+      default: return ring7;
+    }
+  };
   __shared__ double s_invf[64];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -450,7 +474,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const int ua = kb0 + 32 * wave, ub = min(ua + 31, T - 1);
   const int u_last = u_ok ? last_viewer(cu, D, u, window) : -1;  // visible tokens [u, u_last]
   const int ua_last = ua < T ? last_viewer(cu, D, ua, window) : -1;
-  const int ub_last = ua < T ? last_viewer(cu, D, ub, window) : -1;
   // the block's column tiles: tokens [kb0, last viewer of its last key]
   const int kmax = min(kb0 + 127, T - 1);
   const int t_hi = kb0 < T ? last_viewer(cu, D, kmax, window) : -1;
@@ -464,10 +487,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const int r = uc & 63;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const int pos = ((2 * kk + hf) ^ kswz(r)) << 4;
+      const int pos = ((2 * kk + hf) ^ bswz(r)) << 4;
       kB[kk] = rd(kimg + r * 256 + pos);
       vB[kk] = rd(kimg + kKT + r * 256 + pos);
     }
+    // land them before the tile copies start (a later wait would drain those)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) asm volatile("" ::"v"(kB[kk]), "v"(vB[kk]));
   }
   f32x16 acc_dv[4], acc_dk[4];
   {
@@ -480,18 +506,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       zero_acc(acc_dk[dd], zero);
     }
   }
-  // LDS read offsets: row images (rows = columns) and transposed images
-  // (rows = channels 32dd + col)
+  // LDS read offsets: operand reads of the row images (row = column) and
+  // transpose reads (k over the columns, m over channels)
   int roff[8], toff[4][2];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) roff[kk] = col * 256 + (((2 * kk + hf) ^ kswz(col)) << 4);
+  for (int kk = 0; kk < 8; ++kk) roff[kk] = col * 256 + (((2 * kk + hf) ^ bswz(col)) << 4);
 #pragma unroll
   for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int d = 32 * dd + col;
-      toff[dd][j] = d * 64 + (((2 * j + hf) ^ cswz(d)) << 4);
-    }
+    for (int h = 0; h < 2; ++h) toff[dd][h] = tr_off(lane, dd, h);
 
   // The walk runs from the last tile down: the key blocks of a causal
   // document all end at the document's last token, so blocks running at the
@@ -503,15 +526,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // Every LDS operand is read one step ahead of its MFMA, and scheduling
   // fences keep that order (left alone, the compiler reads each operand just
   // before its use and waits out the LDS latency at every MFMA).
-  // Tiles are copied three ahead of the one being scored into a ring of four
-  // LDS slots (tile i in slot i % 4).  Past the last tile the copies repeat
-  // tile c_lo into the slot no later step reads, so every step waits for the
-  // same count.  Tiles this wave's keys cannot see are not skipped: the
+  // Tiles are copied kColBufs - 2 ahead of the one being scored into a ring
+  // of kColBufs LDS slots (tile i in slot i % kColBufs).  Past the last tile
+  // the copies repeat tile c_lo into slots no later step reads, so every step
+  // waits for the same count.  Tiles this wave's keys cannot see are not skipped: the
   // element mask zeroes them (the waves of a block share every step).
   const int n_tiles = c_hi - c_lo + 1;
   auto copy_tile = [&](int i, char* dst) {
     const int c = i < n_tiles ? c_hi - i : c_lo;
-    copy_lds(ctiles + (size_t)c * kColTileBytes, kColTileBytes, tid, kThreads, dst);
+    copy_col_tile(ctiles + (size_t)c * kColTileBytes, tid, dst);
   };
   // -lse*log2e and -D of the 16 columns this lane's accumulator rows hold:
   // the starting values of the score accumulators
@@ -564,9 +587,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
         x = rd(nbuf + roff[k]);
         y = rd(nbuf + kCT + roff[k]);
       } else {
-        const int m = k - 8;
-        x = rd(cbuf + 3 * kCT + toff[m >> 1][m & 1]);
-        y = rd(cbuf + 2 * kCT + toff[m >> 1][m & 1]);
+        // step m = 2 dd + j: dout^T and q^T for channels 32 dd.., columns 16 j..
+        const int m = k - 8, dd = m >> 1, j = m & 1;
+        x = rd_tr(cbuf + kCT + 4096 * j + toff[dd][0], cbuf + kCT + 4096 * j + toff[dd][1]);
+        y = rd_tr(cbuf + 4096 * j + toff[dd][0], cbuf + 4096 * j + toff[dd][1]);
       }
     };
     bf16x8 pb[2], sb[2];
@@ -608,7 +632,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   f32x16 sx[2], dpx[2];  // scores of the tile being finished / being formed
 #pragma unroll
   for (int i = 0; i < kColBufs - 1; ++i) copy_tile(i, slot(i));
-  wait_vmcnt<2 * kColCopyOps>();  // tile 0 landed
+  wait_vmcnt<(kColBufs - 2) * kColCopyOps>();  // tile 0 landed
   barrier_keep_copies();
   {
     bf16x8 qa[8], da[8];
@@ -633,7 +657,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       if (i + 1 >= n_tiles) break;
       const int x = b & 1;  // scores of tile i in sx[x]
       mask(c_hi - i, sx[x]);
-      wait_vmcnt<kColCopyOps>();  // tile i + 1 landed; tile i + 2 may be in flight
+      // tile i + 1 landed; tiles i + 2 .. i + kColBufs - 2 may be in flight
+      wait_vmcnt<(kColBufs - 3) * kColCopyOps>();
       barrier_keep_copies();
       copy_tile(i + kColBufs - 1, slot((b + kColBufs - 1) % kColBufs));
       step(true, slot((b + 1) % kColBufs), slot(b), sx[x], dpx[x], sx[x ^ 1], dpx[x ^ 1]);
@@ -643,15 +668,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // the last tile (i == n_tiles - 1); its scores sit in sx[i & 1]
   {
     f32x16 dummy_s, dummy_dp;
-    const int x = i & 1;
+    // Each case may leave the accumulators in other registers than the next
+    // one, and the compiler then copies them where the cases join.  It cannot
+    // see that the inline-asm MFMAs wrote them, so the fence provides the wait
+    // states an AGPR read needs after an MFMA write.
 #define SA_LAST_TILE(B, X)                                    \
   mask(c_hi - i, sx[X]);                                      \
-  step(false, slot(0), slot(B), sx[X], dpx[X], dummy_s, dummy_dp);
-    switch (i % kColBufs) {
-      case 0: if (x) { SA_LAST_TILE(0, 1) } else { SA_LAST_TILE(0, 0) } break;
-      case 1: if (x) { SA_LAST_TILE(1, 1) } else { SA_LAST_TILE(1, 0) } break;
-      case 2: if (x) { SA_LAST_TILE(2, 1) } else { SA_LAST_TILE(2, 0) } break;
-      default: if (x) { SA_LAST_TILE(3, 1) } else { SA_LAST_TILE(3, 0) } break;
+  step(false, slot(0), slot(B), sx[X], dpx[X], dummy_s, dummy_dp); \
+  agpr_fence();
+    switch (i % kColBufs) {  // the parity of the slot is the parity of i
+      case 0: SA_LAST_TILE(0, 0) break;
+      case 1: SA_LAST_TILE(1, 1) break;
+      case 2: SA_LAST_TILE(2, 0) break;
+      case 3: SA_LAST_TILE(3, 1) break;
+      case 4: SA_LAST_TILE(4, 0) break;
+      case 5: SA_LAST_TILE(5, 1) break;
+      case 6: SA_LAST_TILE(6, 0) break;
+      default: SA_LAST_TILE(7, 1) break;
     }
 #undef SA_LAST_TILE
   }
@@ -687,19 +720,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
                   use_rope != 0, pos, s_invf, eps, hf,
                   dk + ((size_t)uc * Hkv + g) * kHeadDim + 4 * hf, wsum);
     // the weight gradient sums dy x r over the block's keys in a fixed order,
-    // two waves (64 keys) at a time through LDS rows [key][channel]
+    // one wave (32 keys) at a time through LDS rows [key][channel]
+    static_assert(32 * 129 * 4 <= kColTileBytes, "one wave's rows fit a ring slot");
     float* red = reinterpret_cast<float*>(ring0);
     float acc = 0.f;
 #pragma unroll
-    for (int round = 0; round < 2; ++round) {
-      if ((wave >> 1) == round) {
-        float* row = red + (32 * (wave & 1) + col) * 129;
+    for (int round = 0; round < 4; ++round) {
+      if (wave == round) {
+        float* row = red + col * 129;
 #pragma unroll
         for (int i = 0; i < 64; ++i) row[32 * (i >> 4) + 8 * ((i >> 2) & 3) + 4 * hf + (i & 3)] = wsum[i];
       }
       __syncthreads();
       if (tid < kHeadDim)
-        for (int kr = 0; kr < 64; ++kr) acc += red[kr * 129 + tid];
+        for (int kr = 0; kr < 32; ++kr) acc += red[kr * 129 + tid];
       __syncthreads();
     }
     if (tid < kHeadDim) dwk_part[(size_t)blockIdx.x * kHeadDim + tid] = acc;
@@ -711,9 +745,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 // ============================================================================
 constexpr int kDqWaves = 8;
 constexpr int kDqThreads = kDqWaves * 64;
-constexpr int kKeyBufs = 3;  // ring of key tiles in LDS
+constexpr int kKeyBufs = 4;  // ring of key tiles in LDS
 constexpr int kKeyCopyOps = kKeyTileBytes / (16 * kDqThreads);  // copies per wave per tile
-static_assert(kKeyBufs == 3, "the waits below assume two copies in flight at most");
+static_assert(kKeyCopyOps * (kKeyBufs - 2) < 64, "vmcnt holds 6 bits");
 
 __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
     const bf16* __restrict__ q, const char* __restrict__ keys, const char* __restrict__ cols,
@@ -724,7 +758,11 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) char ring0[kKeyTileBytes];
   __shared__ __attribute__((aligned(1024))) char ring1[kKeyTileBytes];
   __shared__ __attribute__((aligned(1024))) char ring2[kKeyTileBytes];
-  auto slot = [&](int b) -> char* { return b == 0 ? ring0 : b == 1 ? ring1 : ring2; };
+  __shared__ __attribute__((aligned(1024))) char ring3[kKeyTileBytes];
+  static_assert(kKeyBufs == 4, "one array per ring slot");
+  auto slot = [&](int b) -> char* {
+    return b == 0 ? ring0 : b == 1 ? ring1 : b == 2 ? ring2 : ring3;
+  };
   __shared__ double s_invf[64];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -762,7 +800,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
     const char* cimg = cols + ((size_t)g * n_ct + ctc) * kColTileBytes;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const int off = col * 256 + (((2 * kk + hf) ^ kswz(col)) << 4);
+      const int off = col * 256 + (((2 * kk + hf) ^ bswz(col)) << 4);
       qB[kk] = rd(cimg + off);
       dB[kk] = rd(cimg + kCT + off);
     }
@@ -770,6 +808,10 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
       nlse = reinterpret_cast<const float*>(cimg + kColLd)[col];
       nD = reinterpret_cast<const float*>(cimg + kColLd)[32 + col];
     }
+    // land them before the tile copies start (a later wait would drain those)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) asm volatile("" ::"v"(qB[kk]), "v"(dB[kk]));
+    asm volatile("" ::"v"(nlse), "v"(nD));
   }
   f32x16 acc[4];
   {
@@ -779,11 +821,15 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
 #pragma unroll
     for (int dd = 0; dd < 4; ++dd) zero_acc(acc[dd], zero);
   }
-  int koff[8], voff[4];
+  // operand reads of the key images (row = key) and transpose reads of k_hat
+  // (k over the keys, m over channels)
+  int koff[8], toff[4][2];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) koff[kk] = col * 256 + (((2 * kk + hf) ^ kswz(col)) << 4);
+  for (int kk = 0; kk < 8; ++kk) koff[kk] = col * 256 + (((2 * kk + hf) ^ bswz(col)) << 4);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) voff[j] = col * 128 + (((2 * j + hf) ^ vswz(col)) << 4);
+  for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) toff[dd][h] = tr_off(lane, dd, h);
   f32x16 nl16, nd16;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -793,12 +839,14 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
 
   // Key tiles are copied kKeyBufs - 1 ahead into a ring of kKeyBufs LDS
   // slots; the slot of each unrolled step is a compile-time constant (see the
-  // dK/dV kernel).
+  // dK/dV kernel).  Past the last tile the copies repeat the first tile into
+  // slots no later step reads, so every step waits for the same count.
+  auto copy_tile = [&](int j, char* dst) {
+    const int t_idx = (kt_lo >> 6) + (j < n_tiles ? j : 0);
+    copy_lds(ktiles + (size_t)t_idx * kKeyTileBytes, kKeyTileBytes, tid, kDqThreads, dst);
+  };
 #pragma unroll
-  for (int j = 0; j < kKeyBufs - 1; ++j)
-    if (j < n_tiles)
-      copy_lds(ktiles + (size_t)((kt_lo >> 6) + j) * kKeyTileBytes, kKeyTileBytes, tid,
-               kDqThreads, slot(j));
+  for (int j = 0; j < kKeyBufs - 1; ++j) copy_tile(j, slot(j));
   auto tile = [&](const char* buf, int kt) {
     // keys of the tile this wave's tokens cannot see: skip (wave-uniform)
     if (!wave_ok || kt > tb || kt + kKeyTile - 1 < wa_lo) return;
@@ -830,10 +878,13 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
       for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
+          // K^T for channels 32 dd.., keys 32 kh + 16 jj..
+          const char* kt_rows = buf + 4096 * (2 * kh + jj);
+          const bf16x8 a = rd_tr(kt_rows + toff[dd][0], kt_rows + toff[dd][1]);
           if (dd == 0)
-            mfma32_acc_nop(acc[dd], rd(buf + 2 * kKT + dd * 4096 + voff[2 * kh + jj]), sb[jj]);
+            mfma32_acc_nop(acc[dd], a, sb[jj]);
           else
-            mfma32_acc(acc[dd], rd(buf + 2 * kKT + dd * 4096 + voff[2 * kh + jj]), sb[jj]);
+            mfma32_acc(acc[dd], a, sb[jj]);
         }
     }
   };
@@ -841,14 +892,10 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
 #pragma unroll
     for (int b = 0; b < kKeyBufs; ++b) {  // j % kKeyBufs == b
       if (j >= n_tiles) break;
-      if (j + 1 < n_tiles)
-        wait_vmcnt<kKeyCopyOps>();  // only the copy of tile j + 1 may be outstanding
-      else
-        wait_vmcnt<0>();
+      // tile j landed; tiles j + 1 .. j + kKeyBufs - 2 may be in flight
+      wait_vmcnt<(kKeyBufs - 2) * kKeyCopyOps>();
       barrier_keep_copies();
-      if (j + kKeyBufs - 1 < n_tiles)
-        copy_lds(ktiles + (size_t)((kt_lo >> 6) + j + kKeyBufs - 1) * kKeyTileBytes,
-                 kKeyTileBytes, tid, kDqThreads, slot((b + kKeyBufs - 1) % kKeyBufs));
+      copy_tile(j + kKeyBufs - 1, slot((b + kKeyBufs - 1) % kKeyBufs));
       tile(slot(b), kt_lo + j * kKeyTile);
       ++j;
     }
@@ -871,18 +918,19 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
                   use_rope != 0, pos, s_invf, eps, hf,
                   dq + ((size_t)tcl * Hq + h) * kHeadDim + 4 * hf, wsum);
     // the weight gradient sums dy x r over the block's 256 columns in a fixed
-    // order, two waves (64 columns) at a time through LDS rows
+    // order, one wave (32 columns) at a time through LDS rows
+    static_assert(32 * 129 * 4 <= kKeyTileBytes, "one wave's rows fit a ring slot");
     float* red = reinterpret_cast<float*>(ring0);
 #pragma unroll
-    for (int round = 0; round < kDqWaves / 2; ++round) {
-      if ((wave >> 1) == round) {
-        float* row = red + (32 * (wave & 1) + col) * 129;
+    for (int round = 0; round < kDqWaves; ++round) {
+      if (wave == round) {
+        float* row = red + col * 129;
 #pragma unroll
         for (int i = 0; i < 64; ++i) row[32 * (i >> 4) + 8 * ((i >> 2) & 3) + 4 * hf + (i & 3)] = wsum[i];
       }
       __syncthreads();
       if (tid < kHeadDim)
-        for (int cr = 0; cr < 64; ++cr) part += red[cr * 129 + tid];
+        for (int cr = 0; cr < 32; ++cr) part += red[cr * 129 + tid];
       __syncthreads();
     }
   }

@@ -13,7 +13,13 @@ correctness rest on, checked on the CPU from hipcc's assembly output:
   whole key loop (no accvgpr copies there), waits for tile copies only at the
   per-tile barrier, and every MFMA it issues from inline asm has the two wait
   states an MFMA needs after VALU code wrote one of its A/B operands (the
-  compiler does not insert them for inline asm).
+  compiler does not insert them for inline asm);
+* the same two wait states in the backward kernels, and in every bf16 kernel
+  no instruction other than a chained MFMA reads an AGPR within 18 wait
+  states of an MFMA writing it (the compiler cannot see that inline-asm MFMAs
+  wrote the accumulators it copies; a missed case returned stale values for
+  the last accumulator rows of the dK/dV tail);
+* the backward's tile loops wait for copies only right before their barrier.
 """
 import os
 import re
@@ -147,8 +153,9 @@ def _regs(tok):
     return {(m.group(1), int(m.group(2)))} if m else set()
 
 
-def test_inline_asm_mfma_wait_states(asm):
-    text = asm["attn_bf16_wide.hip"]
+@pytest.mark.parametrize("source, minimum", [("attn_bf16_wide.hip", 100), ("bwd_bf16.hip", 40)])
+def test_inline_asm_mfma_wait_states(asm, source, minimum):
+    text = asm[source]
     lines = [l.strip() for l in text.splitlines()]
     inasm, checked, bad = False, 0, []
     for i, l in enumerate(lines):
@@ -174,5 +181,69 @@ def test_inline_asm_mfma_wait_states(asm):
                     if _regs(p.split(None, 1)[1].split(",")[0].strip()) & srcs:
                         bad.append((p, l))
                 slots += 1
-    assert checked >= 100
+    assert checked >= minimum
     assert not bad, bad[:3]
+
+
+def _agpr_read_hazards(body):
+    """(mfma, reader, wait states) where a non-MFMA instruction reads an AGPR
+    that an MFMA wrote fewer than 18 wait states earlier (an MFMA issue is
+    counted as 8 states, its pass count at most; labels end the search)."""
+    lines = [l.split(";")[0].strip() for l in body.splitlines()]
+    lines = [l for l in lines if l and not (l.startswith(".") and not l.endswith(":"))]
+    found = []
+    for i, l in enumerate(lines):
+        if l.endswith(":") or l.startswith("v_mfma") or not l.startswith("v_") or " " not in l:
+            continue
+        srcs = set()
+        for tok in l.split(None, 1)[1].split(",")[1:]:
+            srcs |= {r for r in _regs(tok.strip()) if r[0] == "a"}
+        if not srcs:
+            continue
+        gap = 0
+        for p in reversed(lines[max(0, i - 40):i]):
+            if p.endswith(":"):
+                break
+            if p.startswith("v_mfma"):
+                if _regs(p.split(None, 1)[1].split(",")[0].strip()) & srcs and gap < 18:
+                    found.append((p, l, gap))
+                gap += 8
+            elif p.startswith("s_nop"):
+                gap += int(p.split()[1]) + 1
+            else:
+                gap += 1
+    return found
+
+
+def test_agpr_reads_wait_for_mfma_results(asm):
+    for source in ("attn_bf16.hip", "attn_bf16_wide.hip", "bwd_bf16.hip"):
+        for kname, body in _kernels(asm[source]):
+            hz = _agpr_read_hazards(body)
+            assert not hz, (kname[:60], hz[:3])
+
+
+def test_backward_loops_wait_for_copies_only_at_barriers(asm):
+    # after every group of tile copies, up to the next barrier in the code,
+    # a vmcnt wait may only stand right before that barrier (the ring's own
+    # wait): a wait between the copies and the step's LDS reads would drain
+    # the copies just issued
+    text = asm["bwd_bf16.hip"]
+    for marker in ("bwd_dkdv_kernel", "bwd_dq_kernel"):
+        body = _kernel(text, marker)
+        code = [l.split(";")[0].strip() for l in body.splitlines()]
+        code = [l for l in code if l and not l.startswith(".")]
+        copies = [i for i, l in enumerate(code) if l.startswith("global_load_lds")]
+        ends = [i for j, i in enumerate(copies) if j + 1 == len(copies) or copies[j + 1] - i > 12]
+        checked = 0
+        for end in ends:
+            nxt = next((k for k in range(end + 1, len(code)) if "s_barrier" in code[k]), None)
+            if nxt is None:
+                continue
+            reads = any(code[k].startswith("ds_read") for k in range(end + 1, nxt))
+            if not reads:
+                continue  # the ring prologue: its wait precedes its barrier anyway
+            for k in range(end + 1, nxt):
+                if code[k].startswith("s_waitcnt") and "vmcnt" in code[k]:
+                    assert nxt - k <= 8, (marker, code[k], code[k + 1:k + 4])
+            checked += 1
+        assert checked >= 4, (marker, checked)
