@@ -83,6 +83,13 @@ def load_library():
     lib.sink_attn_attention.restype = ctypes.c_int
     lib.sink_attn_tile_config.argtypes = [DP, I32]
     lib.sink_attn_tile_config.restype = ctypes.c_int
+    lib.sink_attn_fwd_padded.argtypes = [DP, P, P, P, P, P, P, P, P, I32, I32, P, P, P]
+    lib.sink_attn_fwd_padded.restype = ctypes.c_int
+    lib.sink_attn_bwd_padded.argtypes = [DP, P, P, P, P, P, P, P, P, I32, I32, P, P, P, P, P, P,
+                                         P, P, P, P]
+    lib.sink_attn_bwd_padded.restype = ctypes.c_int
+    lib.sink_attn_mask_to_seqlens.argtypes = [P, I32, I32, P, P, P, P]
+    lib.sink_attn_mask_to_seqlens.restype = ctypes.c_int
     lib.sink_attn_bwd_workspace_bytes.argtypes = [DP]
     lib.sink_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.sink_attn_bwd.argtypes = [DP, P, P, P, P, P, P, P, I32, I32, P, P, P, P, P, P, P, P, P, P]
@@ -160,7 +167,8 @@ class Call:
 
     def __init__(self, q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope,
                  out=None, lse=None, *, rms_eps=1e-6, rope_theta=1e6, softmax_scale=None,
-                 workspace=None, stream=None, return_lse=True, tile_config=SINK_ATTN_TILE_AUTO):
+                 workspace=None, stream=None, return_lse=True, tile_config=SINK_ATTN_TILE_AUTO,
+                 cu_seqlens_padded=None):
         if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
             raise ValueError("q, k, v must be THD tensors [tokens, heads, head_dim]")
         dev = q.device
@@ -173,10 +181,15 @@ class Call:
         for name, t in (("k", k), ("v", v)):
             _check_tensor(name, t, q.dtype, dev)
         _check_tensor("cu_seqlens", cu_seqlens, torch.int32, dev)
+        if cu_seqlens_padded is not None:
+            _check_tensor("cu_seqlens_padded", cu_seqlens_padded, torch.int32, dev)
+            if cu_seqlens_padded.shape != cu_seqlens.shape:
+                raise ValueError("cu_seqlens_padded must have cu_seqlens' shape")
         for name, t in (("sinks", sinks), ("qnorm_w", qnorm_w), ("knorm_w", knorm_w)):
             _check_tensor(name, t, torch.float32, dev)
         self.desc = make_desc(T, cu_seqlens.numel() - 1, Hq, Hkv, d, q.dtype, rms_eps,
                               rope_theta, softmax_scale or 0.0, tile_config=tile_config)
+        self.cu_padded = cu_seqlens_padded
         need = workspace_bytes(self.desc)
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -202,7 +215,17 @@ class Call:
         self.stream = ctypes.c_void_p(stream)
 
     def fwd(self):
-        rc = load_library().sink_attn_fwd(
+        lib = load_library()
+        if self.cu_padded is not None:
+            rc = lib.sink_attn_fwd_padded(
+                ctypes.byref(self.desc), _ptr(self.q), _ptr(self.k), _ptr(self.v),
+                _ptr(self.cu), _ptr(self.cu_padded), _ptr(self.sinks), _ptr(self.qnorm_w),
+                _ptr(self.knorm_w), self.window, self.use_rope, _ptr(self.out), _ptr(self.lse),
+                self.stream)
+            if rc:
+                raise SinkAttnError(rc, "sink_attn_fwd_padded")
+            return
+        rc = lib.sink_attn_fwd(
             ctypes.byref(self.desc), _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.cu),
             _ptr(self.sinks), _ptr(self.qnorm_w), _ptr(self.knorm_w), self.window,
             self.use_rope, _ptr(self.out), _ptr(self.lse), self.stream)
@@ -210,6 +233,8 @@ class Call:
             raise SinkAttnError(rc, "sink_attn_fwd")
 
     def prologue(self):
+        if self.cu_padded is not None:
+            raise ValueError("the two-stage entry points take unpadded THD only")
         rc = load_library().sink_attn_prologue(
             ctypes.byref(self.desc), _ptr(self.k), _ptr(self.v), _ptr(self.cu),
             _ptr(self.knorm_w), self.use_rope, self.stream)
@@ -217,6 +242,8 @@ class Call:
             raise SinkAttnError(rc, "sink_attn_prologue")
 
     def attention(self):
+        if self.cu_padded is not None:
+            raise ValueError("the two-stage entry points take unpadded THD only")
         rc = load_library().sink_attn_attention(
             ctypes.byref(self.desc), _ptr(self.q), _ptr(self.cu), _ptr(self.sinks),
             _ptr(self.qnorm_w), self.window, self.use_rope, _ptr(self.out), _ptr(self.lse),
@@ -265,7 +292,7 @@ class BwdCall:
 
     def __init__(self, q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope, out,
                  lse, dout, *, rms_eps=1e-6, rope_theta=1e6, softmax_scale=None,
-                 workspace=None, stream=None, grads=None):
+                 workspace=None, stream=None, grads=None, cu_seqlens_padded=None):
         if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
             raise ValueError("q, k, v must be THD tensors [tokens, heads, head_dim]")
         if q.dtype != torch.bfloat16:
@@ -280,6 +307,11 @@ class BwdCall:
         for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
             _check_tensor(name, t, q.dtype, dev)
         _check_tensor("cu_seqlens", cu_seqlens, torch.int32, dev)
+        if cu_seqlens_padded is not None:
+            _check_tensor("cu_seqlens_padded", cu_seqlens_padded, torch.int32, dev)
+            if cu_seqlens_padded.shape != cu_seqlens.shape:
+                raise ValueError("cu_seqlens_padded must have cu_seqlens' shape")
+        self.cu_padded = cu_seqlens_padded
         for name, t in (("sinks", sinks), ("qnorm_w", qnorm_w), ("knorm_w", knorm_w),
                         ("lse", lse)):
             _check_tensor(name, t, torch.float32, dev)
@@ -311,13 +343,19 @@ class BwdCall:
 
     def run(self):
         g = self.grads
-        rc = load_library().sink_attn_bwd(
-            ctypes.byref(self.desc), *(_ptr(t) for t in self.args), self.window, self.use_rope,
-            _ptr(self.out), _ptr(self.lse), _ptr(self.dout), _ptr(g["dq"]), _ptr(g["dk"]),
-            _ptr(g["dv"]), _ptr(g["dsinks"]), _ptr(g["dqnorm_w"]), _ptr(g["dknorm_w"]),
-            self.stream)
+        tail = (self.window, self.use_rope, _ptr(self.out), _ptr(self.lse), _ptr(self.dout),
+                _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dsinks"]),
+                _ptr(g["dqnorm_w"]), _ptr(g["dknorm_w"]), self.stream)
+        a = [_ptr(t) for t in self.args]
+        if self.cu_padded is not None:
+            rc = load_library().sink_attn_bwd_padded(
+                ctypes.byref(self.desc), *a[:4], _ptr(self.cu_padded), *a[4:], *tail)
+            name = "sink_attn_bwd_padded"
+        else:
+            rc = load_library().sink_attn_bwd(ctypes.byref(self.desc), *a, *tail)
+            name = "sink_attn_bwd"
         if rc:
-            raise SinkAttnError(rc, "sink_attn_bwd")
+            raise SinkAttnError(rc, name)
         return g
 
 
@@ -334,3 +372,71 @@ def sink_attn_bwd_workspace_bytes(total_tokens, num_docs, num_q_heads, num_kv_he
                                   dtype=torch.bfloat16) -> int:
     return bwd_workspace_bytes(make_desc(total_tokens, num_docs, num_q_heads, num_kv_heads,
                                          head_dim, dtype))
+
+
+def mask_to_seqlens(attention_mask, stream=None):
+    """Padded-THD boundaries (cu_seqlens, cu_seqlens_padded) of a BSHD
+    attention mask [batch, seq] (True / nonzero = real token), computed on the
+    device by sink_attn_mask_to_seqlens.  Raises ValueError when a row's
+    padding does not trail (such inputs have to be packed as THD); that check
+    synchronises the stream."""
+    if attention_mask.dim() != 2:
+        raise ValueError("attention_mask must be [batch, seq]")
+    dev = attention_mask.device
+    m = attention_mask
+    if m.dtype == torch.bool:
+        m = m.view(torch.uint8)
+    if m.dtype != torch.uint8:
+        raise ValueError("attention_mask must be bool or uint8")
+    m = m.contiguous()
+    B, S = m.shape
+    cu = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    cu_padded = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    bad = torch.empty(1, dtype=torch.int32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    rc = load_library().sink_attn_mask_to_seqlens(_ptr(m), B, S, _ptr(cu), _ptr(cu_padded),
+                                                  _ptr(bad), ctypes.c_void_p(stream))
+    if rc:
+        raise SinkAttnError(rc, "sink_attn_mask_to_seqlens")
+    if int(bad.item()):
+        raise ValueError(f"{int(bad.item())} row(s) of attention_mask have padding before "
+                         "real tokens; BSHD takes trailing padding only, pack such inputs "
+                         "as THD")
+    return cu, cu_padded
+
+
+def _bshd_to_thd(x):
+    if x.dim() != 4:
+        raise ValueError("BSHD tensors are [batch, seq, heads, head_dim]")
+    if not x.is_contiguous():
+        raise ValueError("BSHD tensors must be contiguous")
+    B, S, H, d = x.shape
+    return x.view(B * S, H, d)
+
+
+def sink_attn_fwd_bshd(q, k, v, attention_mask, sinks, qnorm_w, knorm_w, window, use_rope,
+                       **kw):
+    """Forward on BSHD tensors [batch, seq, heads, d] with a trailing-padding
+    attention mask [batch, seq].  Returns (out [batch, seq, Hq, d],
+    lse [Hq, batch, seq]); padding rows get out = 0 and lse = the sink."""
+    B, S = q.shape[0], q.shape[1]
+    cu, cu_padded = mask_to_seqlens(attention_mask)
+    out, lse = sink_attn_fwd(_bshd_to_thd(q), _bshd_to_thd(k), _bshd_to_thd(v), cu, sinks,
+                             qnorm_w, knorm_w, window, use_rope, cu_seqlens_padded=cu_padded,
+                             **kw)
+    return out.view(q.shape), (None if lse is None else lse.view(lse.shape[0], B, S))
+
+
+def sink_attn_bwd_bshd(q, k, v, attention_mask, sinks, qnorm_w, knorm_w, window, use_rope,
+                       out, lse, dout, **kw) -> dict:
+    """Backward of sink_attn_fwd_bshd; dq, dk, dv come back in BSHD shapes."""
+    cu, cu_padded = mask_to_seqlens(attention_mask)
+    Hq = q.shape[2]
+    g = sink_attn_bwd(_bshd_to_thd(q), _bshd_to_thd(k), _bshd_to_thd(v), cu, sinks, qnorm_w,
+                      knorm_w, window, use_rope, _bshd_to_thd(out),
+                      lse.reshape(Hq, -1), _bshd_to_thd(dout), cu_seqlens_padded=cu_padded, **kw)
+    g["dq"] = g["dq"].view(q.shape)
+    g["dk"] = g["dk"].view(k.shape)
+    g["dv"] = g["dv"].view(v.shape)
+    return g

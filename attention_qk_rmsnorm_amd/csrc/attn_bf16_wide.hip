@@ -371,7 +371,7 @@ template <bool EXACT>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_wide_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ khat,
     const bf16* __restrict__ vt, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ sched, const float* __restrict__ sinks,
+    const int32_t* __restrict__ cu_end, const int32_t* __restrict__ sched, const float* __restrict__ sinks,
     const float* __restrict__ qnorm_w, bf16* __restrict__ out, float* __restrict__ lse,
     int32_t* __restrict__ redo, int T, int Hq, int Hkv, int G, int log2G, int64_t t_pad,
     int window, int use_rope, float eps, double theta, float c_log2, int xcd_per,
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_wide_kernel(
   const int2 it = reinterpret_cast<const int2*>(sched + 4)[item];
   const int doc = it.x;
   const int doc_start = max(cu[doc], 0);
-  const int doc_end = min(cu[doc + 1], T);
+  const int doc_end = min(cu_end[doc], T);  // real end (document padding follows)
   const int m_tok = (kWaves * kColsPerWaveWide) >> log2G;
   const int tpw = kColsPerWaveWide >> log2G;  // tokens per wave
   const int a = doc_start + it.y * m_tok;
@@ -616,7 +616,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_wide_kernel(
 }  // namespace
 
 hipError_t launch_attention_bf16_wide(const bf16* q, const bf16* khat, const bf16* vt,
-                                      const int32_t* cu, const int32_t* sched,
+                                      const int32_t* cu, const int32_t* cu_end,
+                                      const int32_t* sched,
                                       const float* sinks, const float* qnorm_w, bf16* out,
                                       float* lse, int32_t* redo, int T, int D, int Hq,
                                       int Hkv, int64_t t_pad, int64_t items_ub, int window,
@@ -634,10 +635,10 @@ hipError_t launch_attention_bf16_wide(const bf16* q, const bf16* khat, const bf1
   const float c_log2 = (float)(scale * 1.4426950408889634);
   // main launch, then the follow-up that reruns the blocks it marked
   attn_fwd_bf16_wide_kernel<false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-      q, khat, vt, cu, sched, sinks, qnorm_w, out, lse, redo, T, Hq, Hkv, G, log2G, t_pad,
+      q, khat, vt, cu, cu_end, sched, sinks, qnorm_w, out, lse, redo, T, Hq, Hkv, G, log2G, t_pad,
       window, use_rope, (float)eps, theta, c_log2, xcd_per, exact_all ? 1 : 0);
   attn_fwd_bf16_wide_kernel<true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-      q, khat, vt, cu, sched, sinks, qnorm_w, out, lse, redo, T, Hq, Hkv, G, log2G, t_pad,
+      q, khat, vt, cu, cu_end, sched, sinks, qnorm_w, out, lse, redo, T, Hq, Hkv, G, log2G, t_pad,
       window, use_rope, (float)eps, theta, c_log2, xcd_per, 0);
   return hipGetLastError();
 }

@@ -18,7 +18,7 @@ template <int HD>
 __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ khat,
     const float* __restrict__ v, const int32_t* __restrict__ cu,
-    const float* __restrict__ sinks, const float* __restrict__ qnorm_w,
+    const int32_t* __restrict__ cu_end, const float* __restrict__ sinks, const float* __restrict__ qnorm_w,
     float* __restrict__ out, float* __restrict__ lse, int T, int D, int Hq, int Hkv,
     int window, int use_rope, float eps, double theta, float scale) {
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -59,7 +59,9 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
 #pragma unroll
   for (int i = 0; i < HD; ++i) acc[i] = 0.f;
   const int lo = window > 0 ? max(doc_start, t - window + 1) : doc_start;
-  for (int u = lo; u <= t; ++u) {
+  // a document-padding row sees no key: only the sink (out = 0, lse = sink)
+  const int hi = t < cu_end[doc] ? t : lo - 1;
+  for (int u = lo; u <= hi; ++u) {
     const float* kp = khat + ((int64_t)u * Hkv + g) * HD;
     float dot = 0.f;
 #pragma unroll
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
 }  // namespace
 
 hipError_t launch_attention_f32(const float* q, const float* khat, const float* v,
-                                const int32_t* cu, const float* sinks,
+                                const int32_t* cu, const int32_t* cu_end, const float* sinks,
                                 const float* qnorm_w, float* out, float* lse, int T,
                                 int D, int Hq, int Hkv, int d, int window, int use_rope,
                                 double eps, double theta, double scale,
@@ -93,11 +95,11 @@ hipError_t launch_attention_f32(const float* q, const float* khat, const float* 
   const unsigned grid = (unsigned)((n + kThreads - 1) / kThreads);
   if (d == 128)
     attn_fwd_f32_kernel<128><<<grid, kThreads, 0, stream>>>(
-        q, khat, v, cu, sinks, qnorm_w, out, lse, T, D, Hq, Hkv, window, use_rope,
+        q, khat, v, cu, cu_end, sinks, qnorm_w, out, lse, T, D, Hq, Hkv, window, use_rope,
         (float)eps, theta, (float)scale);
   else
     attn_fwd_f32_kernel<64><<<grid, kThreads, 0, stream>>>(
-        q, khat, v, cu, sinks, qnorm_w, out, lse, T, D, Hq, Hkv, window, use_rope,
+        q, khat, v, cu, cu_end, sinks, qnorm_w, out, lse, T, D, Hq, Hkv, window, use_rope,
         (float)eps, theta, (float)scale);
   return hipGetLastError();
 }

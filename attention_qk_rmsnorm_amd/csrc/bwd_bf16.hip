@@ -172,11 +172,13 @@ __device__ __forceinline__ void copy_col_tile(const char* __restrict__ src, int 
                                      (lds_void*)(uintptr_t)a, 16, 0, 0);
 }
 
-// Latest token that key u is visible to: min(document end, u + W) - 1.
-__device__ __forceinline__ int last_viewer(const int32_t* __restrict__ cu, int D, int u,
+// Latest token that key u is visible to: min(document's real end, u + W) - 1
+// (below u when u is document padding).
+__device__ __forceinline__ int last_viewer(const int32_t* __restrict__ cu,
+                                           const int32_t* __restrict__ cu_end, int D, int u,
                                            int window) {
   const int n = doc_of_token(cu, D, u);
-  int e = cu[n + 1];
+  int e = cu_end[n];
   if (window > 0 && u + window < e) e = u + window;
   return e - 1;
 }
@@ -192,10 +194,12 @@ __device__ __forceinline__ int first_key(const int32_t* __restrict__ cu, int D, 
 // pair: lane half hf holds the gradient w.r.t. the normalised, rotated vector
 // for channels 32dd + 8rq + 4hf + e at dy[16dd + 4rq + e] (dd, rq, e < 4).
 // xp points at the raw input row (+ 4hf), w at the norm weight; pos is the
-// document position (rope only).  Writes dx to dxp when ok, and dy x r (zero
-// when !ok) to wsum in dy's order.
+// document position (rope only).  ok: the row is a real token (a padding row
+// may hold anything and gets a zero gradient).  Writes dx (zero when !ok) to
+// dxp when store, and dy x r (zero when !ok) to wsum in dy's order.
 __device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const bf16* __restrict__ xp,
-                                              const float* __restrict__ w, bool ok, bool rope,
+                                              const float* __restrict__ w, bool ok, bool store,
+                                              bool rope,
                                               int pos, const double* s_invf, float eps, int hf,
                                               bf16* __restrict__ dxp, float (&wsum)[64]) {
   if (rope && ok) {
@@ -218,7 +222,7 @@ __device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const bf16* __res
       const f32x4 wv = *reinterpret_cast<const f32x4*>(w + 32 * dd + 8 * rq + 4 * hf);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x = (float)xv[e];
+        const float x = ok ? (float)xv[e] : 0.f;
         ss += x * x;
         wdx += wv[e] * dy[16 * dd + 4 * rq + e] * x;
       }
@@ -236,11 +240,11 @@ __device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const bf16* __res
       bf16x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x = (float)xv[e], g = dy[16 * dd + 4 * rq + e];
-        o[e] = (bf16)(wv[e] * g * r - x * coef);
+        const float x = ok ? (float)xv[e] : 0.f, g = dy[16 * dd + 4 * rq + e];
+        o[e] = (bf16)(ok ? wv[e] * g * r - x * coef : 0.f);
         wsum[16 * dd + 4 * rq + e] = g * x * r;
       }
-      if (ok) *reinterpret_cast<bf16x4*>(dxp + 32 * dd + 8 * rq) = o;
+      if (store) *reinterpret_cast<bf16x4*>(dxp + 32 * dd + 8 * rq) = o;
     }
 }
 
@@ -249,14 +253,16 @@ __device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const bf16* __res
 // ============================================================================
 __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
     const bf16* __restrict__ k, const bf16* __restrict__ v, const int32_t* __restrict__ cu,
-    const float* __restrict__ knorm_w, int T, int D, int Hkv, int n_kt, float eps,
-    double theta, int use_rope, char* __restrict__ keys) {
+    const int32_t* __restrict__ cu_end, const float* __restrict__ knorm_w, int T, int D,
+    int Hkv, int n_kt, float eps, double theta, int use_rope, char* __restrict__ keys) {
   __shared__ double s_invf[64];
+  __shared__ int s_real[kKeyTile];  // inside [0, T) and not document padding
   const int tid = threadIdx.x;
   const int tile = blockIdx.x / Hkv, g = blockIdx.x - tile * Hkv;
   const int t0 = tile * kKeyTile;
   char* img = keys + ((size_t)g * n_kt + tile) * kKeyTileBytes;
   if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
+  if (tid < kKeyTile) s_real[tid] = t0 + tid < T && t0 + tid < cu_end[doc_of_token(cu, D, t0 + tid)];
   __syncthreads();
   // V rows straight into the V image
 #pragma unroll
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
     const int r = idx >> 4, c = idx & 15;
     const int t = t0 + r;
     uint4 val = make_uint4(0, 0, 0, 0);
-    if (t < T) val = *reinterpret_cast<const uint4*>(v + ((size_t)t * Hkv + g) * kHeadDim + 8 * c);
+    if (s_real[r]) val = *reinterpret_cast<const uint4*>(v + ((size_t)t * Hkv + g) * kHeadDim + 8 * c);
     *reinterpret_cast<uint4*>(img + kKT + r * 256 + 16 * (c ^ bswz(r))) = val;
   }
   // K rows: RMSNorm (+RoPE), 8 lanes per token (channels 8c.. and 64+8c..)
@@ -274,8 +280,9 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
     const int r = (tid >> 3) + 32 * it;
     const int c = tid & 7;
     const int t = t0 + r;
+    const bool real = s_real[r];
     float x[16];
-    if (t < T) {
+    if (real) {
       const bf16* kp = k + ((size_t)t * Hkv + g) * kHeadDim;
       const bf16x8 lo = *reinterpret_cast<const bf16x8*>(kp + 8 * c);
       const bf16x8 hi = *reinterpret_cast<const bf16x8*>(kp + 64 + 8 * c);
@@ -294,13 +301,13 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
     ss += __shfl_xor(ss, 1, 8);
     ss += __shfl_xor(ss, 2, 8);
     ss += __shfl_xor(ss, 4, 8);
-    const float inv = t < T ? 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps) : 0.f;
+    const float inv = real ? 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps) : 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       x[e] *= inv * knorm_w[8 * c + e];
       x[8 + e] *= inv * knorm_w[64 + 8 * c + e];
     }
-    if (use_rope && t < T) {
+    if (use_rope && real) {
       const int p = t - cu[doc_of_token(cu, D, t)];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -328,7 +335,8 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
 __global__ __launch_bounds__(kThreads) void bwd_cols_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ out, const bf16* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ sinks,
-    const int32_t* __restrict__ cu, const float* __restrict__ qnorm_w, int T, int D, int Hq,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_end,
+    const float* __restrict__ qnorm_w, int T, int D, int Hq,
     int Hkv, int G, int log2G, int n_ct, float eps, double theta, int use_rope, float c_log2,
     char* __restrict__ cols, float* __restrict__ dsink_part) {
   __shared__ double s_invf[64];
@@ -344,7 +352,9 @@ __global__ __launch_bounds__(kThreads) void bwd_cols_kernel(
   const int col = tid >> 3, c = tid & 7;
   const int t = ct * tpt + (col >> log2G);
   const int h = g * G + (col & (G - 1));
-  const bool ok = t < T;
+  // a real query: inside [0, T) and not document padding (padded rows have no
+  // gradient: their out is the constant 0)
+  const bool ok = t < T && t < cu_end[doc_of_token(cu, D, t)];
   float x[16], y[16], o[16];
   if (ok) {
     const size_t row = ((size_t)t * Hq + h) * kHeadDim;
@@ -431,7 +441,8 @@ __global__ __launch_bounds__(kThreads) void bwd_cols_kernel(
 // ============================================================================
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     const bf16* __restrict__ k, const char* __restrict__ keys, const char* __restrict__ cols,
-    const int32_t* __restrict__ cu, const float* __restrict__ knorm_w, int T, int D, int Hkv,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_end,
+    const float* __restrict__ knorm_w, int T, int D, int Hkv,
     int log2G, int n_kt, int n_ct, int window, int use_rope, float eps, double theta,
     bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ dwk_part) {
   // the ring: one array per slot, so that the compiler can tell a copy into
@@ -472,12 +483,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const bool u_ok = u < T;
   const int uc = u_ok ? u : T - 1;
   const int ua = kb0 + 32 * wave, ub = min(ua + 31, T - 1);
-  const int u_last = u_ok ? last_viewer(cu, D, u, window) : -1;  // visible tokens [u, u_last]
-  const int ua_last = ua < T ? last_viewer(cu, D, ua, window) : -1;
+  const int u_last = u_ok ? last_viewer(cu, cu_end, D, u, window) : -1;  // visible tokens [u, u_last]
+  const bool u_real = u_ok && u_last >= u;  // else document padding: no gradient
+  const int ua_last = ua < T ? last_viewer(cu, cu_end, D, ua, window) : -1;
   // the block's column tiles: tokens [kb0, last viewer of its last key]
   const int kmax = min(kb0 + 127, T - 1);
-  const int t_hi = kb0 < T ? last_viewer(cu, D, kmax, window) : -1;
-  const int c_lo = kb0 / tpt, c_hi = t_hi >= 0 ? t_hi / tpt : c_lo - 1;
+  // (a block of padding keys only still walks one, fully masked, tile)
+  const int t_hi = max(last_viewer(cu, cu_end, D, kmax, window), kb0);
+  const int c_lo = kb0 / tpt, c_hi = t_hi / tpt;
   const char* ctiles = cols + (size_t)g * n_ct * kColTileBytes;
 
   // K and V rows of this lane's key as B operands (channels 16kk + 8hf ..)
@@ -714,9 +727,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
       for (int r = 0; r < 16; ++r) dy[16 * dd + r] = acc_dk[dd][r] * kLn2;
-    const int pos = u_ok && use_rope ? u - cu[doc_of_token(cu, D, u)] : 0;
+    const int pos = u_real && use_rope ? u - cu[doc_of_token(cu, D, u)] : 0;
     float wsum[64];
-    norm_rope_bwd(dy, k + ((size_t)uc * Hkv + g) * kHeadDim + 4 * hf, knorm_w, u_ok,
+    norm_rope_bwd(dy, k + ((size_t)uc * Hkv + g) * kHeadDim + 4 * hf, knorm_w, u_real, u_ok,
                   use_rope != 0, pos, s_invf, eps, hf,
                   dk + ((size_t)uc * Hkv + g) * kHeadDim + 4 * hf, wsum);
     // the weight gradient sums dy x r over the block's keys in a fixed order,
@@ -751,7 +764,8 @@ static_assert(kKeyCopyOps * (kKeyBufs - 2) < 64, "vmcnt holds 6 bits");
 
 __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
     const bf16* __restrict__ q, const char* __restrict__ keys, const char* __restrict__ cols,
-    const int32_t* __restrict__ cu, const float* __restrict__ qnorm_w, int T, int D, int Hq,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_end,
+    const float* __restrict__ qnorm_w, int T, int D, int Hq,
     int Hkv, int G, int log2G, int n_kt, int n_ct, int window, int use_rope, float eps,
     double theta, float scale, bf16* __restrict__ dq, float* __restrict__ dwq_part) {
   // the ring of key tiles, one array per slot (see the dK/dV kernel)
@@ -777,8 +791,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
   // this lane's column: token t, head h
   const int t = ct * tpt + (col >> log2G);
   const int h = g * G + (col & (G - 1));
-  const bool t_ok = ct < n_ct && t < T;
-  const int tcl = t_ok ? t : 0;
+  const bool t_in = ct < n_ct && t < T;
+  const bool t_ok = t_in && t < cu_end[doc_of_token(cu, D, t)];  // a real query
+  const int tcl = t_in ? t : 0;
   const int t_lo = t_ok ? first_key(cu, D, t, window) : 1 << 30;  // visible keys [t_lo, t]
   // the wave's tokens and the block's key range
   const int ta = ct * tpt, tb = min(ta + tpt - 1, T - 1);
@@ -914,7 +929,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
       for (int r = 0; r < 16; ++r) dy[16 * dd + r] = acc[dd][r] * scale;
     const int pos = t_ok && use_rope ? t - cu[doc_of_token(cu, D, t)] : 0;
     float wsum[64];
-    norm_rope_bwd(dy, q + ((size_t)tcl * Hq + h) * kHeadDim + 4 * hf, qnorm_w, t_ok,
+    norm_rope_bwd(dy, q + ((size_t)tcl * Hq + h) * kHeadDim + 4 * hf, qnorm_w, t_ok, t_in,
                   use_rope != 0, pos, s_invf, eps, hf,
                   dq + ((size_t)tcl * Hq + h) * kHeadDim + 4 * hf, wsum);
     // the weight gradient sums dy x r over the block's 256 columns in a fixed
@@ -984,7 +999,7 @@ __global__ __launch_bounds__(kThreads) void bwd_reduce_kernel(
 
 }  // namespace
 
-BwdWorkspace plan_bwd_workspace(int64_t T, int Hq, int Hkv) {
+BwdWorkspace plan_bwd_workspace(int64_t T, int64_t D, int Hq, int Hkv) {
   BwdWorkspace w;
   if (T <= 0) return w;
   const int G = Hq / Hkv;
@@ -1004,12 +1019,14 @@ BwdWorkspace plan_bwd_workspace(int64_t T, int Hq, int Hkv) {
   off += sizeof(float) * (size_t)w.n_qblk * kHeadDim;
   w.dwk_off = off = round_up(off, 256);
   off += sizeof(float) * (size_t)w.n_kblk * kHeadDim;
+  w.ends_off = off = round_up(off, 256);
+  off += sizeof(int32_t) * (size_t)(D + 1);
   w.total = round_up(off, 256);
   return w;
 }
 
 hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const int32_t* cu,
-                           const float* sinks, const float* qnorm_w, const float* knorm_w,
+                           const int32_t* cu_end, const float* sinks, const float* qnorm_w, const float* knorm_w,
                            const bf16* out, const float* lse, const bf16* dout, bf16* dq,
                            bf16* dk, bf16* dv, float* dsinks, float* dqnorm_w,
                            float* dknorm_w, int T, int D, int Hq, int Hkv, int window,
@@ -1025,15 +1042,15 @@ hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const in
   float* dwk_part = reinterpret_cast<float*>(ws + w.dwk_off);
   const float c_log2 = (float)(scale * 1.4426950408889634);
   bwd_keys_kernel<<<dim3((unsigned)(w.n_kt * Hkv)), dim3(kThreads), 0, stream>>>(
-      k, v, cu, knorm_w, T, D, Hkv, (int)w.n_kt, (float)eps, theta, use_rope, keys);
+      k, v, cu, cu_end, knorm_w, T, D, Hkv, (int)w.n_kt, (float)eps, theta, use_rope, keys);
   bwd_cols_kernel<<<dim3((unsigned)(w.n_ct * Hkv)), dim3(kThreads), 0, stream>>>(
-      q, out, dout, lse, sinks, cu, qnorm_w, T, D, Hq, Hkv, G, log2G, (int)w.n_ct, (float)eps,
+      q, out, dout, lse, sinks, cu, cu_end, qnorm_w, T, D, Hq, Hkv, G, log2G, (int)w.n_ct, (float)eps,
       theta, use_rope, c_log2, cols, dsink_part);
   bwd_dkdv_kernel<<<dim3((unsigned)w.n_kblk), dim3(kThreads), 0, stream>>>(
-      k, keys, cols, cu, knorm_w, T, D, Hkv, log2G, (int)w.n_kt, (int)w.n_ct, window, use_rope,
+      k, keys, cols, cu, cu_end, knorm_w, T, D, Hkv, log2G, (int)w.n_kt, (int)w.n_ct, window, use_rope,
       (float)eps, theta, dk, dv, dwk_part);
   bwd_dq_kernel<<<dim3((unsigned)w.n_qblk), dim3(kDqThreads), 0, stream>>>(
-      q, keys, cols, cu, qnorm_w, T, D, Hq, Hkv, G, log2G, (int)w.n_kt, (int)w.n_ct, window,
+      q, keys, cols, cu, cu_end, qnorm_w, T, D, Hq, Hkv, G, log2G, (int)w.n_kt, (int)w.n_ct, window,
       use_rope, (float)eps, theta, (float)scale, dq, dwq_part);
   bwd_reduce_kernel<<<dim3(Hq + 2 * kHeadDim), dim3(kThreads), 0, stream>>>(
       dsink_part, dwq_part, dwk_part, Hq, G, (int)w.n_ct, (int)w.n_qblk, (int)w.n_kblk,

@@ -17,7 +17,8 @@
 //     Both are written as the exact byte image the attention kernel keeps in
 //     LDS (16-byte chunks swizzled, see sa_device.h), so its tile copy is a
 //     straight 16 KiB memcpy.
-//     Padding keys [T, t_pad) are written as zeros.
+//     Padding keys [T, t_pad) and document padding (tokens past a
+//     document's real end, cu_end) are written as zeros.
 // fp32 debug path: RMSNorm (+RoPE) of K into k_hat fp32 [T][Hkv][d], and a
 // copy of V beside it, so the attention stage reads only the workspace.
 #include "sa_device.h"
@@ -32,7 +33,8 @@ constexpr int kLdsPrefix = 4096;  // documents whose prefix fits in LDS
 // Varlen schedule.  sched[0] = number of items; items (int2 at sched + 4) hold
 // (document, block index in document) in descending order of block position.
 // prefix_g is global scratch of D + 1 ints used when D + 1 > kLdsPrefix.
-__device__ void build_schedule(const int32_t* __restrict__ cu, int D, int m_tok,
+__device__ void build_schedule(const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_end,
+                               int D, int m_tok,
                                int32_t* __restrict__ sched, int64_t items_ub,
                                int32_t* __restrict__ prefix_g) {
   __shared__ int s_scan[kThreads];
@@ -45,7 +47,7 @@ __device__ void build_schedule(const int32_t* __restrict__ cu, int D, int m_tok,
     const int n = base + tid;
     int cnt = 0;
     if (n < D) {
-      const int len = cu[n + 1] - cu[n];
+      const int len = cu_end[n] - cu[n];
       cnt = len > 0 ? (len + m_tok - 1) / m_tok : 0;
     }
     s_scan[tid] = cnt;
@@ -83,7 +85,8 @@ __device__ void build_schedule(const int32_t* __restrict__ cu, int D, int m_tok,
 
 __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
     const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const int32_t* __restrict__ cu, const float* __restrict__ knorm_w, int T, int D,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_end,
+    const float* __restrict__ knorm_w, int T, int D,
     int Hkv, int64_t t_pad, int m_tok, int m_tok_wide, float eps, double theta,
     int use_rope, bf16* __restrict__ khat, bf16* __restrict__ vt,
     int32_t* __restrict__ sched, int32_t* __restrict__ sched_wide) {
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
     const int mt = wide ? m_tok_wide : m_tok;
     const int64_t items_ub = T / mt + D;
     int32_t* sc = wide ? sched_wide : sched;
-    build_schedule(cu, D, mt, sc, items_ub, sc + 4 + 2 * items_ub);
+    build_schedule(cu, cu_end, D, mt, sc, items_ub, sc + 4 + 2 * items_ub);
     return;
   }
   __shared__ double s_invf[64];
@@ -108,6 +111,15 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
   // channel i with i + 64
   if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
 
+  // real tokens of the tile: inside [0, T) and not document padding (padded
+  // rows are written as zeros, whatever the input holds there)
+  __shared__ int s_real[kKeyTile];
+  if (tid < kKeyTile) {
+    const int t = t0 + tid;
+    s_real[tid] = t < T && t < cu_end[doc_of_token(cu, D, t)];
+  }
+  __syncthreads();
+
   // V tile [64 tokens][128] into LDS
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -115,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
     const int tt = c >> 4, cc = c & 15;
     const int t = t0 + tt;
     uint4 val = make_uint4(0, 0, 0, 0);
-    if (t < T) val = *reinterpret_cast<const uint4*>(v + ((size_t)t * Hkv + g) * kHeadDim + cc * 8);
+    if (s_real[tt]) val = *reinterpret_cast<const uint4*>(v + ((size_t)t * Hkv + g) * kHeadDim + cc * 8);
     *reinterpret_cast<uint4*>(&s_v[tt][cc * 8]) = val;
   }
   __syncthreads();
@@ -126,8 +138,9 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
     const int tt = (tid >> 3) + 32 * it;
     const int c = tid & 7;
     const int t = t0 + tt;
+    const bool real = s_real[tt];
     float x[16];
-    if (t < T) {
+    if (real) {
       const bf16* kp = k + ((size_t)t * Hkv + g) * kHeadDim;
       const bf16x8 lo = *reinterpret_cast<const bf16x8*>(kp + 8 * c);
       const bf16x8 hi = *reinterpret_cast<const bf16x8*>(kp + 64 + 8 * c);
@@ -146,13 +159,14 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
     ss += __shfl_xor(ss, 1, 8);
     ss += __shfl_xor(ss, 2, 8);
     ss += __shfl_xor(ss, 4, 8);
-    const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
+    // rows that are not real stay zero (no 0 * inf when eps == 0)
+    const float inv = real ? 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps) : 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       x[e] *= inv * knorm_w[8 * c + e];
       x[8 + e] *= inv * knorm_w[64 + 8 * c + e];
     }
-    if (use_rope && t < T) {
+    if (use_rope && real) {
       const int p = t - cu[doc_of_token(cu, D, t)];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -197,21 +211,23 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
 template <int HD>
 __global__ __launch_bounds__(kThreads) void prologue_f32_kernel(
     const float* __restrict__ k, const float* __restrict__ v,
-    const int32_t* __restrict__ cu, const float* __restrict__ knorm_w, int T, int D,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_end,
+    const float* __restrict__ knorm_w, int T, int D,
     int Hkv, float eps, double theta, int use_rope, float* __restrict__ khat,
     float* __restrict__ vcopy) {
   const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (idx >= (int64_t)T * Hkv) return;
   const int t = (int)(idx / Hkv);
+  const bool real = t < cu_end[doc_of_token(cu, D, t)];  // else document padding
   const float* kp = k + idx * HD;
   float x[HD];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < HD; ++i) {
-    x[i] = kp[i];
+    x[i] = real ? kp[i] : 0.f;
     ss += x[i] * x[i];
   }
-  const float inv = 1.0f / sqrtf(ss * (1.0f / HD) + eps);
+  const float inv = real ? 1.0f / sqrtf(ss * (1.0f / HD) + eps) : 0.f;
 #pragma unroll
   for (int i = 0; i < HD; ++i) x[i] *= inv * knorm_w[i];
   if (use_rope) {
@@ -230,37 +246,37 @@ __global__ __launch_bounds__(kThreads) void prologue_f32_kernel(
 #pragma unroll
   for (int i = 0; i < HD; ++i) {
     kh[i] = x[i];
-    vc[i] = vp[i];
+    vc[i] = real ? vp[i] : 0.f;
   }
 }
 
 }  // namespace
 
 hipError_t launch_prologue_bf16(const bf16* k, const bf16* v, const int32_t* cu,
-                                const float* knorm_w, int T, int D, int Hkv,
+                                const int32_t* cu_end, const float* knorm_w, int T, int D, int Hkv,
                                 int64_t t_pad, int m_tok, int m_tok_wide, double eps,
                                 double theta, int use_rope, bf16* khat, bf16* vt,
                                 int32_t* sched, int32_t* sched_wide, hipStream_t stream) {
   const int64_t n_tiles = t_pad / kKeyTile;
   const int64_t grid = 2 + n_tiles * Hkv;
   prologue_bf16_kernel<<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-      k, v, cu, knorm_w, T, D, Hkv, t_pad, m_tok, m_tok_wide, (float)eps, theta, use_rope,
+      k, v, cu, cu_end, knorm_w, T, D, Hkv, t_pad, m_tok, m_tok_wide, (float)eps, theta, use_rope,
       khat, vt, sched, sched_wide);
   return hipGetLastError();
 }
 
 hipError_t launch_prologue_f32(const float* k, const float* v, const int32_t* cu,
-                               const float* knorm_w, int T, int D, int Hkv, int d,
+                               const int32_t* cu_end, const float* knorm_w, int T, int D, int Hkv, int d,
                                double eps, double theta, int use_rope, float* khat,
                                float* vcopy, hipStream_t stream) {
   const int64_t n = (int64_t)T * Hkv;
   const unsigned grid = (unsigned)((n + kThreads - 1) / kThreads);
   if (d == 128)
     prologue_f32_kernel<128><<<grid, kThreads, 0, stream>>>(
-        k, v, cu, knorm_w, T, D, Hkv, (float)eps, theta, use_rope, khat, vcopy);
+        k, v, cu, cu_end, knorm_w, T, D, Hkv, (float)eps, theta, use_rope, khat, vcopy);
   else
     prologue_f32_kernel<64><<<grid, kThreads, 0, stream>>>(
-        k, v, cu, knorm_w, T, D, Hkv, (float)eps, theta, use_rope, khat, vcopy);
+        k, v, cu, cu_end, knorm_w, T, D, Hkv, (float)eps, theta, use_rope, khat, vcopy);
   return hipGetLastError();
 }
 

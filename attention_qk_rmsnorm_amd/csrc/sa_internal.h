@@ -45,6 +45,7 @@ struct Workspace {
   size_t sched_off = 0;      // narrow schedule: int32 n_items, int2 items[items_ub], prefix
   size_t sched_wide_off = 0; // wide schedule, same format
   size_t redo_off = 0;       // int32 per wide workgroup: rerun with the exact row max
+  size_t ends_off = 0;       // int32 [D]: real end of every document (padded THD)
   size_t total = 0;
 };
 
@@ -70,21 +71,31 @@ struct BwdWorkspace {
   int64_t n_kblk = 0;  // dK/dV workgroups (128 keys x kv head)
   int64_t n_qblk = 0;  // dQ workgroups (256 columns x kv head)
   size_t keys_off = 0, cols_off = 0, dsink_off = 0, dwq_off = 0, dwk_off = 0;
+  size_t ends_off = 0;  // int32 [D]: real end of every document (padded THD)
   size_t total = 0;
 };
 
-BwdWorkspace plan_bwd_workspace(int64_t T, int Hq, int Hkv);
+BwdWorkspace plan_bwd_workspace(int64_t T, int64_t D, int Hq, int Hkv);
+
+// Padded THD support (sink_attn_api.hip): real document ends from
+// cu_seqlens (real lengths) and cu_seqlens_padded (starts), and the output rows
+// of padding tokens (out = 0, lse = the sink).
+hipError_t launch_doc_ends(const int32_t* cu, const int32_t* cu_padded, int D, int32_t* ends,
+                           hipStream_t stream);
+hipError_t launch_pad_fill(const int32_t* starts, const int32_t* ends, int D, int T, int Hq,
+                           int d, int dtype, const float* sinks, void* out, float* lse,
+                           hipStream_t stream);
 
 // ---- launch wrappers (return hipGetLastError after the launches) ----------
 
 hipError_t launch_prologue_bf16(const bf16* k, const bf16* v, const int32_t* cu,
-                                const float* knorm_w, int T, int D, int Hkv,
+                                const int32_t* cu_end, const float* knorm_w, int T, int D, int Hkv,
                                 int64_t t_pad, int m_tok, int m_tok_wide, double eps,
                                 double theta, int use_rope, bf16* khat, bf16* vt,
                                 int32_t* sched, int32_t* sched_wide, hipStream_t stream);
 
 hipError_t launch_attention_bf16(const bf16* q, const bf16* khat, const bf16* vt,
-                                 const int32_t* cu, const int32_t* sched,
+                                 const int32_t* cu, const int32_t* cu_end, const int32_t* sched,
                                  const float* sinks, const float* qnorm_w, bf16* out,
                                  float* lse, int T, int D, int Hq, int Hkv,
                                  int64_t t_pad, int64_t items_ub, int window,
@@ -92,7 +103,8 @@ hipError_t launch_attention_bf16(const bf16* q, const bf16* khat, const bf16* vt
                                  double scale, hipStream_t stream);
 
 hipError_t launch_attention_bf16_wide(const bf16* q, const bf16* khat, const bf16* vt,
-                                      const int32_t* cu, const int32_t* sched,
+                                      const int32_t* cu, const int32_t* cu_end,
+                                      const int32_t* sched,
                                       const float* sinks, const float* qnorm_w, bf16* out,
                                       float* lse, int32_t* redo, int T, int D, int Hq,
                                       int Hkv, int64_t t_pad, int64_t items_ub, int window,
@@ -100,7 +112,7 @@ hipError_t launch_attention_bf16_wide(const bf16* q, const bf16* khat, const bf1
                                       bool exact_all, hipStream_t stream);
 
 hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const int32_t* cu,
-                           const float* sinks, const float* qnorm_w, const float* knorm_w,
+                           const int32_t* cu_end, const float* sinks, const float* qnorm_w, const float* knorm_w,
                            const bf16* out, const float* lse, const bf16* dout, bf16* dq,
                            bf16* dk, bf16* dv, float* dsinks, float* dqnorm_w,
                            float* dknorm_w, int T, int D, int Hq, int Hkv, int window,
@@ -108,12 +120,12 @@ hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const in
                            const BwdWorkspace& w, hipStream_t stream);
 
 hipError_t launch_prologue_f32(const float* k, const float* v, const int32_t* cu,
-                               const float* knorm_w, int T, int D, int Hkv, int d,
+                               const int32_t* cu_end, const float* knorm_w, int T, int D, int Hkv, int d,
                                double eps, double theta, int use_rope, float* khat,
                                float* vcopy, hipStream_t stream);
 
 hipError_t launch_attention_f32(const float* q, const float* khat, const float* v,
-                                const int32_t* cu, const float* sinks,
+                                const int32_t* cu, const int32_t* cu_end, const float* sinks,
                                 const float* qnorm_w, float* out, float* lse, int T,
                                 int D, int Hq, int Hkv, int d, int window, int use_rope,
                                 double eps, double theta, double scale,

@@ -7,7 +7,7 @@
 
 #include <math.h>
 
-#include "sa_internal.h"
+#include "sa_device.h"
 
 namespace sa {
 
@@ -41,9 +41,107 @@ Workspace plan_workspace(int64_t T, int64_t D, int Hq, int Hkv, int d, int dtype
     w.vt_off = off;
     off += (size_t)T * Hkv * d * sizeof(float);
   }
+  w.ends_off = off = round_up(off, 256);
+  off += sizeof(int32_t) * (size_t)(D + 1);
   w.total = round_up(off, 256);
   return w;
 }
+
+namespace {
+
+__global__ void doc_ends_kernel(const int32_t* __restrict__ cu,
+                                const int32_t* __restrict__ cu_padded, int D,
+                                int32_t* __restrict__ ends) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  if (n < D) ends[n] = cu_padded[n] + (cu[n + 1] - cu[n]);
+}
+
+// One thread per (token, head): rows of document padding get out = 0 and
+// lse = sinks[h] (their softmax holds the sink alone).
+template <typename T_OUT>
+__global__ void pad_fill_kernel(const int32_t* __restrict__ starts,
+                                const int32_t* __restrict__ ends, int D, int T, int Hq, int d,
+                                const float* __restrict__ sinks, T_OUT* __restrict__ out,
+                                float* __restrict__ lse) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)T * Hq) return;
+  const int t = (int)(idx / Hq), h = (int)(idx - (int64_t)t * Hq);
+  if (t < ends[doc_of_token(starts, D, t)]) return;
+  T_OUT* o = out + idx * d;
+  for (int i = 0; i < d; ++i) o[i] = (T_OUT)0.f;
+  if (lse != nullptr) lse[(int64_t)h * T + t] = sinks[h];
+}
+
+}  // namespace
+
+hipError_t launch_doc_ends(const int32_t* cu, const int32_t* cu_padded, int D, int32_t* ends,
+                           hipStream_t stream) {
+  doc_ends_kernel<<<dim3((unsigned)((D + 255) / 256)), dim3(256), 0, stream>>>(cu, cu_padded,
+                                                                               D, ends);
+  return hipGetLastError();
+}
+
+hipError_t launch_pad_fill(const int32_t* starts, const int32_t* ends, int D, int T, int Hq,
+                           int d, int dtype, const float* sinks, void* out, float* lse,
+                           hipStream_t stream) {
+  const int64_t n = (int64_t)T * Hq;
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (dtype == SINK_ATTN_BF16)
+    pad_fill_kernel<bf16><<<dim3(grid), dim3(256), 0, stream>>>(
+        starts, ends, D, T, Hq, d, sinks, static_cast<bf16*>(out), lse);
+  else
+    pad_fill_kernel<float><<<dim3(grid), dim3(256), 0, stream>>>(
+        starts, ends, D, T, Hq, d, sinks, static_cast<float*>(out), lse);
+  return hipGetLastError();
+}
+
+namespace {
+
+// BSHD attention mask [batch][seq] (nonzero = real token) to padded THD
+// boundaries, one workgroup walking the rows in order: the real length of row
+// b is its count of real tokens; padding must trail (the row is a prefix of
+// real tokens), else the row is counted in bad_rows.
+__global__ void mask_to_seqlens_kernel(const uint8_t* __restrict__ mask, int batch, int seq,
+                                       int32_t* __restrict__ cu, int32_t* __restrict__ cu_padded,
+                                       int32_t* __restrict__ bad_rows) {
+  __shared__ int s_count, s_first_pad, s_last_real;
+  int running = 0, bad = 0;
+  if (threadIdx.x == 0) {
+    cu[0] = 0;
+    cu_padded[0] = 0;
+  }
+  for (int b = 0; b < batch; ++b) {
+    if (threadIdx.x == 0) {
+      s_count = 0;
+      s_first_pad = seq;
+      s_last_real = -1;
+    }
+    __syncthreads();
+    int count = 0, first_pad = seq, last_real = -1;
+    for (int i = threadIdx.x; i < seq; i += blockDim.x) {
+      if (mask[(size_t)b * seq + i]) {
+        ++count;
+        last_real = i;
+      } else if (first_pad == seq) {
+        first_pad = i;
+      }
+    }
+    atomicAdd(&s_count, count);
+    atomicMin(&s_first_pad, first_pad);
+    atomicMax(&s_last_real, last_real);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      running += s_count;
+      bad += s_first_pad < s_last_real;
+      cu[b + 1] = running;
+      cu_padded[b + 1] = (b + 1) * seq;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *bad_rows = bad;
+}
+
+}  // namespace
 
 }  // namespace sa
 
@@ -140,15 +238,15 @@ int check_attention(const sink_attn_desc* d, const void* q, const int32_t* cu,
 }
 
 int launch_prologue(const sink_attn_desc* d, const void* k, const void* v,
-                    const int32_t* cu, const float* knorm_w, int32_t use_rope,
-                    hipStream_t stream) {
+                    const int32_t* cu, const int32_t* cu_end, const float* knorm_w,
+                    int32_t use_rope, hipStream_t stream) {
   const sa::Workspace w = plan(d);
   char* ws = static_cast<char*>(d->workspace);
   hipError_t e;
   if (d->dtype == SINK_ATTN_BF16) {
     const int G = d->num_q_heads / d->num_kv_heads;
     e = sa::launch_prologue_bf16(
-        static_cast<const sa::bf16*>(k), static_cast<const sa::bf16*>(v), cu, knorm_w,
+        static_cast<const sa::bf16*>(k), static_cast<const sa::bf16*>(v), cu, cu_end, knorm_w,
         d->total_tokens, d->num_docs, d->num_kv_heads, w.t_pad, sa::tokens_per_block(G),
         sa::tokens_per_block_wide(G), d->rms_eps, d->rope_theta, use_rope,
         reinterpret_cast<sa::bf16*>(ws + w.khat_off), reinterpret_cast<sa::bf16*>(ws + w.vt_off),
@@ -156,7 +254,7 @@ int launch_prologue(const sink_attn_desc* d, const void* k, const void* v,
         reinterpret_cast<int32_t*>(ws + w.sched_wide_off), stream);
   } else {
     e = sa::launch_prologue_f32(static_cast<const float*>(k), static_cast<const float*>(v), cu,
-                                knorm_w, d->total_tokens, d->num_docs, d->num_kv_heads,
+                                cu_end, knorm_w, d->total_tokens, d->num_docs, d->num_kv_heads,
                                 d->head_dim, d->rms_eps, d->rope_theta, use_rope,
                                 reinterpret_cast<float*>(ws + w.khat_off),
                                 reinterpret_cast<float*>(ws + w.vt_off), stream);
@@ -164,7 +262,8 @@ int launch_prologue(const sink_attn_desc* d, const void* k, const void* v,
   return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;
 }
 
-int launch_attention(const sink_attn_desc* d, const void* q, const int32_t* cu, const float* sinks, const float* qnorm_w,
+int launch_attention(const sink_attn_desc* d, const void* q, const int32_t* cu,
+                     const int32_t* cu_end, const float* sinks, const float* qnorm_w,
                      int32_t window, int32_t use_rope, void* out, float* lse,
                      hipStream_t stream) {
   const sa::Workspace w = plan(d);
@@ -174,7 +273,7 @@ int launch_attention(const sink_attn_desc* d, const void* q, const int32_t* cu, 
   if (tile == sa::kTileWide || tile == sa::kTileWideExact) {
     e = sa::launch_attention_bf16_wide(
         static_cast<const sa::bf16*>(q), reinterpret_cast<const sa::bf16*>(ws + w.khat_off),
-        reinterpret_cast<const sa::bf16*>(ws + w.vt_off), cu,
+        reinterpret_cast<const sa::bf16*>(ws + w.vt_off), cu, cu_end,
         reinterpret_cast<const int32_t*>(ws + w.sched_wide_off), sinks, qnorm_w,
         static_cast<sa::bf16*>(out), lse, reinterpret_cast<int32_t*>(ws + w.redo_off),
         d->total_tokens, d->num_docs, d->num_q_heads, d->num_kv_heads, w.t_pad,
@@ -184,14 +283,15 @@ int launch_attention(const sink_attn_desc* d, const void* q, const int32_t* cu, 
     e = sa::launch_attention_bf16(
         static_cast<const sa::bf16*>(q), reinterpret_cast<const sa::bf16*>(ws + w.khat_off),
         reinterpret_cast<const sa::bf16*>(ws + w.vt_off),
-        cu, reinterpret_cast<const int32_t*>(ws + w.sched_off), sinks, qnorm_w,
+        cu, cu_end, reinterpret_cast<const int32_t*>(ws + w.sched_off), sinks, qnorm_w,
         static_cast<sa::bf16*>(out), lse, d->total_tokens, d->num_docs, d->num_q_heads,
         d->num_kv_heads, w.t_pad, w.items_ub, window, use_rope, d->rms_eps, d->rope_theta,
         softmax_scale(d), stream);
   } else {
     e = sa::launch_attention_f32(
         static_cast<const float*>(q), reinterpret_cast<const float*>(ws + w.khat_off),
-        reinterpret_cast<const float*>(ws + w.vt_off), cu, sinks, qnorm_w, static_cast<float*>(out), lse,
+        reinterpret_cast<const float*>(ws + w.vt_off), cu, cu_end, sinks, qnorm_w,
+        static_cast<float*>(out), lse,
         d->total_tokens, d->num_docs, d->num_q_heads, d->num_kv_heads, d->head_dim, window,
         use_rope, d->rms_eps, d->rope_theta, softmax_scale(d), stream);
   }
@@ -199,7 +299,7 @@ int launch_attention(const sink_attn_desc* d, const void* q, const int32_t* cu, 
 }
 
 sa::BwdWorkspace plan_bwd(const sink_attn_desc* d) {
-  return sa::plan_bwd_workspace(d->total_tokens, d->num_q_heads, d->num_kv_heads);
+  return sa::plan_bwd_workspace(d->total_tokens, d->num_docs, d->num_q_heads, d->num_kv_heads);
 }
 
 int check_bwd(const sink_attn_desc* d, const void* q, const void* k, const void* v,
@@ -239,6 +339,85 @@ __global__ void zero_f32_kernel(float* a, int na, float* b, int nb, float* c, in
   if (i < nc) c[i] = 0.f;
 }
 
+// Document boundaries the kernels use: starts (D + 1 entries, searched to
+// find a token's document) and real ends (D entries).  Unpadded THD: both
+// from cu_seqlens.  Padded THD: starts = cu_seqlens_padded, ends computed
+// into the workspace from the real lengths.
+struct Docs {
+  const int32_t* starts;
+  const int32_t* ends;
+};
+
+hipError_t doc_bounds(const sink_attn_desc* d, const int32_t* cu, const int32_t* cu_padded,
+                      size_t ends_off, hipStream_t s, Docs* out) {
+  if (cu_padded == nullptr) {
+    *out = Docs{cu, cu + 1};
+    return hipSuccess;
+  }
+  int32_t* ends = reinterpret_cast<int32_t*>(static_cast<char*>(d->workspace) + ends_off);
+  *out = Docs{cu_padded, ends};
+  return sa::launch_doc_ends(cu, cu_padded, d->num_docs, ends, s);
+}
+
+int fwd_impl(const sink_attn_desc* desc, const void* q, const void* k, const void* v,
+             const int32_t* cu_seqlens, const int32_t* cu_padded, const float* sinks,
+             const float* qnorm_w, const float* knorm_w, int32_t window, int32_t use_rope,
+             void* out, float* lse, void* stream) {
+  int rc = check_prologue(desc, k, v, cu_seqlens, knorm_w, use_rope);
+  if (rc != SINK_ATTN_OK) return rc;
+  rc = check_attention(desc, q, cu_seqlens, sinks, qnorm_w, window, use_rope, out, lse);
+  if (rc != SINK_ATTN_OK) return rc;
+  if (cu_padded != nullptr && !aligned(cu_padded, 4)) return SINK_ATTN_EINVAL;
+  if (desc->total_tokens == 0) return SINK_ATTN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Docs docs;
+  if (doc_bounds(desc, cu_seqlens, cu_padded, plan(desc).ends_off, s, &docs) != hipSuccess)
+    return SINK_ATTN_ELAUNCH;
+  rc = launch_prologue(desc, k, v, docs.starts, docs.ends, knorm_w, use_rope, s);
+  if (rc != SINK_ATTN_OK) return rc;
+  rc = launch_attention(desc, q, docs.starts, docs.ends, sinks, qnorm_w, window, use_rope, out,
+                        lse, s);
+  if (rc != SINK_ATTN_OK || cu_padded == nullptr || desc->dtype != SINK_ATTN_BF16) return rc;
+  // the fp32 kernel writes padding rows itself; the bf16 kernels never visit them
+  return sa::launch_pad_fill(docs.starts, docs.ends, desc->num_docs, desc->total_tokens,
+                             desc->num_q_heads, desc->head_dim, desc->dtype, sinks, out, lse,
+                             s) == hipSuccess
+             ? SINK_ATTN_OK
+             : SINK_ATTN_ELAUNCH;
+}
+
+int bwd_impl(const sink_attn_desc* desc, const void* q, const void* k, const void* v,
+             const int32_t* cu_seqlens, const int32_t* cu_padded, const float* sinks,
+             const float* qnorm_w, const float* knorm_w, int32_t window, int32_t use_rope,
+             const void* out, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+             float* dsinks, float* dqnorm_w, float* dknorm_w, void* stream) {
+  const int rc = check_bwd(desc, q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window,
+                           use_rope, out, lse, dout, dq, dk, dv, dsinks, dqnorm_w, dknorm_w);
+  if (rc != SINK_ATTN_OK) return rc;
+  if (cu_padded != nullptr && !aligned(cu_padded, 4)) return SINK_ATTN_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int Hq = desc->num_q_heads, dh = desc->head_dim;
+  if (desc->total_tokens == 0) {
+    const int n = Hq > dh ? Hq : dh;
+    zero_f32_kernel<<<dim3((n + 255) / 256), dim3(256), 0, s>>>(dsinks, Hq, dqnorm_w, dh,
+                                                                 dknorm_w, dh);
+    return hipGetLastError() == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;
+  }
+  const sa::BwdWorkspace w = plan_bwd(desc);
+  Docs docs;
+  if (doc_bounds(desc, cu_seqlens, cu_padded, w.ends_off, s, &docs) != hipSuccess)
+    return SINK_ATTN_ELAUNCH;
+  using sa::bf16;
+  const hipError_t e = sa::launch_bwd_bf16(
+      static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+      docs.starts, docs.ends, sinks, qnorm_w, knorm_w, static_cast<const bf16*>(out), lse,
+      static_cast<const bf16*>(dout), static_cast<bf16*>(dq), static_cast<bf16*>(dk),
+      static_cast<bf16*>(dv), dsinks, dqnorm_w, dknorm_w, desc->total_tokens, desc->num_docs,
+      Hq, desc->num_kv_heads, window, use_rope, desc->rms_eps, desc->rope_theta,
+      softmax_scale(desc), static_cast<char*>(desc->workspace), w, s);
+  return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;
+}
+
 }  // namespace
 
 extern "C" {
@@ -253,7 +432,7 @@ int sink_attn_prologue(const sink_attn_desc* desc, const void* k, const void* v,
                        void* stream) {
   const int rc = check_prologue(desc, k, v, cu_seqlens, knorm_w, use_rope);
   if (rc != SINK_ATTN_OK || desc->total_tokens == 0) return rc;
-  return launch_prologue(desc, k, v, cu_seqlens, knorm_w, use_rope,
+  return launch_prologue(desc, k, v, cu_seqlens, cu_seqlens + 1, knorm_w, use_rope,
                          static_cast<hipStream_t>(stream));
 }
 
@@ -264,22 +443,26 @@ int sink_attn_attention(const sink_attn_desc* desc, const void* q,
   const int rc = check_attention(desc, q, cu_seqlens, sinks, qnorm_w, window, use_rope, out,
                                  lse);
   if (rc != SINK_ATTN_OK || desc->total_tokens == 0) return rc;
-  return launch_attention(desc, q, cu_seqlens, sinks, qnorm_w, window, use_rope, out,
-                          lse, static_cast<hipStream_t>(stream));
+  return launch_attention(desc, q, cu_seqlens, cu_seqlens + 1, sinks, qnorm_w, window,
+                          use_rope, out, lse, static_cast<hipStream_t>(stream));
 }
 
 int sink_attn_fwd(const sink_attn_desc* desc, const void* q, const void* k, const void* v,
                   const int32_t* cu_seqlens, const float* sinks, const float* qnorm_w,
                   const float* knorm_w, int32_t window, int32_t use_rope, void* out,
                   float* lse, void* stream) {
-  int rc = check_prologue(desc, k, v, cu_seqlens, knorm_w, use_rope);
-  if (rc != SINK_ATTN_OK) return rc;
-  rc = check_attention(desc, q, cu_seqlens, sinks, qnorm_w, window, use_rope, out, lse);
-  if (rc != SINK_ATTN_OK || desc->total_tokens == 0) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = launch_prologue(desc, k, v, cu_seqlens, knorm_w, use_rope, s);
-  if (rc != SINK_ATTN_OK) return rc;
-  return launch_attention(desc, q, cu_seqlens, sinks, qnorm_w, window, use_rope, out, lse, s);
+  return fwd_impl(desc, q, k, v, cu_seqlens, nullptr, sinks, qnorm_w, knorm_w, window,
+                  use_rope, out, lse, stream);
+}
+
+int sink_attn_fwd_padded(const sink_attn_desc* desc, const void* q, const void* k,
+                         const void* v, const int32_t* cu_seqlens,
+                         const int32_t* cu_seqlens_padded, const float* sinks,
+                         const float* qnorm_w, const float* knorm_w, int32_t window,
+                         int32_t use_rope, void* out, float* lse, void* stream) {
+  if (cu_seqlens_padded == nullptr) return SINK_ATTN_EINVAL;
+  return fwd_impl(desc, q, k, v, cu_seqlens, cu_seqlens_padded, sinks, qnorm_w, knorm_w,
+                  window, use_rope, out, lse, stream);
 }
 
 size_t sink_attn_bwd_workspace_bytes(const sink_attn_desc* desc) {
@@ -292,26 +475,35 @@ int sink_attn_bwd(const sink_attn_desc* desc, const void* q, const void* k, cons
                   const float* knorm_w, int32_t window, int32_t use_rope, const void* out,
                   const float* lse, const void* dout, void* dq, void* dk, void* dv,
                   float* dsinks, float* dqnorm_w, float* dknorm_w, void* stream) {
-  const int rc = check_bwd(desc, q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window,
-                           use_rope, out, lse, dout, dq, dk, dv, dsinks, dqnorm_w, dknorm_w);
-  if (rc != SINK_ATTN_OK) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int Hq = desc->num_q_heads, dh = desc->head_dim;
-  if (desc->total_tokens == 0) {
-    const int n = Hq > dh ? Hq : dh;
-    zero_f32_kernel<<<dim3((n + 255) / 256), dim3(256), 0, s>>>(dsinks, Hq, dqnorm_w, dh,
-                                                                 dknorm_w, dh);
-    return hipGetLastError() == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;
-  }
-  using sa::bf16;
-  const hipError_t e = sa::launch_bwd_bf16(
-      static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-      cu_seqlens, sinks, qnorm_w, knorm_w, static_cast<const bf16*>(out), lse,
-      static_cast<const bf16*>(dout), static_cast<bf16*>(dq), static_cast<bf16*>(dk),
-      static_cast<bf16*>(dv), dsinks, dqnorm_w, dknorm_w, desc->total_tokens, desc->num_docs,
-      Hq, desc->num_kv_heads, window, use_rope, desc->rms_eps, desc->rope_theta,
-      softmax_scale(desc), static_cast<char*>(desc->workspace), plan_bwd(desc), s);
-  return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;
+  return bwd_impl(desc, q, k, v, cu_seqlens, nullptr, sinks, qnorm_w, knorm_w, window,
+                  use_rope, out, lse, dout, dq, dk, dv, dsinks, dqnorm_w, dknorm_w, stream);
+}
+
+int sink_attn_bwd_padded(const sink_attn_desc* desc, const void* q, const void* k,
+                         const void* v, const int32_t* cu_seqlens,
+                         const int32_t* cu_seqlens_padded, const float* sinks,
+                         const float* qnorm_w, const float* knorm_w, int32_t window,
+                         int32_t use_rope, const void* out, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* dsinks,
+                         float* dqnorm_w, float* dknorm_w, void* stream) {
+  if (cu_seqlens_padded == nullptr) return SINK_ATTN_EINVAL;
+  return bwd_impl(desc, q, k, v, cu_seqlens, cu_seqlens_padded, sinks, qnorm_w, knorm_w,
+                  window, use_rope, out, lse, dout, dq, dk, dv, dsinks, dqnorm_w, dknorm_w,
+                  stream);
+}
+
+int sink_attn_mask_to_seqlens(const uint8_t* attention_mask, int32_t batch, int32_t seq,
+                              int32_t* cu_seqlens, int32_t* cu_seqlens_padded,
+                              int32_t* bad_rows, void* stream) {
+  if (batch < 0 || seq < 0 || (int64_t)batch * seq > INT32_MAX - 2 * sa::kKeyTile)
+    return SINK_ATTN_EINVAL;
+  if (cu_seqlens == nullptr || cu_seqlens_padded == nullptr || bad_rows == nullptr ||
+      !aligned(cu_seqlens, 4) || !aligned(cu_seqlens_padded, 4) || !aligned(bad_rows, 4))
+    return SINK_ATTN_EINVAL;
+  if ((int64_t)batch * seq > 0 && attention_mask == nullptr) return SINK_ATTN_EINVAL;
+  sa::mask_to_seqlens_kernel<<<dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
+      attention_mask, batch, seq, cu_seqlens, cu_seqlens_padded, bad_rows);
+  return hipGetLastError() == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;
 }
 
 int sink_attn_tile_config(const sink_attn_desc* desc, int32_t window) {
@@ -333,6 +525,6 @@ const char* sink_attn_status_string(int status) {
   }
 }
 
-int sink_attn_version(void) { return 300; }
+int sink_attn_version(void) { return 400; }
 
 }  // extern "C"

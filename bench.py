@@ -18,6 +18,13 @@ attention stage is one launch of the narrow-tile kernel or, with wide tiles,
 the main launch plus the follow-up that reruns the (normally no) blocks whose
 fixed softmax reference proved too low; the events cover both.
 
+--workload sliding_bshd times the padded entry point (sink_attn_fwd_padded):
+a BSHD batch of 8 rows of 4096 slots with trailing padding (real lengths those
+of the sliding workload), the boundaries computed once from the attention mask
+before the timed region (sink_attn_mask_to_seqlens, timed on its own); the
+step's events cover all of its launches (K prologue, attention, padding-row
+fill).  FLOP counts real visible entries only.
+
 --pass bwd times the backward instead: a step is one sink_attn_bwd call (key
 and column tile preparation, the dK/dV and dQ kernels, the final sums) on the
 out and lse of one forward, counted as 2.5 forward passes
@@ -171,6 +178,101 @@ def cpu_baseline_bwd(w, target_seconds: float):
     }
 
 
+def unpadded_view(inp, w, out_gpu, lse_gpu):
+    """The real rows of a padded workload as an unpadded batch (the oracle's
+    own definition of the padded call: its real rows are the unpadded call on
+    the gathered documents), with the matching rows of the GPU results."""
+    import workloads
+    rows = np.concatenate([np.arange(b * w.pad_to, b * w.pad_to + L)
+                           for b, L in enumerate(w.lengths)]).astype(np.int64)
+    sub = workloads.custom_workload(w.lengths, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                    w.dtype, w.window, w.use_rope, w.sink_mean,
+                                    name=w.name + " (real rows)")
+    got = dict(inp, q=inp["q"][rows], k=inp["k"][rows], v=inp["v"][rows])
+    return got, sub, out_gpu[rows], lse_gpu[:, rows]
+
+
+def run_fwd_padded(args, A, w, inp, d_inp, dev):
+    import torch
+
+    cu, cu_padded = A.mask_to_seqlens(d_inp["attention_mask"])
+    if not (torch.equal(cu.cpu(), inp["cu_seqlens"])
+            and torch.equal(cu_padded.cpu(), inp["cu_seqlens_padded"])):
+        raise RuntimeError("mask_to_seqlens disagrees with the workload's boundaries")
+    stream = torch.cuda.current_stream(dev)
+    m_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    mask_ms = []
+    for _ in range(3):
+        m_ev[0].record(stream)
+        A.mask_to_seqlens(d_inp["attention_mask"])   # checks the mask: synchronises
+        m_ev[1].record(stream)
+        torch.cuda.synchronize()
+        mask_ms.append(m_ev[0].elapsed_time(m_ev[1]))
+    call = A.Call(d_inp["q"], d_inp["k"], d_inp["v"], cu, d_inp["sinks"], d_inp["qnorm_w"],
+                  d_inp["knorm_w"], w.window, w.use_rope, rms_eps=w.rms_eps,
+                  rope_theta=w.rope_theta, cu_seqlens_padded=cu_padded)
+    for _ in range(args.warmup):
+        call.fwd()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        call.fwd()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    n_vis = visible_entries(w.lengths, w.window)
+    flop = 4.0 * w.head_dim * w.num_q_heads * n_vis
+    value = flop / (ms_step * 1e-3) / 1e12
+    achieved = flop / (call_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.description}",
+            "tokens": w.total_tokens, "rows": w.num_rows, "docs": w.num_docs,
+            "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "window": w.window, "rope": w.use_rope, "visible_entries": n_vis,
+            "flop_per_step": flop, "parallelism": "single GPU",
+        },
+        "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "sink_attn_fwd_padded (all launches)",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "avg_launch_ms": call_ms,
+        },
+        "kernels": {"mask_to_seqlens_ms": float(np.median(mask_ms))},
+    }
+    if args.cpu_seconds > 0:
+        call.fwd()
+        torch.cuda.synchronize()
+        got, sub, out_r, lse_r = unpadded_view(inp, w, call.out, call.lse)
+        base = cpu_baseline(got, sub, out_r, lse_r, args.cpu_seconds)
+        base["sample"] += " (the real rows of the padded batch)"
+        result["cpu_baseline"] = base
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def run_bwd(args, A, w, d_inp, call, dev):
     import torch
     import workloads
@@ -180,7 +282,8 @@ def run_bwd(args, A, w, d_inp, call, dev):
     torch.cuda.synchronize()
     bc = A.BwdCall(d_inp["q"], d_inp["k"], d_inp["v"], d_inp["cu_seqlens"], d_inp["sinks"],
                    d_inp["qnorm_w"], d_inp["knorm_w"], w.window, w.use_rope, call.out, call.lse,
-                   dout, rms_eps=w.rms_eps, rope_theta=w.rope_theta)
+                   dout, rms_eps=w.rms_eps, rope_theta=w.rope_theta,
+                   cu_seqlens_padded=d_inp.get("cu_seqlens_padded"))
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
         bc.run()
@@ -214,15 +317,15 @@ def run_bwd(args, A, w, d_inp, call, dev):
         "data": "synthetic",
         "config": {
             "workload": f"{w.name} backward: {w.description}",
-            "tokens": w.total_tokens, "docs": w.num_docs, "q_heads": w.num_q_heads,
-            "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "window": w.window,
-            "rope": w.use_rope, "visible_entries": n_vis, "flop_per_step": flop,
-            "parallelism": "single GPU",
+            "tokens": w.total_tokens, "rows": w.num_rows, "docs": w.num_docs,
+            "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "window": w.window, "rope": w.use_rope, "visible_entries": n_vis,
+            "flop_per_step": flop, "parallelism": "single GPU",
         },
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
         "roofline": {
             "bound": "mfma",
-            "kernel": "sink_attn_bwd (all five launches)",
+            "kernel": "sink_attn_bwd%s (all launches)" % ("_padded" if w.pad_to else ""),
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
@@ -243,7 +346,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="full",
-                    choices=["full", "sliding", "long", "mixed_sliding", "mixed_causal"])
+                    choices=["full", "sliding", "long", "mixed_sliding", "mixed_causal",
+                             "sliding_bshd"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target host time of the oracle sample (0 skips the CPU baseline)")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
@@ -287,9 +391,13 @@ def main():
     torch.cuda.synchronize()
     call = A.Call(d_inp["q"], d_inp["k"], d_inp["v"], d_inp["cu_seqlens"], d_inp["sinks"],
                   d_inp["qnorm_w"], d_inp["knorm_w"], w.window, w.use_rope,
-                  rms_eps=w.rms_eps, rope_theta=w.rope_theta)
+                  rms_eps=w.rms_eps, rope_theta=w.rope_theta,
+                  cu_seqlens_padded=d_inp.get("cu_seqlens_padded"))
     if args.which == "bwd":
         run_bwd(args, A, w, d_inp, call, dev)
+        return
+    if w.pad_to:
+        run_fwd_padded(args, A, w, inp, d_inp, dev)
         return
     stream = torch.cuda.current_stream(dev)
     tile = A.tile_config(call.desc, w.window)

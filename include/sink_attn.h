@@ -20,6 +20,12 @@
  *                      (_FlintSinkParameters) and q_norm / k_norm are RMSNorm
  *                      modules with weights, so a training step needs the
  *                      gradients of q, k, v, the sinks and both weights.
+ *   "flint.layers"     (padding) FlintAttention.forward attention_mask:
+ *                      padded queries and keys are excluded from the real
+ *                      attention while the sink stays valid; BSHD supports
+ *                      trailing padding, other padding uses THD packing.
+ *   "attention.utils"  (padding) packed inputs may carry cu_seqlens_padded
+ *                      beside cu_seqlens, both int32 [documents + 1].
  *   "attention.utils"  preprocess_args_and_kwargs_for_attn: THD tensors
  *                      [tokens, heads, head_dim], K and V share a layout,
  *                      int32 cu_seqlens [documents + 1], a positive left
@@ -156,6 +162,38 @@ int sink_attn_attention(const sink_attn_desc* desc, const void* q,
  * 2048 keys.  Reads no device memory. */
 int sink_attn_tile_config(const sink_attn_desc* desc, int32_t window);
 
+/* Padded THD.  cu_seqlens holds the real document lengths (as prefix sums)
+ * and cu_seqlens_padded, also int32 [D+1], where each document starts in the
+ * packed tensors: document n's real tokens are
+ *   [cu_seqlens_padded[n], cu_seqlens_padded[n] + cu_seqlens[n+1] - cu_seqlens[n])
+ * and the rest of [cu_seqlens_padded[n], cu_seqlens_padded[n+1]) is padding;
+ * desc->total_tokens = cu_seqlens_padded[D] counts the padding.  Positions
+ * run from 0 at each document's first token.  Padding tokens are excluded as
+ * keys and as queries: a padding query's softmax holds the sink alone, so its
+ * out row is 0 and its lse is sinks[h].  Whatever the inputs hold at padding
+ * rows (even NaN) does not reach the real rows.  The boundaries are not
+ * checked on the device: cu_seqlens_padded must start at 0, be
+ * non-decreasing, end at T, and leave every document room for its real
+ * tokens.  Otherwise as sink_attn_fwd (same workspace size). */
+int sink_attn_fwd_padded(const sink_attn_desc* desc, const void* q, const void* k,
+                         const void* v, const int32_t* cu_seqlens,
+                         const int32_t* cu_seqlens_padded, const float* sinks,
+                         const float* qnorm_w, const float* knorm_w, int32_t window,
+                         int32_t use_rope, void* out, float* lse, void* stream);
+
+/* Padded-THD boundaries of a BSHD attention mask: attention_mask is a device
+ * uint8 [batch][seq] (nonzero = real token) whose rows must be a run of real
+ * tokens followed by padding (trailing padding, as Transformer Engine's BSHD
+ * takes; other padding has to be packed as THD).  Writes cu_seqlens and
+ * cu_seqlens_padded (int32 [batch+1] each; row b starts at b * seq) so that
+ * [batch, seq, heads, d] tensors, viewed as [batch * seq, heads, d], run
+ * through the padded-THD entry points; writes into *bad_rows (device int32)
+ * the number of rows whose padding does not trail (those boundaries are then
+ * meaningless; check it before use).  Every pointer is a device pointer. */
+int sink_attn_mask_to_seqlens(const uint8_t* attention_mask, int32_t batch, int32_t seq,
+                              int32_t* cu_seqlens, int32_t* cu_seqlens_padded,
+                              int32_t* bad_rows, void* stream);
+
 /* Bytes of device workspace sink_attn_bwd needs for this descriptor (0 when
  * T == 0, for the fp32 path, or for an invalid descriptor).  The forward's
  * workspace can be reused once the forward has completed; the backward does
@@ -184,6 +222,17 @@ int sink_attn_bwd(const sink_attn_desc* desc, const void* q, const void* k,
                   int32_t use_rope, const void* out, const float* lse,
                   const void* dout, void* dq, void* dk, void* dv, float* dsinks,
                   float* dqnorm_w, float* dknorm_w, void* stream);
+
+/* Backward of sink_attn_fwd_padded: as sink_attn_bwd, with padded-THD
+ * boundaries.  Padding rows of dq, dk and dv are written as zeros; padding
+ * rows contribute nothing to dsinks and the norm-weight gradients. */
+int sink_attn_bwd_padded(const sink_attn_desc* desc, const void* q, const void* k,
+                         const void* v, const int32_t* cu_seqlens,
+                         const int32_t* cu_seqlens_padded, const float* sinks,
+                         const float* qnorm_w, const float* knorm_w, int32_t window,
+                         int32_t use_rope, const void* out, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* dsinks,
+                         float* dqnorm_w, float* dknorm_w, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* sink_attn_status_string(int status);

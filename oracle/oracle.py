@@ -180,3 +180,69 @@ def sink_attn_bwd(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope
     if rc:
         raise OracleError(f"oracle_sink_attn_bwd rejected its arguments ({rc})")
     return res
+
+
+# ---- padded THD --------------------------------------------------------------
+# Padded THD (attention.utils: cu_seqlens with cu_seqlens_padded): document n's
+# real tokens are [cu_padded[n], cu_padded[n] + cu[n+1] - cu[n]) of the packed
+# tensors, the rest of [cu_padded[n], cu_padded[n+1]) is padding.  flint.layers
+# FlintAttention.forward (attention_mask): padded queries and keys are excluded
+# from the real attention and the sink stays valid.  The oracle takes that
+# literally: the real tokens, gathered into an unpadded batch, go through the
+# definitions above unchanged; a padding query's softmax holds the sink alone
+# (out = 0, lse = sink), and no gradient reaches a padding row.
+
+def padded_real_rows(cu_seqlens, cu_seqlens_padded) -> np.ndarray:
+    """Indices of the real tokens of a padded-THD batch, in order."""
+    cu = _i32(cu_seqlens)
+    cp = _i32(cu_seqlens_padded)
+    if cu.shape != cp.shape:
+        raise OracleError("cu_seqlens and cu_seqlens_padded must have the same shape")
+    parts = [np.arange(cp[n], cp[n] + (cu[n + 1] - cu[n])) for n in range(len(cu) - 1)]
+    rows = np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+    for n in range(len(cu) - 1):
+        if cu[n + 1] - cu[n] > cp[n + 1] - cp[n]:
+            raise OracleError("a document's real tokens do not fit its padded slot")
+    return rows.astype(np.int64)
+
+
+def sink_attn_fwd_padded(q, k, v, cu_seqlens, cu_seqlens_padded, sinks, qnorm_w, knorm_w,
+                         window, use_rope, eps=1e-6, theta=1e6, scale=None, rows=None):
+    """Forward over a padded-THD batch: (out [T, Hq, d], lse [Hq, T]), or,
+    when rows (padded-batch indices) is given, (out [n, Hq, d], lse [Hq, n])
+    of those rows only.  q, k, v always hold all T rows."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, Hq, d = q.shape
+    real = padded_real_rows(cu_seqlens, cu_seqlens_padded)
+    want = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    packed = np.full(T, -1, dtype=np.int64)      # padded row -> index among the real rows
+    packed[real] = np.arange(len(real))
+    out = np.zeros((len(want), Hq, d))
+    lse = np.repeat(_f64(sinks)[:, None], len(want), axis=1)
+    hit = np.nonzero(packed[want] >= 0)[0]
+    if len(hit):
+        o, l = sink_attn_fwd(q[want[hit]], k[real], v[real], _i32(cu_seqlens), sinks, qnorm_w,
+                             knorm_w, window, use_rope, eps=eps, theta=theta, scale=scale,
+                             rows=None if rows is None else packed[want[hit]])
+        out[hit] = o
+        lse[:, hit] = l
+    return out, lse
+
+
+def sink_attn_bwd_padded(q, k, v, cu_seqlens, cu_seqlens_padded, sinks, qnorm_w, knorm_w,
+                         window, use_rope, dout, eps=1e-6, theta=1e6, scale=None):
+    """Gradients of sum(dout * out) for the padded-THD forward; padding rows
+    of dq, dk, dv are zero (a padding row's out is the constant 0)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    rows = padded_real_rows(cu_seqlens, cu_seqlens_padded)
+    res = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v),
+           "dsinks": np.zeros(q.shape[1]), "dqnorm_w": np.zeros(q.shape[2]),
+           "dknorm_w": np.zeros(q.shape[2])}
+    if len(rows):
+        g = sink_attn_bwd(q[rows], k[rows], v[rows], _i32(cu_seqlens), sinks, qnorm_w, knorm_w,
+                          window, use_rope, dout[rows], eps=eps, theta=theta, scale=scale)
+        for key in ("dq", "dk", "dv"):
+            res[key][rows] = g[key]
+        for key in ("dsinks", "dqnorm_w", "dknorm_w"):
+            res[key] = g[key]
+    return res

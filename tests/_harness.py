@@ -72,7 +72,9 @@ def check_parity(inp: dict, window: int, use_rope: bool, rows=None, label="", **
     dev = to_device(inp)
     out, lse = gpu_forward(dev, window, use_rope, **kw)
     ref_out, ref_lse = oracle_forward(inp, window, use_rope, rows=rows,
-                                      scale=kw.get("softmax_scale"))
+                                      scale=kw.get("softmax_scale"),
+                                      eps=kw.get("rms_eps", 1e-6),
+                                      theta=kw.get("rope_theta", 1e6))
     out_np = out.float().cpu().numpy().astype(np.float64)
     lse_np = lse.cpu().numpy().astype(np.float64)
     if rows is not None:

@@ -27,7 +27,8 @@ def test_every_declared_symbol_is_exported(A):
     assert set(names) >= {"sink_attn_fwd", "sink_attn_workspace_bytes",
                           "sink_attn_status_string", "sink_attn_prologue",
                           "sink_attn_attention", "sink_attn_version", "sink_attn_tile_config",
-                          "sink_attn_bwd", "sink_attn_bwd_workspace_bytes"}
+                          "sink_attn_bwd", "sink_attn_bwd_workspace_bytes", "sink_attn_fwd_padded",
+                          "sink_attn_bwd_padded", "sink_attn_mask_to_seqlens"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -274,3 +275,41 @@ def test_bwd_invalid_arguments_rejected(A, case, expected):
     elif case == "misaligned_workspace":
         desc.workspace = 0x10000000 + 64
     assert _bwd(A, desc, **kw) == expected
+
+
+def _padded_fwd(A, desc, cu_padded=FAKE, window=-1, **ptrs):
+    names = ["q", "k", "v", "cu", "sinks", "qw", "kw", "out", "lse"]
+    p = {n: FAKE for n in names}
+    p.update(ptrs)
+    P = ctypes.c_void_p
+    return A.load_library().sink_attn_fwd_padded(
+        ctypes.byref(desc), P(p["q"]), P(p["k"]), P(p["v"]), P(p["cu"]), P(cu_padded),
+        P(p["sinks"]), P(p["qw"]), P(p["kw"]), window, 0, P(p["out"]), P(p["lse"]), None)
+
+
+def test_padded_entry_points_validate(A):
+    desc = _desc(A)
+    assert _padded_fwd(A, desc, cu_padded=0) == EINVAL          # padded boundaries required
+    assert _padded_fwd(A, desc, cu_padded=FAKE + 2) == EINVAL   # misaligned
+    assert _padded_fwd(A, desc, window=0) == EINVAL
+    small = _desc(A, ws_bytes=1024)
+    assert _padded_fwd(A, small) == EWORKSPACE
+    lib = A.load_library()
+    P = ctypes.c_void_p
+    bdesc = _bwd_desc(A)
+    args = [P(FAKE)] * 4 + [P(0)] + [P(FAKE)] * 3
+    tail = [-1, 0] + [P(FAKE)] * 9 + [None]
+    assert lib.sink_attn_bwd_padded(ctypes.byref(bdesc), *args, *tail) == EINVAL
+    # the workspace query covers the document-end table the padded calls keep
+    assert A.sink_attn_workspace_bytes(1000, 3, 32, 4, 128) < \
+        A.sink_attn_workspace_bytes(1000, 300, 32, 4, 128)
+
+
+def test_mask_to_seqlens_validates(A):
+    lib = A.load_library()
+    P = ctypes.c_void_p
+    assert lib.sink_attn_mask_to_seqlens(P(FAKE), -1, 4, P(FAKE), P(FAKE), P(FAKE), None) == EINVAL
+    assert lib.sink_attn_mask_to_seqlens(P(0), 2, 4, P(FAKE), P(FAKE), P(FAKE), None) == EINVAL
+    assert lib.sink_attn_mask_to_seqlens(P(FAKE), 2, 4, P(0), P(FAKE), P(FAKE), None) == EINVAL
+    assert lib.sink_attn_mask_to_seqlens(P(FAKE), 1 << 16, 1 << 16, P(FAKE), P(FAKE), P(FAKE),
+                                         None) == EINVAL

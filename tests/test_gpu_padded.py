@@ -1,0 +1,304 @@
+"""GPU parity of the padded layouts against the padded-THD oracle.
+
+* padded THD (cu_seqlens with cu_seqlens_padded) through sink_attn_fwd_padded
+  with every tile configuration and the fp32 path, and through
+  sink_attn_bwd_padded; NaN stored at padding rows must not reach real rows;
+  padding rows come back exactly as the pages' reading fixes them (out = 0,
+  lse = sink, zero gradients);
+* BSHD with a trailing-padding attention mask (sink_attn_fwd_bshd /
+  sink_attn_bwd_bshd); a mask with padding before real tokens is rejected;
+* RMSNorm eps = 0 with a ragged token count (keys past T once came out NaN).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from _harness import (BF16_MAX, BF16_MEAN, BWD_REL_MAX, BWD_REL_MEAN, F32_MAX, GRAD_KEYS,
+                      check_parity, custom_inputs, errors, require_gpu, to_device)
+
+pytestmark = pytest.mark.gpu
+
+LENGTHS = [70, 1, 0, 200, 33, 129]
+SLOTS = [128, 64, 64, 256, 40, 192]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    return require_gpu()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _padded_inputs(lengths, slots, Hq=32, Hkv=4, d=128, dtype="bf16", seed=0, junk=True):
+    inp = custom_inputs(slots, Hq=Hq, Hkv=Hkv, d=d, dtype=dtype, seed=seed)
+    cu, cp = workloads.padded_boundaries(lengths, slots)
+    import oracle.oracle as O
+    rows = O.padded_real_rows(cu, cp)
+    pad = np.setdiff1d(np.arange(sum(slots)), rows)
+    if junk and len(pad):
+        for key in ("q", "k", "v"):
+            inp[key][torch.from_numpy(pad)] = float("nan")
+    inp["cu_seqlens"] = torch.from_numpy(cu)
+    inp["cu_seqlens_padded"] = torch.from_numpy(cp)
+    return inp, rows, pad
+
+
+def _oracle_fwd(inp, window, use_rope, rows):
+    import oracle.oracle as O
+    f = lambda t: t.double().numpy()  # noqa: E731
+    q, k, v = f(inp["q"]), f(inp["k"]), f(inp["v"])
+    pad = np.setdiff1d(np.arange(q.shape[0]), rows)
+    for a in (q, k, v):
+        a[pad] = 0.0  # the oracle must not see them either way
+    return O.sink_attn_fwd_padded(q, k, v, inp["cu_seqlens"].numpy(),
+                                  inp["cu_seqlens_padded"].numpy(), f(inp["sinks"]),
+                                  f(inp["qnorm_w"]), f(inp["knorm_w"]), window, use_rope)
+
+
+def _check_fwd(inp, rows, pad, out, lse, window, use_rope, label):
+    ref_out, ref_lse = _oracle_fwd(inp, window, use_rope, rows)
+    o = out.float().cpu().numpy().astype(np.float64)
+    l = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o[rows])) and np.all(np.isfinite(l[:, rows])), label
+    eo = errors(o[rows], ref_out[rows])
+    el = errors(l[:, rows], ref_lse[:, rows])
+    _say(f"  {label}: out max/mean {eo[0]:.3e}/{eo[1]:.3e} lse max {el[0]:.3e}")
+    if inp["q"].dtype == torch.float32:
+        assert eo[0] <= F32_MAX and el[0] <= F32_MAX, (label, eo, el)
+    else:
+        assert eo[0] <= BF16_MAX and eo[1] <= BF16_MEAN and el[0] <= BF16_MAX, (label, eo, el)
+    assert np.all(o[pad] == 0.0), label
+    assert np.array_equal(l[:, pad], np.repeat(inp["sinks"].numpy()[:, None], len(pad), 1)
+                          .astype(np.float64)), label
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+@pytest.mark.parametrize("window,use_rope", [(-1, False), (50, True)])
+def test_padded_thd_forward(tile, window, use_rope):
+    import attention_qk_rmsnorm_amd as A
+    _say(f"case padded fwd tile={tile} W={window}")
+    inp, rows, pad = _padded_inputs(LENGTHS, SLOTS)
+    dev = to_device(inp)
+    out, lse = A.sink_attn_fwd(dev["q"], dev["k"], dev["v"], dev["cu_seqlens"], dev["sinks"],
+                               dev["qnorm_w"], dev["knorm_w"], window, use_rope,
+                               cu_seqlens_padded=dev["cu_seqlens_padded"], tile_config=tile)
+    torch.cuda.synchronize()
+    _check_fwd(inp, rows, pad, out, lse, window, use_rope, f"tile {tile}")
+
+
+def test_padded_thd_forward_fp32():
+    import attention_qk_rmsnorm_amd as A
+    _say("case padded fwd fp32")
+    inp, rows, pad = _padded_inputs([40, 0, 77, 5], [64, 16, 96, 8], Hq=4, Hkv=1, d=64,
+                                    dtype="f32")
+    dev = to_device(inp)
+    out, lse = A.sink_attn_fwd(dev["q"], dev["k"], dev["v"], dev["cu_seqlens"], dev["sinks"],
+                               dev["qnorm_w"], dev["knorm_w"], 20, True,
+                               cu_seqlens_padded=dev["cu_seqlens_padded"])
+    torch.cuda.synchronize()
+    _check_fwd(inp, rows, pad, out, lse, 20, True, "fp32")
+
+
+def test_eps_zero_with_ragged_token_count():
+    # T = 317 leaves padding keys in the last 64-key tile; with eps = 0 their
+    # norm must not turn into 0 * inf
+    _say("case eps=0 ragged T")
+    inp = custom_inputs([200, 117])
+    check_parity(inp, -1, False, label="eps 0 narrow", rms_eps=0.0, tile_config=1)
+    check_parity(inp, 64, True, label="eps 0 wide", rms_eps=0.0, tile_config=2)
+
+
+def _check_grads(g, ref, rows, pad, label):
+    msg, bad = [], []
+    for key in GRAD_KEYS:
+        got = g[key].float().cpu().numpy().astype(np.float64)
+        r = ref[key]
+        if key in ("dq", "dk", "dv"):
+            assert np.all(got[pad] == 0.0), (label, key)
+            got, r = got[rows], r[rows]
+        assert np.all(np.isfinite(got)), (label, key)
+        emax, emean = errors(got, r)
+        smax, smean = float(np.abs(r).max()), float(np.abs(r).mean())
+        msg.append(f"{key} {emax / smax:.2e}/{emean / smean:.2e}")
+        if emax > BWD_REL_MAX * smax or emean > BWD_REL_MEAN * smean:
+            bad.append(key)
+    _say(f"  {label}: rel max/mean " + ", ".join(msg))
+    assert not bad, (label, bad)
+
+
+def _oracle_bwd(inp, window, use_rope, rows, dout):
+    import oracle.oracle as O
+    f = lambda t: t.double().numpy()  # noqa: E731
+    q, k, v, do = f(inp["q"]), f(inp["k"]), f(inp["v"]), f(dout)
+    pad = np.setdiff1d(np.arange(q.shape[0]), rows)
+    for a in (q, k, v, do):
+        a[pad] = 0.0
+    return O.sink_attn_bwd_padded(q, k, v, inp["cu_seqlens"].numpy(),
+                                  inp["cu_seqlens_padded"].numpy(), f(inp["sinks"]),
+                                  f(inp["qnorm_w"]), f(inp["knorm_w"]), window, use_rope, do)
+
+
+@pytest.mark.parametrize("window,use_rope", [(-1, False), (50, True)])
+def test_padded_thd_backward(window, use_rope):
+    import attention_qk_rmsnorm_amd as A
+    _say(f"case padded bwd W={window}")
+    inp, rows, pad = _padded_inputs(LENGTHS, SLOTS)
+    T = sum(SLOTS)
+    dout = workloads.make_grad_output(workloads.Workload("g", (T,)), 0)
+    dout[torch.from_numpy(pad)] = float("nan")
+    dev = to_device(inp)
+    out, lse = A.sink_attn_fwd(dev["q"], dev["k"], dev["v"], dev["cu_seqlens"], dev["sinks"],
+                               dev["qnorm_w"], dev["knorm_w"], window, use_rope,
+                               cu_seqlens_padded=dev["cu_seqlens_padded"])
+    g = A.sink_attn_bwd(dev["q"], dev["k"], dev["v"], dev["cu_seqlens"], dev["sinks"],
+                        dev["qnorm_w"], dev["knorm_w"], window, use_rope, out, lse,
+                        dout.to("cuda:0"), cu_seqlens_padded=dev["cu_seqlens_padded"])
+    torch.cuda.synchronize()
+    _check_grads(g, _oracle_bwd(inp, window, use_rope, rows, dout), rows, pad,
+                 f"padded W={window}")
+
+
+def test_bshd_mask_forward_backward_and_rejection():
+    import attention_qk_rmsnorm_amd as A
+    _say("case bshd mask")
+    B, S, lengths = 3, 300, [300, 17, 150]
+    inp = custom_inputs([S] * B, seed=2)
+    mask = torch.arange(S)[None, :] < torch.tensor(lengths)[:, None]
+    dev = to_device(inp)
+    q = dev["q"].view(B, S, 32, 128)
+    k = dev["k"].view(B, S, 4, 128)
+    v = dev["v"].view(B, S, 4, 128)
+    out, lse = A.sink_attn_fwd_bshd(q, k, v, mask.to("cuda:0"), dev["sinks"], dev["qnorm_w"],
+                                    dev["knorm_w"], 100, True)
+    torch.cuda.synchronize()
+    assert out.shape == (B, S, 32, 128) and lse.shape == (32, B, S)
+    cu, cp = workloads.padded_boundaries(lengths, [S] * B)
+    pinp = dict(inp, cu_seqlens=torch.from_numpy(cu), cu_seqlens_padded=torch.from_numpy(cp))
+    import oracle.oracle as O
+    rows = O.padded_real_rows(cu, cp)
+    pad = np.setdiff1d(np.arange(B * S), rows)
+    _check_fwd(pinp, rows, pad, out.view(B * S, 32, 128), lse.reshape(32, B * S), 100, True,
+               "bshd fwd")
+    dout = workloads.make_grad_output(workloads.Workload("g", (B * S,)), 1)
+    g = A.sink_attn_bwd_bshd(q, k, v, mask.to("cuda:0"), dev["sinks"], dev["qnorm_w"],
+                             dev["knorm_w"], 100, True, out, lse,
+                             dout.to("cuda:0").view(B, S, 32, 128))
+    torch.cuda.synchronize()
+    flat = {key: (val.reshape(B * S, *val.shape[2:]) if val.dim() == 4 else val)
+            for key, val in g.items()}
+    _check_grads(flat, _oracle_bwd(pinp, 100, True, rows, dout), rows, pad, "bshd bwd")
+    holes = mask.clone()
+    holes[1, 3] = False  # padding before real tokens
+    with pytest.raises(ValueError):
+        A.sink_attn_fwd_bshd(q, k, v, holes.to("cuda:0"), dev["sinks"], dev["qnorm_w"],
+                             dev["knorm_w"], 100, True)
+
+
+# ------------------------------------------------- full-size padded batch ---
+# The BSHD batch of 8 rows x 4096 slots with the sliding layers' real lengths
+# (W = 1024, RoPE), in the launch configuration the benchmark times: the
+# boundaries from the attention mask, then the padded entry points.
+
+def _full_bshd():
+    import attention_qk_rmsnorm_amd as A
+    w = workloads.named_workloads()["sliding_bshd"]
+    inp = workloads.make_inputs(w)
+    dev = to_device(inp)
+    cu, cp = A.mask_to_seqlens(dev["attention_mask"])
+    assert torch.equal(cu.cpu(), inp["cu_seqlens"]) and torch.equal(cp.cpu(),
+                                                                     inp["cu_seqlens_padded"])
+    return A, w, inp, dev, cu, cp
+
+
+def _doc_rows(w, docs):
+    return np.concatenate([np.arange(b * w.pad_to, b * w.pad_to + w.lengths[b]) for b in docs])
+
+
+def test_full_size_bshd_forward_sampled_rows():
+    A, w, inp, dev, cu, cp = _full_bshd()
+    _say(f"case sliding_bshd fwd rows={w.num_rows} real={w.total_tokens}")
+    c = A.Call(dev["q"], dev["k"], dev["v"], cu, dev["sinks"], dev["qnorm_w"], dev["knorm_w"],
+               w.window, w.use_rope, cu_seqlens_padded=cp)
+    c.fwd()
+    torch.cuda.synchronize()
+    import oracle.oracle as O
+    real = O.padded_real_rows(inp["cu_seqlens"].numpy(), inp["cu_seqlens_padded"].numpy())
+    pick = real[workloads.sample_rows(w.lengths, w.window, 192)]
+    pad = np.setdiff1d(np.arange(w.num_rows), real)
+    pick = np.concatenate([pick, pad[:: max(1, len(pad) // 64)]])
+    f = lambda t: t.double().numpy()  # noqa: E731
+    ref_out, ref_lse = O.sink_attn_fwd_padded(
+        f(inp["q"]), f(inp["k"]), f(inp["v"]), inp["cu_seqlens"].numpy(),
+        inp["cu_seqlens_padded"].numpy(), f(inp["sinks"]), f(inp["qnorm_w"]),
+        f(inp["knorm_w"]), w.window, w.use_rope, rows=pick)
+    o = c.out[torch.from_numpy(pick).cuda()].float().cpu().numpy().astype(np.float64)
+    l = c.lse[:, torch.from_numpy(pick).cuda()].cpu().numpy().astype(np.float64)
+    eo, el = errors(o, ref_out), errors(l, ref_lse)
+    _say(f"  sliding_bshd: rows={len(pick)} out max/mean {eo[0]:.3e}/{eo[1]:.3e} "
+         f"lse max {el[0]:.3e}")
+    assert eo[0] <= BF16_MAX and eo[1] <= BF16_MEAN and el[0] <= BF16_MAX, (eo, el)
+    # every padding row, on the device: out = 0, lse = the sink
+    padt = torch.from_numpy(pad).cuda()
+    assert torch.all(c.out[padt] == 0)
+    assert torch.equal(c.lse[:, padt], dev["sinks"][:, None].expand(-1, len(pad)))
+
+
+def test_full_size_bshd_backward():
+    # dq, dk, dv of four whole documents against the oracle (a document's
+    # gradients depend on that document alone); the batch-wide sums (dsinks,
+    # norm-weight gradients) against the unpadded backward of the same real
+    # tokens; every padding row's gradient is zero.
+    A, w, inp, dev, cu, cp = _full_bshd()
+    _say(f"case sliding_bshd bwd rows={w.num_rows} real={w.total_tokens}")
+    dout = workloads.make_grad_output(w)
+    d_dout = dout.to("cuda:0")
+    c = A.Call(dev["q"], dev["k"], dev["v"], cu, dev["sinks"], dev["qnorm_w"], dev["knorm_w"],
+               w.window, w.use_rope, cu_seqlens_padded=cp)
+    c.fwd()
+    g = A.BwdCall(dev["q"], dev["k"], dev["v"], cu, dev["sinks"], dev["qnorm_w"],
+                  dev["knorm_w"], w.window, w.use_rope, c.out, c.lse, d_dout,
+                  cu_seqlens_padded=cp)
+    g.run()
+    torch.cuda.synchronize()
+    grads = g.grads
+    import oracle.oracle as O
+    real = O.padded_real_rows(inp["cu_seqlens"].numpy(), inp["cu_seqlens_padded"].numpy())
+    pad = torch.from_numpy(np.setdiff1d(np.arange(w.num_rows), real)).cuda()
+    for key in ("dq", "dk", "dv"):
+        assert torch.all(grads[key][pad] == 0), key
+        assert torch.all(torch.isfinite(grads[key].float())), key
+    docs = [3, 5, 6, 7]
+    rows = _doc_rows(w, docs)
+    f = lambda t: t.double().numpy()  # noqa: E731
+    sub_cu = workloads.cu_seqlens([w.lengths[b] for b in docs])
+    ref = O.sink_attn_bwd(f(inp["q"][rows]), f(inp["k"][rows]), f(inp["v"][rows]), sub_cu,
+                          f(inp["sinks"]), f(inp["qnorm_w"]), f(inp["knorm_w"]), w.window,
+                          w.use_rope, f(dout[rows]))
+    msg = []
+    rt = torch.from_numpy(rows).cuda()
+    for key in ("dq", "dk", "dv"):
+        got = grads[key][rt].float().cpu().numpy().astype(np.float64)
+        emax, emean = errors(got, ref[key])
+        smax, smean = float(np.abs(ref[key]).max()), float(np.abs(ref[key]).mean())
+        msg.append(f"{key} {emax / smax:.2e}/{emean / smean:.2e}")
+        assert emax <= BWD_REL_MAX * smax and emean <= BWD_REL_MEAN * smean, (key, emax, emean)
+    # the unpadded backward of the real tokens gives the batch-wide sums
+    rr = torch.from_numpy(real).cuda()
+    q, k, v = (dev[n][rr].contiguous() for n in ("q", "k", "v"))
+    u = A.Call(q, k, v, cu, dev["sinks"], dev["qnorm_w"], dev["knorm_w"], w.window,
+               w.use_rope)
+    u.fwd()
+    ug = A.BwdCall(q, k, v, cu, dev["sinks"], dev["qnorm_w"], dev["knorm_w"], w.window,
+                   w.use_rope, u.out, u.lse, d_dout[rr].contiguous())
+    ug.run()
+    torch.cuda.synchronize()
+    for key in ("dsinks", "dqnorm_w", "dknorm_w"):
+        a = grads[key].double().cpu().numpy()
+        b = ug.grads[key].double().cpu().numpy()
+        rel = float(np.abs(a - b).max() / np.abs(b).max())
+        msg.append(f"{key} vs unpadded {rel:.2e}")
+        assert rel <= BWD_REL_MAX, (key, rel)
+    _say("  sliding_bshd bwd: rel max/mean " + ", ".join(msg))

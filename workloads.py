@@ -13,7 +13,10 @@ Recipe (the same for every configuration):
     1 + N(0, 0.02) fp32 with one weight vector of head_dim entries per
     projection;
   * for the backward, the output gradient dout ~ N(0, 1) [T, Hq, d] from a
-    second generator seeded with seed + 1, rounded to the storage dtype.
+    second generator seeded with seed + 1, rounded to the storage dtype;
+  * padded batches (pad_to > 0): every document sits at the start of a slot
+    of pad_to rows (a BSHD batch [D, pad_to] viewed as THD) and the padding
+    rows hold draws from the same generator like any other row.
 """
 from __future__ import annotations
 
@@ -36,11 +39,18 @@ class Workload:
     sink_mean: float = 0.0
     rope_theta: float = 1e6
     rms_eps: float = 1e-6
+    pad_to: int = 0              # > 0: every document padded to a slot of pad_to rows
     description: str = field(default="", compare=False)
 
     @property
     def total_tokens(self) -> int:
+        """Real tokens (padding excluded)."""
         return int(sum(self.lengths))
+
+    @property
+    def num_rows(self) -> int:
+        """Rows of the q/k/v tensors: real tokens, or D * pad_to when padded."""
+        return self.num_docs * self.pad_to if self.pad_to else self.total_tokens
 
     @property
     def num_docs(self) -> int:
@@ -75,6 +85,10 @@ def named_workloads(seed: int = 0) -> dict:
                                   description="512 docs geometric mean 200 clip [1,2048], W=512 + RoPE"),
         "mixed_causal": Workload("mixed_causal", mixed, window=-1, use_rope=False,
                                  description="512 docs geometric mean 200 clip [1,2048], causal, no RoPE"),
+        "sliding_bshd": Workload("sliding_bshd", _sliding_lengths(seed), window=1024,
+                                 use_rope=True, pad_to=4096,
+                                 description="BSHD batch 8 x 4096 with trailing padding, real "
+                                             "lengths U[256,4096], W=1024, NeoX RoPE"),
     }
 
 
@@ -89,10 +103,12 @@ def cu_seqlens(lengths) -> np.ndarray:
 
 def make_inputs(w: Workload, seed: int = 0) -> dict:
     """CPU tensors for workload ``w``: q [T,Hq,d], k/v [T,Hkv,d] in w.dtype,
-    cu_seqlens int32 [D+1], sinks fp32 [Hq], qnorm_w / knorm_w fp32 [d]."""
+    cu_seqlens int32 [D+1], sinks fp32 [Hq], qnorm_w / knorm_w fp32 [d]; T is
+    w.num_rows.  Padded workloads add cu_seqlens_padded int32 [D+1] (slot
+    starts) and attention_mask bool [D, pad_to]."""
     gen = torch.Generator(device="cpu")
     gen.manual_seed(seed)
-    T, Hq, Hkv, d = w.total_tokens, w.num_q_heads, w.num_kv_heads, w.head_dim
+    T, Hq, Hkv, d = w.num_rows, w.num_q_heads, w.num_kv_heads, w.head_dim
     dt = _TORCH_DTYPES[w.dtype]
     q = torch.randn((T, Hq, d), generator=gen, dtype=torch.float32).to(dt)
     k = torch.randn((T, Hkv, d), generator=gen, dtype=torch.float32).to(dt)
@@ -100,18 +116,24 @@ def make_inputs(w: Workload, seed: int = 0) -> dict:
     sinks = torch.randn((Hq,), generator=gen, dtype=torch.float32) + float(w.sink_mean)
     qnorm_w = 1.0 + 0.02 * torch.randn((d,), generator=gen, dtype=torch.float32)
     knorm_w = 1.0 + 0.02 * torch.randn((d,), generator=gen, dtype=torch.float32)
-    return {
+    out = {
         "q": q, "k": k, "v": v,
         "cu_seqlens": torch.from_numpy(cu_seqlens(w.lengths)),
         "sinks": sinks, "qnorm_w": qnorm_w, "knorm_w": knorm_w,
     }
+    if w.pad_to:
+        _, cp = padded_boundaries(w.lengths, [w.pad_to] * w.num_docs)
+        out["cu_seqlens_padded"] = torch.from_numpy(cp)
+        out["attention_mask"] = (torch.arange(w.pad_to)[None, :]
+                                 < torch.tensor(w.lengths)[:, None])
+    return out
 
 
 def make_grad_output(w: Workload, seed: int = 0) -> torch.Tensor:
     """dout [T, Hq, d] in w.dtype for the backward of workload ``w``."""
     gen = torch.Generator(device="cpu")
     gen.manual_seed(seed + 1)
-    return torch.randn((w.total_tokens, w.num_q_heads, w.head_dim), generator=gen,
+    return torch.randn((w.num_rows, w.num_q_heads, w.head_dim), generator=gen,
                        dtype=torch.float32).to(_TORCH_DTYPES[w.dtype])
 
 
@@ -140,3 +162,14 @@ def sample_rows(lengths, window: int, n_random: int, seed: int = 0,
         rng = np.random.default_rng(seed + 12345)
         picks.update(int(x) for x in rng.integers(0, T, size=n_random))
     return np.array(sorted(picks), dtype=np.int32)
+
+
+def padded_boundaries(lengths, slots):
+    """cu_seqlens (prefix sums of the real lengths) and cu_seqlens_padded
+    (prefix sums of the slot sizes) of a padded-THD batch: document n's real
+    tokens open its slot of slots[n] tokens, padding fills the rest."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    slots = np.asarray(slots, dtype=np.int64)
+    if np.any(lengths > slots):
+        raise ValueError("a document is longer than its slot")
+    return cu_seqlens(lengths), cu_seqlens(slots)
