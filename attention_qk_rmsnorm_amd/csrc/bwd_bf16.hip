@@ -183,6 +183,34 @@ __device__ __forceinline__ int last_viewer(const int32_t* __restrict__ cu,
   return e - 1;
 }
 
+// First and last real token in [a, b] (real: inside some document's
+// [start, real end)); first > last when the range holds none.  Without
+// padding every token is real and this returns [a, b].
+__device__ __forceinline__ void real_span(const int32_t* __restrict__ cu,
+                                          const int32_t* __restrict__ cu_end, int D, int a,
+                                          int b, int& first, int& last) {
+  first = b + 1;
+  const int n = doc_of_token(cu, D, a);
+  if (a < cu_end[n]) {
+    first = a;
+  } else {
+    for (int m = n + 1; m < D && cu[m] <= b; ++m)
+      if (cu_end[m] > cu[m]) {
+        first = cu[m];
+        break;
+      }
+  }
+  last = a - 1;
+  for (int m = doc_of_token(cu, D, b);; --m) {
+    if (cu_end[m] > cu[m]) {
+      last = min(b, cu_end[m] - 1);
+      break;
+    }
+    if (m == 0 || cu[m] <= a) break;
+  }
+  if (first > last) first = last + 1;
+}
+
 // Earliest key visible to token t: max(document start, t - W + 1).
 __device__ __forceinline__ int first_key(const int32_t* __restrict__ cu, int D, int t,
                                          int window) {
@@ -786,23 +814,39 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
   const int qb = n_qb - 1 - (int)(blockIdx.x / Hkv), g = blockIdx.x % Hkv;
   const int tpt = 32 >> log2G;
   const int ct = qb * kDqWaves + wave;  // this wave's column tile
-  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
 
   // this lane's column: token t, head h
   const int t = ct * tpt + (col >> log2G);
   const int h = g * G + (col & (G - 1));
   const bool t_in = ct < n_ct && t < T;
+  // the block's real tokens [a0, a1]; a block of document padding only
+  // (block-uniform) writes zero dq and no weight gradient, and leaves
+  int a0 = 0, a1 = -1;
+  if (qb * kDqWaves * tpt < T)
+    real_span(cu, cu_end, D, qb * kDqWaves * tpt, min((qb + 1) * kDqWaves * tpt, T) - 1, a0, a1);
+  if (a0 > a1) {
+    if (t_in) {
+      bf16* dz = dq + ((size_t)t * Hq + h) * kHeadDim + 4 * hf;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        *reinterpret_cast<uint2*>(dz + 32 * (i >> 2) + 8 * (i & 3)) = make_uint2(0, 0);
+    }
+    if (tid < kHeadDim) dwq_part[(size_t)blockIdx.x * kHeadDim + tid] = 0.f;
+    return;
+  }
+  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
   const bool t_ok = t_in && t < cu_end[doc_of_token(cu, D, t)];  // a real query
   const int tcl = t_in ? t : 0;
   const int t_lo = t_ok ? first_key(cu, D, t, window) : 1 << 30;  // visible keys [t_lo, t]
-  // the wave's tokens and the block's key range
-  const int ta = ct * tpt, tb = min(ta + tpt - 1, T - 1);
-  const bool wave_ok = ct < n_ct && ta < T;
-  const int a0 = qb * kDqWaves * tpt;
-  const int a1 = min((qb + 1) * kDqWaves * tpt, T);
-  const int lo = a0 < T ? first_key(cu, D, a0, window) : 0;
+  // the wave's real tokens [ta, tb] and the block's key range (the keys its
+  // real tokens see; document padding sees none)
+  int ta = 0, tb = -1;
+  if (ct < n_ct && ct * tpt < T)
+    real_span(cu, cu_end, D, ct * tpt, min(ct * tpt + tpt, T) - 1, ta, tb);
+  const bool wave_ok = ta <= tb;
+  const int lo = first_key(cu, D, a0, window);
   const int kt_lo = lo & ~(kKeyTile - 1);
-  const int n_tiles = a0 < a1 ? (a1 - kt_lo + kKeyTile - 1) / kKeyTile : 0;
+  const int n_tiles = (a1 + 1 - kt_lo + kKeyTile - 1) / kKeyTile;
   const int wa_lo = wave_ok ? first_key(cu, D, ta, window) : 0;
   const int wb_lo = wave_ok ? first_key(cu, D, tb, window) : 0;
   const char* ktiles = keys + (size_t)g * n_kt * kKeyTileBytes;

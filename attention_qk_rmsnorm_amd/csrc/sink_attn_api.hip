@@ -56,20 +56,36 @@ __global__ void doc_ends_kernel(const int32_t* __restrict__ cu,
   if (n < D) ends[n] = cu_padded[n] + (cu[n + 1] - cu[n]);
 }
 
-// One thread per (token, head): rows of document padding get out = 0 and
-// lse = sinks[h] (their softmax holds the sink alone).
-template <typename T_OUT>
-__global__ void pad_fill_kernel(const int32_t* __restrict__ starts,
-                                const int32_t* __restrict__ ends, int D, int T, int Hq, int d,
-                                const float* __restrict__ sinks, T_OUT* __restrict__ out,
-                                float* __restrict__ lse) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)T * Hq) return;
-  const int t = (int)(idx / Hq), h = (int)(idx - (int64_t)t * Hq);
-  if (t < ends[doc_of_token(starts, D, t)]) return;
-  T_OUT* o = out + idx * d;
-  for (int i = 0; i < d; ++i) o[i] = (T_OUT)0.f;
-  if (lse != nullptr) lse[(int64_t)h * T + t] = sinks[h];
+// Padding rows of the output: out = 0 and lse = sinks[h] (their softmax holds
+// the sink alone).  A workgroup covers kFillTokens tokens: it finds which are
+// padding, then clears their rows with coalesced row-wide stores of V (16
+// bytes when the output is 16-byte aligned, else 4).
+constexpr int kFillTokens = 8;
+
+template <typename V>
+__global__ __launch_bounds__(256) void pad_fill_kernel(
+    const int32_t* __restrict__ starts, const int32_t* __restrict__ ends, int D, int T, int Hq,
+    int row_words, const float* __restrict__ sinks, V* __restrict__ out,
+    float* __restrict__ lse) {
+  __shared__ int s_pad[kFillTokens];
+  const int t0 = blockIdx.x * kFillTokens;
+  if (threadIdx.x < kFillTokens) {
+    const int t = t0 + (int)threadIdx.x;
+    s_pad[threadIdx.x] = t < T && t >= ends[doc_of_token(starts, D, t)];
+  }
+  __syncthreads();
+  V zero;
+  memset(&zero, 0, sizeof(zero));
+  for (int i = 0; i < kFillTokens; ++i) {
+    if (!s_pad[i]) continue;
+    V* row = out + (size_t)(t0 + i) * row_words;
+    for (int w = threadIdx.x; w < row_words; w += blockDim.x) row[w] = zero;
+  }
+  if (lse != nullptr)
+    for (int idx = threadIdx.x; idx < kFillTokens * Hq; idx += blockDim.x) {
+      const int i = idx % kFillTokens, h = idx / kFillTokens;
+      if (s_pad[i]) lse[(size_t)h * T + t0 + i] = sinks[h];
+    }
 }
 
 }  // namespace
@@ -84,61 +100,103 @@ hipError_t launch_doc_ends(const int32_t* cu, const int32_t* cu_padded, int D, i
 hipError_t launch_pad_fill(const int32_t* starts, const int32_t* ends, int D, int T, int Hq,
                            int d, int dtype, const float* sinks, void* out, float* lse,
                            hipStream_t stream) {
-  const int64_t n = (int64_t)T * Hq;
-  const unsigned grid = (unsigned)((n + 255) / 256);
-  if (dtype == SINK_ATTN_BF16)
-    pad_fill_kernel<bf16><<<dim3(grid), dim3(256), 0, stream>>>(
-        starts, ends, D, T, Hq, d, sinks, static_cast<bf16*>(out), lse);
+  if (T <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((T + kFillTokens - 1) / kFillTokens);
+  const size_t row_bytes = (size_t)Hq * d * (dtype == SINK_ATTN_BF16 ? 2 : 4);
+  if (row_bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0)
+    pad_fill_kernel<uint4><<<dim3(grid), dim3(256), 0, stream>>>(
+        starts, ends, D, T, Hq, (int)(row_bytes / 16), sinks, static_cast<uint4*>(out), lse);
   else
-    pad_fill_kernel<float><<<dim3(grid), dim3(256), 0, stream>>>(
-        starts, ends, D, T, Hq, d, sinks, static_cast<float*>(out), lse);
+    pad_fill_kernel<uint32_t><<<dim3(grid), dim3(256), 0, stream>>>(
+        starts, ends, D, T, Hq, (int)(row_bytes / 4), sinks, static_cast<uint32_t*>(out), lse);
   return hipGetLastError();
 }
 
 namespace {
 
 // BSHD attention mask [batch][seq] (nonzero = real token) to padded THD
-// boundaries, one workgroup walking the rows in order: the real length of row
-// b is its count of real tokens; padding must trail (the row is a prefix of
-// real tokens), else the row is counted in bad_rows.
-__global__ void mask_to_seqlens_kernel(const uint8_t* __restrict__ mask, int batch, int seq,
-                                       int32_t* __restrict__ cu, int32_t* __restrict__ cu_padded,
-                                       int32_t* __restrict__ bad_rows) {
+// boundaries in two launches.  mask_rows_kernel: one workgroup per row counts
+// its real tokens and checks that the padding trails (the first padding
+// position comes after the last real one); it leaves the count in
+// cu[b + 1], or -1 - count for a row whose padding does not trail.
+__global__ __launch_bounds__(256) void mask_rows_kernel(const uint8_t* __restrict__ mask,
+                                                        int seq, int32_t* __restrict__ cu) {
   __shared__ int s_count, s_first_pad, s_last_real;
-  int running = 0, bad = 0;
+  const int b = blockIdx.x;
   if (threadIdx.x == 0) {
-    cu[0] = 0;
-    cu_padded[0] = 0;
+    s_count = 0;
+    s_first_pad = seq;
+    s_last_real = -1;
   }
-  for (int b = 0; b < batch; ++b) {
-    if (threadIdx.x == 0) {
-      s_count = 0;
-      s_first_pad = seq;
-      s_last_real = -1;
+  __syncthreads();
+  const uint8_t* row = mask + (size_t)b * seq;
+  int count = 0, first_pad = seq, last_real = -1;
+  for (int i = threadIdx.x; i < seq; i += blockDim.x) {
+    if (row[i]) {
+      ++count;
+      last_real = i;
+    } else {
+      first_pad = min(first_pad, i);
     }
-    __syncthreads();
-    int count = 0, first_pad = seq, last_real = -1;
-    for (int i = threadIdx.x; i < seq; i += blockDim.x) {
-      if (mask[(size_t)b * seq + i]) {
-        ++count;
-        last_real = i;
-      } else if (first_pad == seq) {
-        first_pad = i;
-      }
-    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    count += __shfl_xor(count, o);
+    first_pad = min(first_pad, __shfl_xor(first_pad, o));
+    last_real = max(last_real, __shfl_xor(last_real, o));
+  }
+  if ((threadIdx.x & 63) == 0) {
     atomicAdd(&s_count, count);
     atomicMin(&s_first_pad, first_pad);
     atomicMax(&s_last_real, last_real);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) cu[b + 1] = s_first_pad < s_last_real ? -1 - s_count : s_count;
+}
+
+// mask_seqlens_scan_kernel: one workgroup turns the row counts into prefix
+// sums (cu_seqlens), writes the slot starts b * seq (cu_seqlens_padded) and
+// the number of rows whose padding does not trail.
+__global__ __launch_bounds__(256) void mask_seqlens_scan_kernel(int batch, int seq,
+                                                                int32_t* __restrict__ cu,
+                                                                int32_t* __restrict__ cu_padded,
+                                                                int32_t* __restrict__ bad_rows) {
+  __shared__ int s_scan[256];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_bad = 0;
+  int carry = 0, bad = 0;
+  for (int base = 0; base < batch; base += 256) {
+    const int b = base + tid;
+    int v = 0;
+    if (b < batch) {
+      v = cu[b + 1];
+      if (v < 0) {
+        v = -1 - v;
+        ++bad;
+      }
+    }
+    s_scan[tid] = v;
     __syncthreads();
-    if (threadIdx.x == 0) {
-      running += s_count;
-      bad += s_first_pad < s_last_real;
-      cu[b + 1] = running;
+    for (int o = 1; o < 256; o <<= 1) {  // inclusive scan (Hillis-Steele)
+      const int add = tid >= o ? s_scan[tid - o] : 0;
+      __syncthreads();
+      s_scan[tid] += add;
+      __syncthreads();
+    }
+    if (b < batch) {
+      cu[b + 1] = carry + s_scan[tid];
       cu_padded[b + 1] = (b + 1) * seq;
     }
+    carry += s_scan[255];
     __syncthreads();
   }
-  if (threadIdx.x == 0) *bad_rows = bad;
+  if (tid == 0) {
+    cu[0] = 0;
+    cu_padded[0] = 0;
+  }
+  atomicAdd(&s_bad, bad);
+  __syncthreads();
+  if (tid == 0) *bad_rows = s_bad;
 }
 
 }  // namespace
@@ -501,8 +559,12 @@ int sink_attn_mask_to_seqlens(const uint8_t* attention_mask, int32_t batch, int3
       !aligned(cu_seqlens, 4) || !aligned(cu_seqlens_padded, 4) || !aligned(bad_rows, 4))
     return SINK_ATTN_EINVAL;
   if ((int64_t)batch * seq > 0 && attention_mask == nullptr) return SINK_ATTN_EINVAL;
-  sa::mask_to_seqlens_kernel<<<dim3(1), dim3(256), 0, static_cast<hipStream_t>(stream)>>>(
-      attention_mask, batch, seq, cu_seqlens, cu_seqlens_padded, bad_rows);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (batch > 0)  // (seq = 0: every row counts 0 and reads nothing)
+    sa::mask_rows_kernel<<<dim3((unsigned)batch), dim3(256), 0, st>>>(attention_mask, seq,
+                                                                       cu_seqlens);
+  sa::mask_seqlens_scan_kernel<<<dim3(1), dim3(256), 0, st>>>(batch, seq, cu_seqlens,
+                                                              cu_seqlens_padded, bad_rows);
   return hipGetLastError() == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;
 }
 

@@ -302,3 +302,63 @@ def test_full_size_bshd_backward():
         msg.append(f"{key} vs unpadded {rel:.2e}")
         assert rel <= BWD_REL_MAX, (key, rel)
     _say("  sliding_bshd bwd: rel max/mean " + ", ".join(msg))
+
+
+# tight slots: empty slots, slots that the document fills exactly and short
+# padding gaps, so query blocks and key tiles span several documents
+TIGHT_LENGTHS = [5, 0, 0, 3, 60, 0, 17, 1, 130, 64, 2]
+TIGHT_SLOTS = [9, 0, 4, 3, 64, 0, 20, 2, 131, 64, 70]
+
+
+@pytest.mark.parametrize("heads", [(32, 4), (8, 8), (32, 1)])
+def test_padded_backward_tight_slots(heads):
+    import attention_qk_rmsnorm_amd as A
+    _say(f"case padded bwd tight slots heads={heads}")
+    Hq, Hkv = heads
+    inp, rows, pad = _padded_inputs(TIGHT_LENGTHS, TIGHT_SLOTS, Hq=Hq, Hkv=Hkv)
+    T = sum(TIGHT_SLOTS)
+    dout = workloads.make_grad_output(workloads.Workload("g", (T,), Hq, Hkv), 3)
+    dout[torch.from_numpy(pad)] = float("nan")
+    dev = to_device(inp)
+    for window, use_rope in ((-1, False), (7, True)):
+        out, lse = A.sink_attn_fwd(dev["q"], dev["k"], dev["v"], dev["cu_seqlens"],
+                                   dev["sinks"], dev["qnorm_w"], dev["knorm_w"], window,
+                                   use_rope, cu_seqlens_padded=dev["cu_seqlens_padded"])
+        torch.cuda.synchronize()
+        _check_fwd(inp, rows, pad, out, lse, window, use_rope, f"tight fwd W={window}")
+        g = A.sink_attn_bwd(dev["q"], dev["k"], dev["v"], dev["cu_seqlens"], dev["sinks"],
+                            dev["qnorm_w"], dev["knorm_w"], window, use_rope, out, lse,
+                            dout.to("cuda:0"), cu_seqlens_padded=dev["cu_seqlens_padded"])
+        torch.cuda.synchronize()
+        _check_grads(g, _oracle_bwd(inp, window, use_rope, rows, dout), rows, pad,
+                     f"tight {heads} W={window}")
+
+
+@pytest.mark.parametrize("batch,seq", [(1, 1), (3, 5), (300, 77), (700, 1), (2, 1000)])
+def test_mask_to_seqlens_shapes(batch, seq):
+    import attention_qk_rmsnorm_amd as A
+    _say(f"case mask_to_seqlens {batch}x{seq}")
+    rng = np.random.default_rng(batch * 1000 + seq)
+    lengths = rng.integers(0, seq + 1, size=batch)
+    mask = torch.from_numpy(np.arange(seq)[None, :] < lengths[:, None])
+    cu, cp = A.mask_to_seqlens(mask.to("cuda:0"))
+    ref_cu, ref_cp = workloads.padded_boundaries(lengths, [seq] * batch)
+    assert np.array_equal(cu.cpu().numpy(), ref_cu) and np.array_equal(cp.cpu().numpy(), ref_cp)
+    if seq > 2:
+        holes = mask.clone()
+        hit = np.nonzero(lengths >= 2)[0][:5]
+        for b in hit:
+            holes[b, 0] = False  # a gap before real tokens
+        if len(hit):
+            lib = A.load_library()
+            m = holes.to("cuda:0").view(torch.uint8).contiguous()
+            c = torch.empty(batch + 1, dtype=torch.int32, device="cuda:0")
+            p = torch.empty_like(c)
+            bad = torch.full((1,), -7, dtype=torch.int32, device="cuda:0")
+            import ctypes
+            rc = lib.sink_attn_mask_to_seqlens(
+                ctypes.c_void_p(m.data_ptr()), batch, seq, ctypes.c_void_p(c.data_ptr()),
+                ctypes.c_void_p(p.data_ptr()), ctypes.c_void_p(bad.data_ptr()),
+                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            torch.cuda.synchronize()
+            assert rc == 0 and int(bad.item()) == len(hit)
