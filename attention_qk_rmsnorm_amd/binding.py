@@ -18,13 +18,15 @@ from .build import LIB_PATH
 
 SINK_ATTN_BF16 = 0
 SINK_ATTN_F32 = 1
+SINK_ATTN_F16 = 2
 
 SINK_ATTN_TILE_AUTO = 0
 SINK_ATTN_TILE_NARROW = 1
 SINK_ATTN_TILE_WIDE = 2
 SINK_ATTN_TILE_WIDE_EXACT = 3
 
-_DTYPES = {torch.bfloat16: SINK_ATTN_BF16, torch.float32: SINK_ATTN_F32}
+_DTYPES = {torch.bfloat16: SINK_ATTN_BF16, torch.float32: SINK_ATTN_F32,
+           torch.float16: SINK_ATTN_F16}
 
 
 class SinkAttnDesc(ctypes.Structure):
@@ -295,8 +297,8 @@ class BwdCall:
                  workspace=None, stream=None, grads=None, cu_seqlens_padded=None):
         if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
             raise ValueError("q, k, v must be THD tensors [tokens, heads, head_dim]")
-        if q.dtype != torch.bfloat16:
-            raise ValueError("the backward takes bf16 q, k, v, out and dout")
+        if q.dtype not in (torch.bfloat16, torch.float16):
+            raise ValueError("the backward takes bf16 or fp16 q, k, v, out and dout")
         dev = q.device
         T, Hq, d = q.shape
         Hkv = k.shape[1]

@@ -1,4 +1,7 @@
-// attn_bf16.hip -- sink-aware GQA attention forward, bf16 in/out, gfx950 MFMA.
+// attn_bf16.hip -- sink-aware GQA attention forward, 16-bit in/out (bf16, or
+// fp16 for the fp16 I/O variant), gfx950 MFMA.  The kernel is a template over
+// the element type E; everything below says "E" where the two differ only in
+// the type of the operands (v_mfma_f32_32x32x16_bf16 or _f16).
 //
 // Computes, for every (token t, query head h) of a packed THD batch
 //   out = sum_{j visible} exp(s_j - M) v_j / (exp(sink_h - M) + sum_j exp(s_j - M))
@@ -11,20 +14,20 @@
 // Workgroup = 4 waves = one query block of one kv head g: tokens
 // [a, a + 128/G) of one document, times the G query heads that read kv head g.
 // Each wave owns 32 (token, head) columns.  RMSNorm and RoPE of the wave's
-// queries are done once at the start, in fp32, straight into bf16 MFMA
+// queries are done once at the start, in fp32, straight into E MFMA
 // operands.  The key loop walks 64-key tiles of k_hat and V^T (written by the
 // prologue), copied global -> LDS by global_load_lds_dwordx4 (no VGPR
 // staging) into one of two buffers while the other is consumed; the tile is
 // shared by all 4 waves, i.e. by the 8 query heads of the group at 4 tokens
 // per wave.  Per tile and wave:
-//   S^T[key][col] = K Q^T - m_ref   2 x (8 + 1) v_mfma_f32_32x32x16_bf16: Q is
+//   S^T[key][col] = K Q^T - m_ref   2 x (8 + 1) v_mfma_f32_32x32x16_E: Q is
 //   pre-scaled by scale * log2(e), and a ninth step with A = a column of ones
 //   and B = -m_ref subtracts the column's reference max inside the MFMA, so
 //   the weights need one v_exp_f32 each and no other VALU op
 //   online softmax in the log2 domain, the sink seeding the running max and
 //   denominator; band masks only on tiles that cross a document, causal or
 //   window edge; tiles outside the band are never visited
-//   O^T[d][col] += V^T P^T     16 v_mfma_f32_32x32x16_bf16 (P rounded to bf16)
+//   O^T[d][col] += V^T P^T     16 v_mfma_f32_32x32x16_E (P rounded to E)
 // MFMA operand layouts (32x32x16, wave64): A lane l holds A[l%32][8(l/32)..+7],
 // B lane l holds B[8(l/32)..+7][l%32], and accumulator register r of lane l is
 // C[8(r/4) + 4(l/32) + r%4][l%32].  With S^T in that layout a lane holds 16 keys
@@ -44,12 +47,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazy = 8.0f;  // log2-domain slack before the running max moves
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // Copy the 64-key tile at kt into LDS buffer `buf`: the prologue wrote k_hat
 // and V^T as the exact LDS image (see sa_device.h), so this is a straight
@@ -69,22 +67,24 @@ __device__ __forceinline__ void issue_tile(const char* __restrict__ ktile,
 }
 
 // Per-lane state of one wave's 32 query columns.
+template <typename E>
 struct ColState {
-  bf16x8 qf[8];     // Q^T B operands, channels 16kk + 8hf .. +7
+  vec8<E> qf[8];    // Q^T B operands, channels 16kk + 8hf .. +7
   f32x16 o[4];      // O^T accumulators, channels 32dd + ...
-  bf16x8 ones_a;    // A operand of the reference step: A[key][0] = 1
-  bf16x8 negm_b;    // B operand of the reference step: B[0][col] = -m_ref
-  float m_ref;      // reference max (log2 domain, bf16-representable, or -inf)
+  vec8<E> ones_a;   // A operand of the reference step: A[key][0] = 1
+  vec8<E> negm_b;   // B operand of the reference step: B[0][col] = -m_ref
+  float m_ref;      // reference max (log2 domain, E-representable, or -inf)
   float l_part;     // this lane's share of the denominator
 };
 
 // B operand that makes the reference MFMA step subtract m_ref from every
 // score of the column: lanes 0-31 hold k-slot 0 of their column.
-__device__ __forceinline__ bf16x8 neg_ref_operand(float m_ref, int hf) {
-  bf16x8 b;
+template <typename E>
+__device__ __forceinline__ vec8<E> neg_ref_operand(float m_ref, int hf) {
+  vec8<E> b;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) b[e] = (bf16)0.f;
-  if (hf == 0 && m_ref != -INFINITY) b[0] = (bf16)(-m_ref);
+  for (int e = 0; e < 8; ++e) b[e] = (E)0.f;
+  if (hf == 0 && m_ref != -INFINITY) b[0] = (E)(-m_ref);
   return b;
 }
 
@@ -92,14 +92,14 @@ __device__ __forceinline__ bf16x8 neg_ref_operand(float m_ref, int hf) {
 // sink-seeded state, O^T += V^T P^T.  LDS operand reads are issued one step
 // ahead of the MFMAs that consume them; sched_barrier keeps the compiler from
 // sinking them back next to their use.
-template <int BUF>
+template <typename E, int BUF>
 __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8],
-                                            const int (&voff)[4], ColState& st, int kt,
+                                            const int (&voff)[4], ColState<E>& st, int kt,
                                             int hf, int tok, bool tok_ok, int tw0, int tw1,
                                             int doc_start, int window) {
   const char* kbuf = lds + BUF * kBuf;
   const char* vbuf = kbuf + kTileK;
-  auto rd = [](const char* p) { return *reinterpret_cast<const bf16x8*>(p); };
+  auto rd = [](const char* p) { return *reinterpret_cast<const vec8<E>*>(p); };
 
   // ---- S^T = K Q^T: two 32-key chains, K fragments one step ahead --------
   f32x16 s0, s1;
@@ -108,10 +108,10 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
     s0[r] = 0.f;
     s1[r] = 0.f;
   }
-  bf16x8 a0 = rd(kbuf + koff[0]), a1 = rd(kbuf + 8192 + koff[0]);
+  vec8<E> a0 = rd(kbuf + koff[0]), a1 = rd(kbuf + 8192 + koff[0]);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    bf16x8 n0 = a0, n1 = a1;
+    vec8<E> n0 = a0, n1 = a1;
     if (kk < 7) {
       n0 = rd(kbuf + koff[kk + 1]);
       n1 = rd(kbuf + 8192 + koff[kk + 1]);
@@ -122,12 +122,12 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
     a0 = n0;
     a1 = n1;
   }
-  // reference step: every score of a column minus m_ref (exact: m_ref is a
-  // bf16 value), so the accumulators hold s * scale * log2e - m_ref
+  // reference step: every score of a column minus m_ref (exact: m_ref is an
+  // E value), so the accumulators hold s * scale * log2e - m_ref
   s0 = mfma32(st.ones_a, st.negm_b, s0);
   s1 = mfma32(st.ones_a, st.negm_b, s1);
   // V fragments of the first PV step, read while the softmax runs
-  bf16x8 va[4];
+  vec8<E> va[4];
 #pragma unroll
   for (int dd = 0; dd < 4; ++dd) va[dd] = rd(vbuf + dd * 4096 + voff[0]);
   __builtin_amdgcn_sched_barrier(0);
@@ -164,11 +164,11 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
   const bool grow = no_ref ? mx > -INFINITY : mx > kLazy;
   if (__any(grow)) {
     const float m_eff = no_ref ? 0.f : st.m_ref;         // what the step subtracted
-    const float m_new = grow ? (float)(bf16)(m_eff + mx) : st.m_ref;
+    const float m_new = grow ? ref_round<E>(m_eff + mx) : st.m_ref;
     const float delta = grow ? m_new - m_eff : 0.f;
     const float alpha = grow ? (no_ref ? 0.f : __builtin_amdgcn_exp2f(st.m_ref - m_new)) : 1.f;
     st.m_ref = m_new;
-    st.negm_b = neg_ref_operand(m_new, hf);
+    st.negm_b = neg_ref_operand<E>(m_new, hf);
     st.l_part *= alpha;
 #pragma unroll
     for (int dd = 0; dd < 4; ++dd)
@@ -181,30 +181,30 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
     }
   }
 
-  // ---- P = exp2(s * scale * log2e - m) into bf16 B operands; O^T += V^T P^T.
+  // ---- P = exp2(s * scale * log2e - m) into E B operands; O^T += V^T P^T.
   // Step j covers keys 16j..16j+15 (j = 2 kb + sp): B operand k-slot 8hf + e
   // <-> key 16j + 8(e/4) + 4hf + e%4, which is the order the prologue stored
   // V^T keys in, so the A operand is one 16-byte read.  The denominator sums
-  // the same bf16 weights the PV product uses.
-  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  // the same rounded weights the PV product uses.
+  const vec2<E> ones = {(E)1.0f, (E)1.0f};
   auto weights = [&](int j) {
     const f32x16& sv = (j < 2) ? s0 : s1;
     const int base = 8 * (j & 1);
-    bf16x8 pb;
+    vec8<E> pb;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      pb[e] = (bf16)__builtin_amdgcn_exp2f(sv[base + e]);
+      pb[e] = (E)__builtin_amdgcn_exp2f(sv[base + e]);
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const bf16x2 pr = {pb[e], pb[e + 1]};
-      st.l_part = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, st.l_part, false);
+      const vec2<E> pr = {pb[e], pb[e + 1]};
+      st.l_part = dot2<E>(pr, ones, st.l_part);
     }
     return pb;
   };
-  bf16x8 pb = weights(0);
+  vec8<E> pb = weights(0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    bf16x8 vn[4];
+    vec8<E> vn[4];
     if (j < 3) {
 #pragma unroll
       for (int dd = 0; dd < 4; ++dd) vn[dd] = rd(vbuf + dd * 4096 + voff[j + 1]);
@@ -220,11 +220,12 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
   }
 }
 
+template <typename E>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ khat,
-    const bf16* __restrict__ vt, const int32_t* __restrict__ cu,
+    const E* __restrict__ q, const E* __restrict__ khat,
+    const E* __restrict__ vt, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ cu_end, const int32_t* __restrict__ sched, const float* __restrict__ sinks,
-    const float* __restrict__ qnorm_w, bf16* __restrict__ out, float* __restrict__ lse,
+    const float* __restrict__ qnorm_w, E* __restrict__ out, float* __restrict__ lse,
     int T, int Hq, int Hkv, int G, int log2G, int64_t t_pad, int window, int use_rope,
     float eps, double theta, float c_log2, int xcd_per) {
   // ---- work item: blocks of one kv head stay on one group of XCDs --------
@@ -276,19 +277,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
   __syncthreads();
 
-  ColState st;
-  // ---- Q: load, RMSNorm, RoPE, round to bf16 B operands --------------------
+  ColState<E> st;
+  // ---- Q: load, RMSNorm, RoPE, round to E B operands -----------------------
   // lane holds channels 16kk + 8hf + e (kk < 8, e < 8) of its column; NeoX
   // partners i and i + 64 (kk and kk + 4) sit in the same lane.  The global
   // loads go out before the first tile's copy: vmcnt retires in order, so
   // waiting for them then does not wait for the copy.
   {
-    bf16x8 qraw[8];
+    vec8<E> qraw[8];
     float w[64];
-    const bf16* qp = q + ((size_t)(tok_ok ? tok : a) * Hq + hq) * kHeadDim + 8 * hf;
+    const E* qp = q + ((size_t)(tok_ok ? tok : a) * Hq + hq) * kHeadDim + 8 * hf;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      qraw[kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+      qraw[kk] = *reinterpret_cast<const vec8<E>*>(qp + 16 * kk);
 #pragma unroll
       for (int e = 0; e < 8; ++e) w[8 * kk + e] = qnorm_w[16 * kk + 8 * hf + e];
     }
@@ -326,19 +327,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) st.qf[kk][e] = (bf16)(x[8 * kk + e] * c_log2);
+      for (int e = 0; e < 8; ++e) st.qf[kk][e] = (E)(x[8 * kk + e] * c_log2);
   }
 
   // running state in the log2 domain: m = max(sink, scores) * log2(e) scaled,
   // l = partial denominator of this lane's keys (the sink's 1 in half 0 only)
   {
     const float sl = sinks[hq] * kLog2e;
-    st.m_ref = sl == -INFINITY ? -INFINITY : (float)(bf16)sl;
+    st.m_ref = sl == -INFINITY ? -INFINITY : ref_round<E>(sl);
     st.l_part = (hf == 0 && sl != -INFINITY) ? __builtin_amdgcn_exp2f(sl - st.m_ref) : 0.f;
-    st.negm_b = neg_ref_operand(st.m_ref, hf);
+    st.negm_b = neg_ref_operand<E>(st.m_ref, hf);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) st.ones_a[e] = (bf16)0.f;
-    if (hf == 0) st.ones_a[0] = (bf16)1.f;
+    for (int e = 0; e < 8; ++e) st.ones_a[e] = (E)0.f;
+    if (hf == 0) st.ones_a[0] = (E)1.f;
   }
 #pragma unroll
   for (int dd = 0; dd < 4; ++dd)
@@ -367,27 +368,27 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       const bool active = (tw0 < tw1) && (kt < tw1) && (kt + kKeyTile > wlo);
       if (active) {
         if (b == 0)
-          attend_tile<0>(lds, koff, voff, st, kt, hf, tok, tok_ok, tw0, tw1, doc_start, window);
+          attend_tile<E, 0>(lds, koff, voff, st, kt, hf, tok, tok_ok, tw0, tw1, doc_start, window);
         else
-          attend_tile<1>(lds, koff, voff, st, kt, hf, tok, tok_ok, tw0, tw1, doc_start, window);
+          attend_tile<E, 1>(lds, koff, voff, st, kt, hf, tok, tok_ok, tw0, tw1, doc_start, window);
       }
       kt += kKeyTile;
     }
   }
 
-  // ---- epilogue: out = O / l in bf16, lse = ln2 * (m + log2 l) -------------
+  // ---- epilogue: out = O / l in E, lse = ln2 * (m + log2 l) ----------------
   const float l = lane_pair_sum(st.l_part);
   if (tok_ok) {
     const float inv_l = 1.0f / l;
-    bf16* op = out + ((size_t)tok * Hq + hq) * kHeadDim + 4 * hf;
+    E* op = out + ((size_t)tok * Hq + hq) * kHeadDim + 4 * hf;
 #pragma unroll
     for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        bf16x4 w;
+        vec4<E> w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)(st.o[dd][4 * rq + e] * inv_l);
-        *reinterpret_cast<bf16x4*>(op + 32 * dd + 8 * rq) = w;
+        for (int e = 0; e < 4; ++e) w[e] = (E)(st.o[dd][4 * rq + e] * inv_l);
+        *reinterpret_cast<vec4<E>*>(op + 32 * dd + 8 * rq) = w;
       }
     if (lse != nullptr && hf == 0) lse[(size_t)hq * T + tok] = (st.m_ref + __log2f(l)) * kLn2;
   }
@@ -395,9 +396,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 
 }  // namespace
 
-hipError_t launch_attention_bf16(const bf16* q, const bf16* khat, const bf16* vt,
+template <typename E>
+hipError_t launch_attention_bf16(const E* q, const E* khat, const E* vt,
                                  const int32_t* cu, const int32_t* cu_end, const int32_t* sched,
-                                 const float* sinks, const float* qnorm_w, bf16* out,
+                                 const float* sinks, const float* qnorm_w, E* out,
                                  float* lse, int T, int D, int Hq, int Hkv,
                                  int64_t t_pad, int64_t items_ub, int window,
                                  int use_rope, double eps, double theta,
@@ -417,10 +419,20 @@ hipError_t launch_attention_bf16(const bf16* q, const bf16* khat, const bf16* vt
   }
   if (grid <= 0) return hipSuccess;
   const float c_log2 = (float)(scale * 1.4426950408889634);
-  attn_fwd_bf16_kernel<<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+  attn_fwd_bf16_kernel<E><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
       q, khat, vt, cu, cu_end, sched, sinks, qnorm_w, out, lse, T, Hq, Hkv, G, log2G, t_pad,
       window, use_rope, (float)eps, theta, c_log2, xcd_per);
   return hipGetLastError();
 }
+
+#define SA_INSTANTIATE(E)                                                                    \
+  template hipError_t launch_attention_bf16<E>(const E*, const E*, const E*, const int32_t*, \
+                                               const int32_t*, const int32_t*, const float*,   \
+                                               const float*, E*, float*, int, int, int, int,   \
+                                               int64_t, int64_t, int, int, double, double,     \
+                                               double, hipStream_t);
+SA_INSTANTIATE(bf16)
+SA_INSTANTIATE(f16)
+#undef SA_INSTANTIATE
 
 }  // namespace sa

@@ -1,5 +1,6 @@
-// attn_bf16_wide.hip -- sink-aware GQA attention forward, bf16 in/out, gfx950
-// MFMA, wide tiles (64 query columns per wave, one workgroup per CU).
+// attn_bf16_wide.hip -- sink-aware GQA attention forward, 16-bit in/out (bf16,
+// or fp16 for the fp16 I/O variant: a template over the element type E),
+// gfx950 MFMA, wide tiles (64 query columns per wave, one workgroup per CU).
 //
 // Computes, for every (token t, query head h) of a packed THD batch
 //   out = sum_{j visible} exp(s_j - M) v_j / (exp(sink_h - M) + sum_j exp(s_j - M))
@@ -14,7 +15,7 @@
 // head g.  Each wave owns 64 (token, head) columns as two 32-column blocks, so
 // every K or V^T operand read from LDS feeds two MFMAs: half the LDS traffic
 // per MFMA of the narrow configuration.  RMSNorm and RoPE of the wave's
-// queries are done once at the start, in fp32, straight into bf16 MFMA
+// queries are done once at the start, in fp32, straight into E MFMA
 // operands pre-scaled by scale * log2(e), which then live in AGPRs.
 //
 // Keys are walked in 64-key tiles of k_hat and V^T, which the prologue wrote
@@ -23,17 +24,19 @@
 // loop is software-pipelined inside each wave in 32-key half tiles: while the
 // VALU forms the weights of half tile u, the matrix core computes the scores
 // of half tile u + 1; then O accumulates half tile u's values.
-//   S^T[key][col] = K Q^T - m_ref   8 v_mfma_f32_32x32x16_bf16 per 32-key x
+//   S^T[key][col] = K Q^T - m_ref   8 v_mfma_f32_32x32x16_E per 32-key x
 //                                   32-column block; the chain starts from a
 //                                   tile of -m_ref, so a weight is one v_exp
-//   O^T[d][col] += V^T P^T          P rounded to bf16; O in AGPRs
+//   O^T[d][col] += V^T P^T          P rounded to E; O in AGPRs
 // The reference each weight is taken against is fixed for the whole key loop:
 // the larger of the sink and the token's score against its own key (always
 // visible).  Weights may exceed 1 -- exp2 of up to 90 keeps bf16 weights and
 // the fp32 sums finite and exact to their usual relative precision -- so the
 // loop never rescales O.  A block where some denominator passes 2^90 (a score
 // more than 90 log2 units above the reference) hands itself to a second
-// launch that finds the exact row max with a scores-only pass first.  Band
+// launch that finds the exact row max with a scores-only pass first.  fp16
+// weights overflow past 2^16 instead: such a weight rounds to inf, its
+// denominator is no longer finite, and the same rerun takes the block.  Band
 // masks run only on half tiles that cross a document, causal or window edge;
 // tiles outside the block's band are never visited.
 // MFMA operand layouts (32x32x16, wave64): A lane l holds A[l%32][8(l/32)..+7],
@@ -59,28 +62,31 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRedo = 0x1p90f;  // denominator bound that sends a block to its exact pass
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ inline f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // O^T accumulation kept in AGPRs: the accumulators are touched only by these
 // MFMAs, by their zeroing and by the epilogue (after agpr_fence()), which
 // leaves the 256 VGPRs to the scores, weights and operands.
-__device__ __forceinline__ void mfma32_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+template <typename E>
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, vec8<E> a, vec8<E> b) {
+  if constexpr (is_f16<E>)
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // Zero an AGPR accumulator with an MFMA of zero operands, so that every
 // definition of the accumulators is an AGPR one and the register allocator
 // never moves them through VGPRs.
-__device__ __forceinline__ void zero_acc(f32x16& acc, bf16x8 zero) {
+template <typename E>
+__device__ __forceinline__ void zero_acc(f32x16& acc, vec8<E> zero) {
   // s_nop 1: the zero operand was just written by VALU code, and an MFMA
   // needs two wait states before reading such a register; the compiler does
   // not count them for inline asm
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero));
+  if constexpr (is_f16<E>)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero));
 }
 
 // Wait states before VALU code reads or writes accumulators that an
@@ -89,8 +95,9 @@ __device__ __forceinline__ void agpr_fence() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
-__device__ __forceinline__ bf16x8 rd(const char* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
+template <typename E>
+__device__ __forceinline__ vec8<E> rd(const char* p) {
+  return *reinterpret_cast<const vec8<E>*>(p);
 }
 
 // Copy one 16 KiB tile image into LDS at dst: chunk 256 i + tid of the image
@@ -105,8 +112,9 @@ __device__ __forceinline__ void copy_image(const char* __restrict__ src, int tid
 }
 
 // Per-lane state of one wave's 64 query columns (column block cb = 0, 1).
+template <typename E>
 struct WaveState {
-  bf16x8 qf[2][8];   // Q^T B operands, channels 16kk + 8hf .. +7
+  vec8<E> qf[2][8];  // Q^T B operands, channels 16kk + 8hf .. +7
   f32x16 o[2][4];    // O^T accumulators (AGPRs), channels 32dd + ...
   f32x16 negm[2];    // -m_ref splat: the score MFMA chains start from it
   float m_ref[2];    // reference (log2 domain)
@@ -150,35 +158,37 @@ __device__ __forceinline__ void mask_half(int kh, const Cols& c, f32x16 (&s)[2])
 // Weights of keys 16jj .. 16jj + 15 of a half tile for column block cb:
 // B operand k-slot 8hf + e <-> key 16jj + 8(e/4) + 4hf + e%4, the order the
 // prologue stored V^T keys in.
-__device__ __forceinline__ bf16x8 weights(const f32x16& sv, int jj) {
-  bf16x8 pb;
+template <typename E>
+__device__ __forceinline__ vec8<E> weights(const f32x16& sv, int jj) {
+  vec8<E> pb;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) pb[e] = (bf16)__builtin_amdgcn_exp2f(sv[8 * jj + e]);
+  for (int e = 0; e < 8; ++e) pb[e] = (E)__builtin_amdgcn_exp2f(sv[8 * jj + e]);
   return pb;
 }
 
-__device__ __forceinline__ void add_denominator(const bf16x8& pb, float& l) {
-  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+template <typename E>
+__device__ __forceinline__ void add_denominator(const vec8<E>& pb, float& l) {
+  const vec2<E> ones = {(E)1.0f, (E)1.0f};
 #pragma unroll
   for (int e = 0; e < 8; e += 2) {
-    const bf16x2 pr = {pb[e], pb[e + 1]};
-    l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+    const vec2<E> pr = {pb[e], pb[e + 1]};
+    l = dot2<E>(pr, ones, l);
   }
 }
 
 // Scores of the half tile H of k_hat slot SLOT: s[cb] = K_H Q_cb^T - m_ref[cb]
 // (the chain starts from the -m_ref splat).
-template <int SLOT, int H>
+template <int SLOT, int H, typename E>
 __device__ __forceinline__ void score_half(const char* lds, const int (&koff)[8],
-                                           const WaveState& st, f32x16 (&s)[2]) {
+                                           const WaveState<E>& st, f32x16 (&s)[2]) {
   const char* kbuf = lds + SLOT * kSlot + H * 8192;
   s[0] = st.negm[0];
   s[1] = st.negm[1];
-  bf16x8 a = rd(kbuf + koff[0]);
+  vec8<E> a = rd<E>(kbuf + koff[0]);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
-    bf16x8 n = a;
-    if (kk < 7) n = rd(kbuf + koff[kk + 1]);
+    vec8<E> n = a;
+    if (kk < 7) n = rd<E>(kbuf + koff[kk + 1]);
     __builtin_amdgcn_sched_barrier(0);
     s[0] = mfma32(a, st.qf[0][kk], s[0]);
     s[1] = mfma32(a, st.qf[1][kk], s[1]);
@@ -193,23 +203,23 @@ __device__ __forceinline__ void score_half(const char* lds, const int (&koff)[8]
 // O^T += V^T P^T and the denominator, then masks sn if it crosses an edge.
 // When there is no next half tile (next == false) sn is still computed, from
 // valid LDS, and ignored.
-template <int VS, int VH, int KS, int KH, int KSN, int KHN>
+template <int VS, int VH, int KS, int KH, int KSN, int KHN, typename E>
 __device__ __forceinline__ void half_step(const char* lds, const int (&koff)[8],
-                                          const int (&voff)[4], WaveState& st,
-                                          f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&kf)[8],
+                                          const int (&voff)[4], WaveState<E>& st,
+                                          f32x16 (&sc)[2], f32x16 (&sn)[2], vec8<E> (&kf)[8],
                                           bool next, int kh_next, const Cols& c) {
   // ---- phase A: weights of this half || scores of the next half ----------
   // All eight K fragments of the half tile, then the first PV step's V^T
   // fragments, are read up front: with one wave per SIMD nothing else hides
   // LDS latency, so each MFMA waits only for its own fragment.
   const char* vbuf = lds + VS * kSlot + kTileK;
-  bf16x8 va[4];
-  bf16x8 p[2][2];
+  vec8<E> va[4];
+  vec8<E> p[2][2];
   {
     // kf: this half tile's K fragments (K slot KS, half KH), read during the
     // previous half step
 #pragma unroll
-    for (int dd = 0; dd < 4; ++dd) va[dd] = rd(vbuf + dd * 4096 + voff[2 * VH]);
+    for (int dd = 0; dd < 4; ++dd) va[dd] = rd<E>(vbuf + dd * 4096 + voff[2 * VH]);
     sn[0] = st.negm[0];  // the chains start from -m_ref: no separate subtraction
     sn[1] = st.negm[1];
 #pragma unroll
@@ -218,7 +228,7 @@ __device__ __forceinline__ void half_step(const char* lds, const int (&koff)[8],
       sn[0] = mfma32(kf[kk], st.qf[0][kk], sn[0]);
       if ((kk & 1) == 0) {
         const int g = kk >> 1;  // weight group: cb = g >> 1, jj = g & 1
-        p[g >> 1][g & 1] = weights(sc[g >> 1], g & 1);
+        p[g >> 1][g & 1] = weights<E>(sc[g >> 1], g & 1);
       }
       sn[1] = mfma32(kf[kk], st.qf[1][kk], sn[1]);
       __builtin_amdgcn_sched_barrier(0);
@@ -229,7 +239,7 @@ __device__ __forceinline__ void half_step(const char* lds, const int (&koff)[8],
   // the weights were just written by VALU code; the inline-asm MFMAs below
   // read them, and the compiler does not count wait states for inline asm
   asm volatile("s_nop 1");
-  bf16x8 vn[4];
+  vec8<E> vn[4];
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
     __builtin_amdgcn_sched_barrier(0);
@@ -241,10 +251,10 @@ __device__ __forceinline__ void half_step(const char* lds, const int (&koff)[8],
         // the second PV step's fragments, and the next half step's K
         // fragments (K slot KSN, half KHN), behind the first MFMAs
 #pragma unroll
-        for (int d2 = 0; d2 < 4; ++d2) vn[d2] = rd(vbuf + d2 * 4096 + voff[2 * VH + 1]);
+        for (int d2 = 0; d2 < 4; ++d2) vn[d2] = rd<E>(vbuf + d2 * 4096 + voff[2 * VH + 1]);
         const char* knext = lds + KSN * kSlot + KHN * 8192;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) kf[kk] = rd(knext + koff[kk]);
+        for (int kk = 0; kk < 8; ++kk) kf[kk] = rd<E>(knext + koff[kk]);
       }
     }
     add_denominator(p[0][jj], st.l_part[0]);
@@ -261,7 +271,8 @@ __device__ __forceinline__ void half_step(const char* lds, const int (&koff)[8],
 // Scores-only pass over the block's tiles (k_hat images only, both K slots):
 // the exact max of every column, in the log2 domain, reduced over the lane
 // pair.  Run only for blocks whose fixed reference proved too low.
-__device__ __forceinline__ void max_pass(char* lds, const int (&koff)[8], const WaveState& st,
+template <typename E>
+__device__ __forceinline__ void max_pass(char* lds, const int (&koff)[8], const WaveState<E>& st,
                                          const char* kimg, int kt_lo, int n_tiles, int tid,
                                          int wave_u, const Cols& c, float (&mx)[2]) {
   mx[0] = mx[1] = -INFINITY;
@@ -304,10 +315,10 @@ __device__ __forceinline__ void max_pass(char* lds, const int (&koff)[8], const 
 // tile's first half (slot SN).  After the last tile that second step still
 // runs its MFMAs on whatever slot SN holds (nothing copies into it then) and
 // ignores the result, which keeps a single code path.
-template <int SL, int SN>
+template <int SL, int SN, typename E>
 __device__ __forceinline__ void tile_steps(const char* lds, const int (&koff)[8],
-                                           const int (&voff)[4], WaveState& st,
-                                           f32x16 (&sA)[2], f32x16 (&sB)[2], bf16x8 (&kf)[8],
+                                           const int (&voff)[4], WaveState<E>& st,
+                                           f32x16 (&sA)[2], f32x16 (&sB)[2], vec8<E> (&kf)[8],
                                            int kt, bool has_next_tile, const Cols& c) {
   half_step<SL, 0, SL, 1, SN, 0>(lds, koff, voff, st, sA, sB, kf, true, kt + 32, c);
   half_step<SL, 1, SN, 0, SN, 1>(lds, koff, voff, st, sB, sA, kf, has_next_tile,
@@ -318,8 +329,9 @@ __device__ __forceinline__ void tile_steps(const char* lds, const int (&koff)[8]
 // Tile j sits in LDS slot j % 3.  At the top of tile j every wave is done with
 // tile j - 1, whose slot then takes tile j + 2; tile j + 1 (needed halfway
 // through tile j) was copied during tile j - 1, so one barrier per tile.
+template <typename E>
 __device__ __forceinline__ void attend_pass(char* lds, const int (&koff)[8], const int (&voff)[4],
-                                            WaveState& st, const char* kimg, const char* vimg,
+                                            WaveState<E>& st, const char* kimg, const char* vimg,
                                             int kt_lo, int n_tiles, int tid, int wave_u,
                                             const Cols& c, bool copies_issued) {
   auto kimg_at = [&](int j) { return kimg + (size_t)(kt_lo + j * kKeyTile) * 256; };
@@ -339,9 +351,9 @@ __device__ __forceinline__ void attend_pass(char* lds, const int (&koff)[8], con
   __syncthreads();
   score_half<0, 0>(lds, koff, st, sA);
   if (!half_full(kt_lo, c)) mask_half(kt_lo, c, sA);
-  bf16x8 kf[8];  // K fragments of the next half tile to score (slot 0, half 1)
+  vec8<E> kf[8];  // K fragments of the next half tile to score (slot 0, half 1)
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) kf[kk] = rd(lds + 8192 + koff[kk]);
+  for (int kk = 0; kk < 8; ++kk) kf[kk] = rd<E>(lds + 8192 + koff[kk]);
 
   for (int j = 0; j < n_tiles;) {
 #pragma unroll
@@ -367,12 +379,12 @@ __device__ __forceinline__ void attend_pass(char* lds, const int (&koff)[8], con
 // denominators left the safe range marks itself in redo[] and writes nothing.
 // EXACT = true: the follow-up launch; only marked blocks run, with the exact
 // row max found by a scores-only pass first.
-template <bool EXACT>
+template <bool EXACT, typename E>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_wide_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ khat,
-    const bf16* __restrict__ vt, const int32_t* __restrict__ cu,
+    const E* __restrict__ q, const E* __restrict__ khat,
+    const E* __restrict__ vt, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ cu_end, const int32_t* __restrict__ sched, const float* __restrict__ sinks,
-    const float* __restrict__ qnorm_w, bf16* __restrict__ out, float* __restrict__ lse,
+    const float* __restrict__ qnorm_w, E* __restrict__ out, float* __restrict__ lse,
     int32_t* __restrict__ redo, int T, int Hq, int Hkv, int G, int log2G, int64_t t_pad,
     int window, int use_rope, float eps, double theta, float c_log2, int xcd_per,
     int exact_all) {
@@ -445,20 +457,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_wide_kernel(
   if (tid == 0) s_bad = 0;
   __syncthreads();
 
-  WaveState st;
+  WaveState<E> st;
   float sink_raw[2], self_score[2];
-  // ---- Q: load, RMSNorm, RoPE, scale, round to bf16 B operands ------------
+  // ---- Q: load, RMSNorm, RoPE, scale, round to E B operands ---------------
   // lane holds channels 16kk + 8hf + e (kk < 8, e < 8) of its columns; NeoX
   // partners i and i + 64 (kk and kk + 4) sit in the same lane.  The global
   // loads go out before the first tiles' copies: vmcnt retires in order, so
   // waiting for them then does not wait for the copies.
   {
-    bf16x8 qraw[2][8], kself[2][8];
+    vec8<E> qraw[2][8], kself[2][8];
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      const bf16* qp = q + ((size_t)(c.ok[cb] ? c.tok[cb] : a) * Hq + hq[cb]) * kHeadDim + 8 * hf;
+      const E* qp = q + ((size_t)(c.ok[cb] ? c.tok[cb] : a) * Hq + hq[cb]) * kHeadDim + 8 * hf;
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) qraw[cb][kk] = *reinterpret_cast<const bf16x8*>(qp + 16 * kk);
+      for (int kk = 0; kk < 8; ++kk) qraw[cb][kk] = *reinterpret_cast<const vec8<E>*>(qp + 16 * kk);
     }
     float w[64];
 #pragma unroll
@@ -475,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_wide_kernel(
         const char* kp = kimg + (size_t)ts * 256;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
-          kself[cb][kk] = *reinterpret_cast<const bf16x8*>(kp + (((2 * kk + hf) ^ (ts & 15)) << 4));
+          kself[cb][kk] = *reinterpret_cast<const vec8<E>*>(kp + (((2 * kk + hf) ^ (ts & 15)) << 4));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -520,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_wide_kernel(
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st.qf[cb][kk][e] = (bf16)(x[8 * kk + e] * c_log2);
+        for (int e = 0; e < 8; ++e) st.qf[cb][kk][e] = (E)(x[8 * kk + e] * c_log2);
         // park the Q operands in AGPRs (MFMAs read them from there), which
         // leaves the VGPRs to the scores, weights and operand prefetch
         asm volatile("" : "+a"(st.qf[cb][kk]));
@@ -543,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_wide_kernel(
 #pragma unroll
   for (int j = 0; j < 4; ++j) voff[j] = col * 128 + (((2 * j + hf) ^ vswz(col)) << 4);
 
-  // ---- references (log2 domain, bf16-representable) ------------------------
+  // ---- references (log2 domain) ---------------------------------------------
   // main launch: max(sink, the token's own score); follow-up: the exact row max
   float mref[2];
   if (EXACT) {
@@ -564,9 +576,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_wide_kernel(
     for (int r = 0; r < 16; ++r) st.negm[cb][r] = -st.m_ref[cb];
   }
   {
-    bf16x8 zero;
+    vec8<E> zero;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) zero[e] = (bf16)0.f;
+    for (int e = 0; e < 8; ++e) zero[e] = (E)0.f;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
@@ -575,7 +587,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_wide_kernel(
 
   attend_pass(lds, koff, voff, st, kimg, vimg, kt_lo, n_tiles, tid, wave_u, c, !EXACT);
 
-  // ---- epilogue: out = O / l in bf16, lse = ln2 * (m + log2 l) -------------
+  // ---- epilogue: out = O / l in E, lse = ln2 * (m + log2 l) ----------------
   float l[2];
   bool bad = false;
 #pragma unroll
@@ -597,15 +609,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_wide_kernel(
   for (int cb = 0; cb < 2; ++cb) {
     if (c.ok[cb]) {
       const float inv_l = 1.0f / l[cb];
-      bf16* op = out + ((size_t)c.tok[cb] * Hq + hq[cb]) * kHeadDim + 4 * hf;
+      E* op = out + ((size_t)c.tok[cb] * Hq + hq[cb]) * kHeadDim + 4 * hf;
 #pragma unroll
       for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          bf16x4 w;
+          vec4<E> w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (bf16)(st.o[cb][dd][4 * rq + e] * inv_l);
-          *reinterpret_cast<bf16x4*>(op + 32 * dd + 8 * rq) = w;
+          for (int e = 0; e < 4; ++e) w[e] = (E)(st.o[cb][dd][4 * rq + e] * inv_l);
+          *reinterpret_cast<vec4<E>*>(op + 32 * dd + 8 * rq) = w;
         }
       if (lse != nullptr && hf == 0)
         lse[(size_t)hq[cb] * T + c.tok[cb]] = (st.m_ref[cb] + __log2f(l[cb])) * kLn2;
@@ -615,10 +627,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_wide_kernel(
 
 }  // namespace
 
-hipError_t launch_attention_bf16_wide(const bf16* q, const bf16* khat, const bf16* vt,
+template <typename E>
+hipError_t launch_attention_bf16_wide(const E* q, const E* khat, const E* vt,
                                       const int32_t* cu, const int32_t* cu_end,
                                       const int32_t* sched,
-                                      const float* sinks, const float* qnorm_w, bf16* out,
+                                      const float* sinks, const float* qnorm_w, E* out,
                                       float* lse, int32_t* redo, int T, int D, int Hq,
                                       int Hkv, int64_t t_pad, int64_t items_ub, int window,
                                       int use_rope, double eps, double theta, double scale,
@@ -634,13 +647,22 @@ hipError_t launch_attention_bf16_wide(const bf16* q, const bf16* khat, const bf1
   if (grid <= 0) return hipSuccess;
   const float c_log2 = (float)(scale * 1.4426950408889634);
   // main launch, then the follow-up that reruns the blocks it marked
-  attn_fwd_bf16_wide_kernel<false><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+  attn_fwd_bf16_wide_kernel<false, E><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
       q, khat, vt, cu, cu_end, sched, sinks, qnorm_w, out, lse, redo, T, Hq, Hkv, G, log2G, t_pad,
       window, use_rope, (float)eps, theta, c_log2, xcd_per, exact_all ? 1 : 0);
-  attn_fwd_bf16_wide_kernel<true><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+  attn_fwd_bf16_wide_kernel<true, E><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
       q, khat, vt, cu, cu_end, sched, sinks, qnorm_w, out, lse, redo, T, Hq, Hkv, G, log2G, t_pad,
       window, use_rope, (float)eps, theta, c_log2, xcd_per, 0);
   return hipGetLastError();
 }
+
+#define SA_INSTANTIATE(E)                                                                     \
+  template hipError_t launch_attention_bf16_wide<E>(                                          \
+      const E*, const E*, const E*, const int32_t*, const int32_t*, const int32_t*,           \
+      const float*, const float*, E*, float*, int32_t*, int, int, int, int, int64_t, int64_t, \
+      int, int, double, double, double, bool, hipStream_t);
+SA_INSTANTIATE(bf16)
+SA_INSTANTIATE(f16)
+#undef SA_INSTANTIATE
 
 }  // namespace sa

@@ -1,5 +1,6 @@
-// bwd_bf16.hip -- backward pass of the sink-aware GQA attention, bf16 in/out,
-// gfx950 MFMA.
+// bwd_bf16.hip -- backward pass of the sink-aware GQA attention, 16-bit in/out
+// (bf16, or fp16 for the fp16 I/O variant: the kernels are templates over the
+// element type E), gfx950 MFMA.
 //
 // Gradients of L = sum(dout * out) for the forward of attn_bf16*.hip
 // (flint.layers FlintAttention: the sinks are trainable fp32 logits,
@@ -12,16 +13,17 @@
 //   dx = w dy r - x r^3 (sum_c w_c dy_c x_c) / d,  dw += dy x r,  r = (mean(x^2)+eps)^-1/2.
 //
 // Kernels (one launch each, in this order):
-//   bwd_keys_kernel    per 64-key tile: k_hat, the raw V rows and K^T as LDS
-//                      tile images (the forward prologue's formats)
+//   bwd_keys_kernel    per 64-key tile: k_hat rows and V rows as LDS row
+//                      images
 //   bwd_cols_kernel    per 32-column tile (32/G tokens x the G heads of one kv
-//                      head): q_hat * scale * log2(e) and dout as row images
-//                      and transposed images, -lse*log2(e) and -D per column,
-//                      and the tile's share of dsink
+//                      head): q_hat * scale * log2(e) and dout as row images,
+//                      -lse*log2(e) and -D per column, and the tile's share of
+//                      dsink
 //   bwd_dkdv_kernel    per 128-key block (a wave holds 32 keys' K and V rows
 //                      as MFMA operands): walks the column tiles that see the
 //                      keys; S = q K^T, P, dP - D = dout V^T - D, dS; dV^T +=
-//                      dout^T P, dK^T += q^T dS (AGPR accumulators); epilogue:
+//                      dout^T P, dK^T += q^T dS (AGPR accumulators, the
+//                      transposed operands by LDS transpose reads); epilogue:
 //                      dv, and dk through the rotation and norm backward
 //   bwd_dq_kernel      per 256-column block (8 waves of 32 columns): walks the
 //                      key tiles the columns see; S^T = K q^T, P^T, dP^T - D,
@@ -32,9 +34,8 @@
 // MFMA operand layouts (32x32x16, wave64): A lane l holds A[l%32][8(l/32)..+7],
 // B lane l holds B[8(l/32)..+7][l%32], accumulator register r of lane l is
 // C[8(r/4) + 4(l/32) + r%4][l%32].  A 16-step of an accumulator taken as an
-// operand (registers 8j..8j+7) covers rows 16j + 8(e/4) + 4(l/32) + e%4; the
-// transposed images store their 16-groups in that order, so every operand is
-// one 16-byte LDS read.
+// operand (registers 8j..8j+7) covers rows 16j + 8(e/4) + 4(l/32) + e%4, which
+// is the order the transpose reads deliver the rows of a row image in.
 #include "sa_device.h"
 
 namespace sa {
@@ -45,11 +46,10 @@ constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 // ---- workspace images ------------------------------------------------------
-// Row images only: 256-byte rows of 128 bf16 channels, 16-byte chunk c of
+// Row images only: 256-byte rows of 128 16-bit channels, 16-byte chunk c of
 // row r at chunk position c ^ bswz(r).  MFMA operands that run over the rows
 // (the transposed products) come from the same images through the LDS
 // transpose read.
@@ -83,27 +83,37 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 // accumulation into AGPR-resident accumulators (see attn_bf16_wide.hip)
-__device__ __forceinline__ void mfma32_acc(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+template <typename E>
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, vec8<E> a, vec8<E> b) {
+  if constexpr (is_f16<E>)
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 // The same with the two wait states a VALU write of a or b needs before an
 // MFMA reads it (the first use of an operand just converted from scores).
-__device__ __forceinline__ void mfma32_acc_nop(f32x16& acc, bf16x8 a, bf16x8 b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+template <typename E>
+__device__ __forceinline__ void mfma32_acc_nop(f32x16& acc, vec8<E> a, vec8<E> b) {
+  if constexpr (is_f16<E>)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
-__device__ __forceinline__ void zero_acc(f32x16& acc, bf16x8 zero) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero));
+template <typename E>
+__device__ __forceinline__ void zero_acc(f32x16& acc, vec8<E> zero) {
+  if constexpr (is_f16<E>)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero));
 }
 __device__ __forceinline__ void agpr_fence() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
-__device__ __forceinline__ bf16x8 rd(const char* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
+template <typename E>
+__device__ __forceinline__ vec8<E> rd(const char* p) {
+  return *reinterpret_cast<const vec8<E>*>(p);
 }
 
 // Chunk swizzle of the backward's row images.  Rows are 256 B, so every row
@@ -117,16 +127,17 @@ __device__ __forceinline__ int bswz(int r) { return ((r & 3) << 2) | ((r >> 2) &
 // LDS transpose read (ds_read_b64_tr_b16): in every group of 16 lanes, lane
 // 4a + b receives, as its elements 0..3, element b of the 8 bytes read by
 // lanes a, a + 4, a + 8 and a + 12 of the group.  Two such reads make one
-// MFMA operand of 8 bf16.
+// MFMA operand of 8 16-bit elements.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) char lds_char;
-__device__ __forceinline__ bf16x8 rd_tr(const char* p0, const char* p1) {
+template <typename E>
+__device__ __forceinline__ vec8<E> rd_tr(const char* p0, const char* p1) {
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_char*)p0);
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_char*)p1);
   const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
+  return __builtin_bit_cast(vec8<E>, v);
 }
 
 // Per-lane offsets of the transpose reads for an A operand A[m][k] with
@@ -225,11 +236,12 @@ __device__ __forceinline__ int first_key(const int32_t* __restrict__ cu, int D, 
 // document position (rope only).  ok: the row is a real token (a padding row
 // may hold anything and gets a zero gradient).  Writes dx (zero when !ok) to
 // dxp when store, and dy x r (zero when !ok) to wsum in dy's order.
-__device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const bf16* __restrict__ xp,
+template <typename E>
+__device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const E* __restrict__ xp,
                                               const float* __restrict__ w, bool ok, bool store,
                                               bool rope,
                                               int pos, const double* s_invf, float eps, int hf,
-                                              bf16* __restrict__ dxp, float (&wsum)[64]) {
+                                              E* __restrict__ dxp, float (&wsum)[64]) {
   if (rope && ok) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {  // channel 32dd + 8rq + 4hf + e (dd < 2), partner + 64
@@ -246,7 +258,7 @@ __device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const bf16* __res
   for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const bf16x4 xv = *reinterpret_cast<const bf16x4*>(xp + 32 * dd + 8 * rq);
+      const vec4<E> xv = *reinterpret_cast<const vec4<E>*>(xp + 32 * dd + 8 * rq);
       const f32x4 wv = *reinterpret_cast<const f32x4*>(w + 32 * dd + 8 * rq + 4 * hf);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -263,24 +275,25 @@ __device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const bf16* __res
   for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const bf16x4 xv = *reinterpret_cast<const bf16x4*>(xp + 32 * dd + 8 * rq);
+      const vec4<E> xv = *reinterpret_cast<const vec4<E>*>(xp + 32 * dd + 8 * rq);
       const f32x4 wv = *reinterpret_cast<const f32x4*>(w + 32 * dd + 8 * rq + 4 * hf);
-      bf16x4 o;
+      vec4<E> o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float x = ok ? (float)xv[e] : 0.f, g = dy[16 * dd + 4 * rq + e];
-        o[e] = (bf16)(ok ? wv[e] * g * r - x * coef : 0.f);
+        o[e] = (E)(ok ? wv[e] * g * r - x * coef : 0.f);
         wsum[16 * dd + 4 * rq + e] = g * x * r;
       }
-      if (store) *reinterpret_cast<bf16x4*>(dxp + 32 * dd + 8 * rq) = o;
+      if (store) *reinterpret_cast<vec4<E>*>(dxp + 32 * dd + 8 * rq) = o;
     }
 }
 
 // ============================================================================
 // bwd_keys_kernel: one block per (64-key tile, kv head)
 // ============================================================================
+template <typename E>
 __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
-    const bf16* __restrict__ k, const bf16* __restrict__ v, const int32_t* __restrict__ cu,
+    const E* __restrict__ k, const E* __restrict__ v, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ cu_end, const float* __restrict__ knorm_w, int T, int D,
     int Hkv, int n_kt, float eps, double theta, int use_rope, char* __restrict__ keys) {
   __shared__ double s_invf[64];
@@ -311,9 +324,9 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
     const bool real = s_real[r];
     float x[16];
     if (real) {
-      const bf16* kp = k + ((size_t)t * Hkv + g) * kHeadDim;
-      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(kp + 8 * c);
-      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(kp + 64 + 8 * c);
+      const E* kp = k + ((size_t)t * Hkv + g) * kHeadDim;
+      const vec8<E> lo = *reinterpret_cast<const vec8<E>*>(kp + 8 * c);
+      const vec8<E> hi = *reinterpret_cast<const vec8<E>*>(kp + 64 + 8 * c);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         x[e] = (float)lo[e];
@@ -346,22 +359,23 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
         x[8 + e] = b * cs + a * sn;
       }
     }
-    bf16x8 lo, hi;
+    vec8<E> lo, hi;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      lo[e] = (bf16)x[e];
-      hi[e] = (bf16)x[8 + e];
+      lo[e] = (E)x[e];
+      hi[e] = (E)x[8 + e];
     }
-    *reinterpret_cast<bf16x8*>(img + r * 256 + 16 * (c ^ bswz(r))) = lo;
-    *reinterpret_cast<bf16x8*>(img + r * 256 + 16 * ((c + 8) ^ bswz(r))) = hi;
+    *reinterpret_cast<vec8<E>*>(img + r * 256 + 16 * (c ^ bswz(r))) = lo;
+    *reinterpret_cast<vec8<E>*>(img + r * 256 + 16 * ((c + 8) ^ bswz(r))) = hi;
   }
 }
 
 // ============================================================================
 // bwd_cols_kernel: one block per (32-column tile, kv head)
 // ============================================================================
+template <typename E>
 __global__ __launch_bounds__(kThreads) void bwd_cols_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ out, const bf16* __restrict__ dout,
+    const E* __restrict__ q, const E* __restrict__ out, const E* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ sinks,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_end,
     const float* __restrict__ qnorm_w, int T, int D, int Hq,
@@ -386,12 +400,12 @@ __global__ __launch_bounds__(kThreads) void bwd_cols_kernel(
   float x[16], y[16], o[16];
   if (ok) {
     const size_t row = ((size_t)t * Hq + h) * kHeadDim;
-    const bf16x8 ql = *reinterpret_cast<const bf16x8*>(q + row + 8 * c);
-    const bf16x8 qh = *reinterpret_cast<const bf16x8*>(q + row + 64 + 8 * c);
-    const bf16x8 dl = *reinterpret_cast<const bf16x8*>(dout + row + 8 * c);
-    const bf16x8 dh = *reinterpret_cast<const bf16x8*>(dout + row + 64 + 8 * c);
-    const bf16x8 ol = *reinterpret_cast<const bf16x8*>(out + row + 8 * c);
-    const bf16x8 oh = *reinterpret_cast<const bf16x8*>(out + row + 64 + 8 * c);
+    const vec8<E> ql = *reinterpret_cast<const vec8<E>*>(q + row + 8 * c);
+    const vec8<E> qh = *reinterpret_cast<const vec8<E>*>(q + row + 64 + 8 * c);
+    const vec8<E> dl = *reinterpret_cast<const vec8<E>*>(dout + row + 8 * c);
+    const vec8<E> dh = *reinterpret_cast<const vec8<E>*>(dout + row + 64 + 8 * c);
+    const vec8<E> ol = *reinterpret_cast<const vec8<E>*>(out + row + 8 * c);
+    const vec8<E> oh = *reinterpret_cast<const vec8<E>*>(out + row + 64 + 8 * c);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       x[e] = (float)ql[e];
@@ -434,19 +448,19 @@ __global__ __launch_bounds__(kThreads) void bwd_cols_kernel(
       x[8 + e] = b * cs + a * sn;
     }
   }
-  bf16x8 ql, qh, dl, dh;
+  vec8<E> ql, qh, dl, dh;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    ql[e] = (bf16)(x[e] * c_log2);
-    qh[e] = (bf16)(x[8 + e] * c_log2);
-    dl[e] = (bf16)y[e];
-    dh[e] = (bf16)y[8 + e];
+    ql[e] = (E)(x[e] * c_log2);
+    qh[e] = (E)(x[8 + e] * c_log2);
+    dl[e] = (E)y[e];
+    dh[e] = (E)y[8 + e];
   }
   // row images
-  *reinterpret_cast<bf16x8*>(img + col * 256 + 16 * (c ^ bswz(col))) = ql;
-  *reinterpret_cast<bf16x8*>(img + col * 256 + 16 * ((c + 8) ^ bswz(col))) = qh;
-  *reinterpret_cast<bf16x8*>(img + kCT + col * 256 + 16 * (c ^ bswz(col))) = dl;
-  *reinterpret_cast<bf16x8*>(img + kCT + col * 256 + 16 * ((c + 8) ^ bswz(col))) = dh;
+  *reinterpret_cast<vec8<E>*>(img + col * 256 + 16 * (c ^ bswz(col))) = ql;
+  *reinterpret_cast<vec8<E>*>(img + col * 256 + 16 * ((c + 8) ^ bswz(col))) = qh;
+  *reinterpret_cast<vec8<E>*>(img + kCT + col * 256 + 16 * (c ^ bswz(col))) = dl;
+  *reinterpret_cast<vec8<E>*>(img + kCT + col * 256 + 16 * ((c + 8) ^ bswz(col))) = dh;
   // per column: -lse*log2e, -D, and the sink's share -p_sink * D
   if (c == 0) {
     float* ld = reinterpret_cast<float*>(img + kColLd);
@@ -467,12 +481,13 @@ __global__ __launch_bounds__(kThreads) void bwd_cols_kernel(
 // ============================================================================
 // bwd_dkdv_kernel: one block per (128-key block, kv head); 4 waves, one per SIMD
 // ============================================================================
+template <typename E>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
-    const bf16* __restrict__ k, const char* __restrict__ keys, const char* __restrict__ cols,
+    const E* __restrict__ k, const char* __restrict__ keys, const char* __restrict__ cols,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_end,
     const float* __restrict__ knorm_w, int T, int D, int Hkv,
     int log2G, int n_kt, int n_ct, int window, int use_rope, float eps, double theta,
-    bf16* __restrict__ dk, bf16* __restrict__ dv, float* __restrict__ dwk_part) {
+    E* __restrict__ dk, E* __restrict__ dv, float* __restrict__ dwk_part) {
   // the ring: one array per slot, so that the compiler can tell a copy into
   // one slot from reads of another (with one array and computed offsets it
   // waits for every copy in flight before reading)
@@ -522,15 +537,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const char* ctiles = cols + (size_t)g * n_ct * kColTileBytes;
 
   // K and V rows of this lane's key as B operands (channels 16kk + 8hf ..)
-  bf16x8 kB[8], vB[8];
+  vec8<E> kB[8], vB[8];
   {
     const char* kimg = keys + ((size_t)g * n_kt + (uc >> 6)) * kKeyTileBytes;
     const int r = uc & 63;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int pos = ((2 * kk + hf) ^ bswz(r)) << 4;
-      kB[kk] = rd(kimg + r * 256 + pos);
-      vB[kk] = rd(kimg + kKT + r * 256 + pos);
+      kB[kk] = rd<E>(kimg + r * 256 + pos);
+      vB[kk] = rd<E>(kimg + kKT + r * 256 + pos);
     }
     // land them before the tile copies start (a later wait would drain those)
 #pragma unroll
@@ -538,9 +553,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   }
   f32x16 acc_dv[4], acc_dk[4];
   {
-    bf16x8 zero;
+    vec8<E> zero;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) zero[e] = (bf16)0.f;
+    for (int e = 0; e < 8; ++e) zero[e] = (E)0.f;
 #pragma unroll
     for (int dd = 0; dd < 4; ++dd) {
       zero_acc(acc_dv[dd], zero);
@@ -603,14 +618,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     }
   };
   // elements 2m, 2m + 1 of P and dS = P (dP - D), packed as B operands
-  auto grads2 = [&](int m, const f32x16& s, const f32x16& dp, bf16x8 (&pb)[2],
-                    bf16x8 (&sb)[2]) {
+  auto grads2 = [&](int m, const f32x16& s, const f32x16& dp, vec8<E> (&pb)[2],
+                    vec8<E> (&sb)[2]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int e = 2 * m + h;
       const float p = __builtin_amdgcn_exp2f(s[e]);
-      pb[e >> 3][e & 7] = (bf16)p;
-      sb[e >> 3][e & 7] = (bf16)(p * dp[e]);
+      pb[e >> 3][e & 7] = (E)p;
+      sb[e >> 3][e & 7] = (E)(p * dp[e]);
     }
   };
   // scores of the tile in nbuf (into s_n, dp_n) while P and dS of the
@@ -623,19 +638,19 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     // nbuf), k >= 8 the products of the finished tile (dout^T and q^T of
     // cbuf); the operands of pair k are read kReadAhead pairs earlier
     constexpr int kReadAhead = 3;
-    auto operands = [&](int k, bf16x8& x, bf16x8& y) {
+    auto operands = [&](int k, vec8<E>& x, vec8<E>& y) {
       if (k < 8) {
-        x = rd(nbuf + roff[k]);
-        y = rd(nbuf + kCT + roff[k]);
+        x = rd<E>(nbuf + roff[k]);
+        y = rd<E>(nbuf + kCT + roff[k]);
       } else {
         // step m = 2 dd + j: dout^T and q^T for channels 32 dd.., columns 16 j..
         const int m = k - 8, dd = m >> 1, j = m & 1;
-        x = rd_tr(cbuf + kCT + 4096 * j + toff[dd][0], cbuf + kCT + 4096 * j + toff[dd][1]);
-        y = rd_tr(cbuf + 4096 * j + toff[dd][0], cbuf + 4096 * j + toff[dd][1]);
+        x = rd_tr<E>(cbuf + kCT + 4096 * j + toff[dd][0], cbuf + kCT + 4096 * j + toff[dd][1]);
+        y = rd_tr<E>(cbuf + 4096 * j + toff[dd][0], cbuf + 4096 * j + toff[dd][1]);
       }
     };
-    bf16x8 pb[2], sb[2];
-    bf16x8 ox[16], oy[16];
+    vec8<E> pb[2], sb[2];
+    vec8<E> ox[16], oy[16];
     if (has_next) init_scores(nbuf, s_n, dp_n);
 #pragma unroll
     for (int k = 0; k < kReadAhead; ++k)
@@ -676,12 +691,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   wait_vmcnt<(kColBufs - 2) * kColCopyOps>();  // tile 0 landed
   barrier_keep_copies();
   {
-    bf16x8 qa[8], da[8];
+    vec8<E> qa[8], da[8];
     init_scores(slot(0), sx[0], dpx[0]);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      qa[kk] = rd(slot(0) + roff[kk]);
-      da[kk] = rd(slot(0) + kCT + roff[kk]);
+      qa[kk] = rd<E>(slot(0) + roff[kk]);
+      da[kk] = rd<E>(slot(0) + kCT + roff[kk]);
     }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
@@ -736,15 +751,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   // ---- epilogue: lane holds channels 32dd + 8(r/4) + 4hf + r%4 of key u ----
   // dv: the accumulation is the gradient
   if (u_ok) {
-    bf16* vp = dv + ((size_t)u * Hkv + g) * kHeadDim + 4 * hf;
+    E* vp = dv + ((size_t)u * Hkv + g) * kHeadDim + 4 * hf;
 #pragma unroll
     for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        bf16x4 w;
+        vec4<E> w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16)acc_dv[dd][4 * rq + e];
-        *reinterpret_cast<bf16x4*>(vp + 32 * dd + 8 * rq) = w;
+        for (int e = 0; e < 4; ++e) w[e] = (E)acc_dv[dd][4 * rq + e];
+        *reinterpret_cast<vec4<E>*>(vp + 32 * dd + 8 * rq) = w;
       }
   }
   // dk_hat = ln2 * acc (q was scaled by scale*log2e); rotate back; RMSNorm
@@ -790,12 +805,13 @@ constexpr int kKeyBufs = 4;  // ring of key tiles in LDS
 constexpr int kKeyCopyOps = kKeyTileBytes / (16 * kDqThreads);  // copies per wave per tile
 static_assert(kKeyCopyOps * (kKeyBufs - 2) < 64, "vmcnt holds 6 bits");
 
+template <typename E>
 __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
-    const bf16* __restrict__ q, const char* __restrict__ keys, const char* __restrict__ cols,
+    const E* __restrict__ q, const char* __restrict__ keys, const char* __restrict__ cols,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_end,
     const float* __restrict__ qnorm_w, int T, int D, int Hq,
     int Hkv, int G, int log2G, int n_kt, int n_ct, int window, int use_rope, float eps,
-    double theta, float scale, bf16* __restrict__ dq, float* __restrict__ dwq_part) {
+    double theta, float scale, E* __restrict__ dq, float* __restrict__ dwq_part) {
   // the ring of key tiles, one array per slot (see the dK/dV kernel)
   __shared__ __attribute__((aligned(1024))) char ring0[kKeyTileBytes];
   __shared__ __attribute__((aligned(1024))) char ring1[kKeyTileBytes];
@@ -826,7 +842,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
     real_span(cu, cu_end, D, qb * kDqWaves * tpt, min((qb + 1) * kDqWaves * tpt, T) - 1, a0, a1);
   if (a0 > a1) {
     if (t_in) {
-      bf16* dz = dq + ((size_t)t * Hq + h) * kHeadDim + 4 * hf;
+      E* dz = dq + ((size_t)t * Hq + h) * kHeadDim + 4 * hf;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         *reinterpret_cast<uint2*>(dz + 32 * (i >> 2) + 8 * (i & 3)) = make_uint2(0, 0);
@@ -852,7 +868,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
   const char* ktiles = keys + (size_t)g * n_kt * kKeyTileBytes;
 
   // q (scaled) and dout rows of this lane's column as B operands, -lse*log2e, -D
-  bf16x8 qB[8], dB[8];
+  vec8<E> qB[8], dB[8];
   float nlse = -INFINITY, nD = 0.f;
   {
     const int ctc = min(ct, n_ct - 1);
@@ -860,8 +876,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const int off = col * 256 + (((2 * kk + hf) ^ bswz(col)) << 4);
-      qB[kk] = rd(cimg + off);
-      dB[kk] = rd(cimg + kCT + off);
+      qB[kk] = rd<E>(cimg + off);
+      dB[kk] = rd<E>(cimg + kCT + off);
     }
     if (t_ok) {
       nlse = reinterpret_cast<const float*>(cimg + kColLd)[col];
@@ -874,9 +890,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
   }
   f32x16 acc[4];
   {
-    bf16x8 zero;
+    vec8<E> zero;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) zero[e] = (bf16)0.f;
+    for (int e = 0; e < 8; ++e) zero[e] = (E)0.f;
 #pragma unroll
     for (int dd = 0; dd < 4; ++dd) zero_acc(acc[dd], zero);
   }
@@ -916,8 +932,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
       f32x16 s = nl16, dp = nd16;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        s = mfma32(rd(buf + kh * 8192 + koff[kk]), qB[kk], s);
-        dp = mfma32(rd(buf + kKT + kh * 8192 + koff[kk]), dB[kk], dp);
+        s = mfma32(rd<E>(buf + kh * 8192 + koff[kk]), qB[kk], s);
+        dp = mfma32(rd<E>(buf + kKT + kh * 8192 + koff[kk]), dB[kk], dp);
       }
       if (!full) {
 #pragma unroll
@@ -926,12 +942,12 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
           s[r] += (key >= t_lo && key <= t) ? 0.f : -INFINITY;
         }
       }
-      bf16x8 sb[2];
+      vec8<E> sb[2];
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          sb[jj][e] = (bf16)(__builtin_amdgcn_exp2f(s[8 * jj + e]) * dp[8 * jj + e]);
+          sb[jj][e] = (E)(__builtin_amdgcn_exp2f(s[8 * jj + e]) * dp[8 * jj + e]);
       // dq^T[ch][col] += K^T[ch][key] dS^T[key][col]
 #pragma unroll
       for (int dd = 0; dd < 4; ++dd)
@@ -939,7 +955,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
         for (int jj = 0; jj < 2; ++jj) {
           // K^T for channels 32 dd.., keys 32 kh + 16 jj..
           const char* kt_rows = buf + 4096 * (2 * kh + jj);
-          const bf16x8 a = rd_tr(kt_rows + toff[dd][0], kt_rows + toff[dd][1]);
+          const vec8<E> a = rd_tr<E>(kt_rows + toff[dd][0], kt_rows + toff[dd][1]);
           if (dd == 0)
             mfma32_acc_nop(acc[dd], a, sb[jj]);
           else
@@ -1069,10 +1085,11 @@ BwdWorkspace plan_bwd_workspace(int64_t T, int64_t D, int Hq, int Hkv) {
   return w;
 }
 
-hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const int32_t* cu,
+template <typename E>
+hipError_t launch_bwd_bf16(const E* q, const E* k, const E* v, const int32_t* cu,
                            const int32_t* cu_end, const float* sinks, const float* qnorm_w, const float* knorm_w,
-                           const bf16* out, const float* lse, const bf16* dout, bf16* dq,
-                           bf16* dk, bf16* dv, float* dsinks, float* dqnorm_w,
+                           const E* out, const float* lse, const E* dout, E* dq,
+                           E* dk, E* dv, float* dsinks, float* dqnorm_w,
                            float* dknorm_w, int T, int D, int Hq, int Hkv, int window,
                            int use_rope, double eps, double theta, double scale, char* ws,
                            const BwdWorkspace& w, hipStream_t stream) {
@@ -1085,15 +1102,15 @@ hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const in
   float* dwq_part = reinterpret_cast<float*>(ws + w.dwq_off);
   float* dwk_part = reinterpret_cast<float*>(ws + w.dwk_off);
   const float c_log2 = (float)(scale * 1.4426950408889634);
-  bwd_keys_kernel<<<dim3((unsigned)(w.n_kt * Hkv)), dim3(kThreads), 0, stream>>>(
+  bwd_keys_kernel<E><<<dim3((unsigned)(w.n_kt * Hkv)), dim3(kThreads), 0, stream>>>(
       k, v, cu, cu_end, knorm_w, T, D, Hkv, (int)w.n_kt, (float)eps, theta, use_rope, keys);
-  bwd_cols_kernel<<<dim3((unsigned)(w.n_ct * Hkv)), dim3(kThreads), 0, stream>>>(
+  bwd_cols_kernel<E><<<dim3((unsigned)(w.n_ct * Hkv)), dim3(kThreads), 0, stream>>>(
       q, out, dout, lse, sinks, cu, cu_end, qnorm_w, T, D, Hq, Hkv, G, log2G, (int)w.n_ct, (float)eps,
       theta, use_rope, c_log2, cols, dsink_part);
-  bwd_dkdv_kernel<<<dim3((unsigned)w.n_kblk), dim3(kThreads), 0, stream>>>(
+  bwd_dkdv_kernel<E><<<dim3((unsigned)w.n_kblk), dim3(kThreads), 0, stream>>>(
       k, keys, cols, cu, cu_end, knorm_w, T, D, Hkv, log2G, (int)w.n_kt, (int)w.n_ct, window, use_rope,
       (float)eps, theta, dk, dv, dwk_part);
-  bwd_dq_kernel<<<dim3((unsigned)w.n_qblk), dim3(kDqThreads), 0, stream>>>(
+  bwd_dq_kernel<E><<<dim3((unsigned)w.n_qblk), dim3(kDqThreads), 0, stream>>>(
       q, keys, cols, cu, cu_end, qnorm_w, T, D, Hq, Hkv, G, log2G, (int)w.n_kt, (int)w.n_ct, window,
       use_rope, (float)eps, theta, (float)scale, dq, dwq_part);
   bwd_reduce_kernel<<<dim3(Hq + 2 * kHeadDim), dim3(kThreads), 0, stream>>>(
@@ -1101,5 +1118,15 @@ hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const in
       dsinks, dqnorm_w, dknorm_w);
   return hipGetLastError();
 }
+
+#define SA_INSTANTIATE(E)                                                                     \
+  template hipError_t launch_bwd_bf16<E>(                                                     \
+      const E*, const E*, const E*, const int32_t*, const int32_t*, const float*,             \
+      const float*, const float*, const E*, const float*, const E*, E*, E*, E*, float*,       \
+      float*, float*, int, int, int, int, int, int, double, double, double, char*,            \
+      const BwdWorkspace&, hipStream_t);
+SA_INSTANTIATE(bf16)
+SA_INSTANTIATE(f16)
+#undef SA_INSTANTIATE
 
 }  // namespace sa

@@ -1,6 +1,6 @@
 // prologue.hip -- first stage of the forward pass.
 //
-// bf16 path, one launch:
+// 16-bit path (bf16 or fp16 k, v and images; fp32 arithmetic), one launch:
 //   * blocks 0 and 1 build the varlen work schedules from cu_seqlens, one per
 //     attention tile configuration (query blocks of 128/G and 256/G tokens):
 //     the number of query blocks of every document, their exclusive prefix,
@@ -10,7 +10,8 @@
 //     head and
 //       - applies per-head RMSNorm and, when enabled, NeoX RoPE to K
 //         (flint.layers FlintAttention: q_norm / k_norm, _apply_rope; positions
-//         are document-local), writing k_hat bf16 [Hkv][t_pad][128];
+//         are document-local), writing k_hat [Hkv][t_pad][128] in the input's
+//         16-bit type;
 //       - writes V transposed, one [128][64] block per key tile (keys permuted
 //         inside groups of 16, see below) so the PV product reads its operand
 //         with one 16-byte LDS load.
@@ -83,12 +84,13 @@ __device__ void build_schedule(const int32_t* __restrict__ cu, const int32_t* __
   }
 }
 
+template <typename E>
 __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
-    const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const E* __restrict__ k, const E* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_end,
     const float* __restrict__ knorm_w, int T, int D,
     int Hkv, int64_t t_pad, int m_tok, int m_tok_wide, float eps, double theta,
-    int use_rope, bf16* __restrict__ khat, bf16* __restrict__ vt,
+    int use_rope, E* __restrict__ khat, E* __restrict__ vt,
     int32_t* __restrict__ sched, int32_t* __restrict__ sched_wide) {
   if (blockIdx.x < 2) {
     const bool wide = blockIdx.x == 1;
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
     return;
   }
   __shared__ double s_invf[64];
-  __shared__ __attribute__((aligned(16))) bf16 s_v[kKeyTile][kHeadDim + 8];
+  __shared__ __attribute__((aligned(16))) E s_v[kKeyTile][kHeadDim + 8];
 
   const int tid = threadIdx.x;
   const int blk = blockIdx.x - 2;
@@ -141,9 +143,9 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
     const bool real = s_real[tt];
     float x[16];
     if (real) {
-      const bf16* kp = k + ((size_t)t * Hkv + g) * kHeadDim;
-      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(kp + 8 * c);
-      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(kp + 64 + 8 * c);
+      const E* kp = k + ((size_t)t * Hkv + g) * kHeadDim;
+      const vec8<E> lo = *reinterpret_cast<const vec8<E>*>(kp + 8 * c);
+      const vec8<E> hi = *reinterpret_cast<const vec8<E>*>(kp + 64 + 8 * c);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         x[e] = (float)lo[e];
@@ -177,16 +179,16 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
         x[8 + e] = b * cs + a * sn;
       }
     }
-    bf16x8 lo, hi;
+    vec8<E> lo, hi;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      lo[e] = (bf16)x[e];
-      hi[e] = (bf16)x[8 + e];
+      lo[e] = (E)x[e];
+      hi[e] = (E)x[8 + e];
     }
     // row t of the tile image: chunk c at position c ^ kswz(t)
-    bf16* kh = khat + ((size_t)g * t_pad + t) * kHeadDim;
-    *reinterpret_cast<bf16x8*>(kh + 8 * (c ^ kswz(t))) = lo;
-    *reinterpret_cast<bf16x8*>(kh + 8 * ((c + 8) ^ kswz(t))) = hi;
+    E* kh = khat + ((size_t)g * t_pad + t) * kHeadDim;
+    *reinterpret_cast<vec8<E>*>(kh + 8 * (c ^ kswz(t))) = lo;
+    *reinterpret_cast<vec8<E>*>(kh + 8 * ((c + 8) ^ kswz(t))) = hi;
   }
 
   // V^T rows: lane (d, 8-position chunk) writes 16 contiguous bytes of row d.
@@ -198,13 +200,13 @@ __global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
     const int pidx = tid + kThreads * i;
     const int tc = pidx & 7, d = pidx >> 3;
     const int kbase16 = 16 * (tc >> 1) + 4 * (tc & 1);
-    bf16x8 col;
+    vec8<E> col;
 #pragma unroll
     for (int e = 0; e < 8; ++e) col[e] = s_v[kbase16 + 8 * (e >> 2) + (e & 3)][d];
     // tile-major image: tile (g, tile) is 128 rows x 64 keys, chunk tc of
     // row d at position tc ^ vswz(d)
-    bf16* vrow = vt + (((size_t)g * (t_pad / kKeyTile) + tile) * kHeadDim + d) * kKeyTile;
-    *reinterpret_cast<bf16x8*>(vrow + 8 * (tc ^ vswz(d))) = col;
+    E* vrow = vt + (((size_t)g * (t_pad / kKeyTile) + tile) * kHeadDim + d) * kKeyTile;
+    *reinterpret_cast<vec8<E>*>(vrow + 8 * (tc ^ vswz(d))) = col;
   }
 }
 
@@ -252,18 +254,28 @@ __global__ __launch_bounds__(kThreads) void prologue_f32_kernel(
 
 }  // namespace
 
-hipError_t launch_prologue_bf16(const bf16* k, const bf16* v, const int32_t* cu,
+template <typename E>
+hipError_t launch_prologue_bf16(const E* k, const E* v, const int32_t* cu,
                                 const int32_t* cu_end, const float* knorm_w, int T, int D, int Hkv,
                                 int64_t t_pad, int m_tok, int m_tok_wide, double eps,
-                                double theta, int use_rope, bf16* khat, bf16* vt,
+                                double theta, int use_rope, E* khat, E* vt,
                                 int32_t* sched, int32_t* sched_wide, hipStream_t stream) {
   const int64_t n_tiles = t_pad / kKeyTile;
   const int64_t grid = 2 + n_tiles * Hkv;
-  prologue_bf16_kernel<<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+  prologue_bf16_kernel<E><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
       k, v, cu, cu_end, knorm_w, T, D, Hkv, t_pad, m_tok, m_tok_wide, (float)eps, theta, use_rope,
       khat, vt, sched, sched_wide);
   return hipGetLastError();
 }
+
+#define SA_INSTANTIATE(E)                                                                    \
+  template hipError_t launch_prologue_bf16<E>(const E*, const E*, const int32_t*,            \
+                                              const int32_t*, const float*, int, int, int,   \
+                                              int64_t, int, int, double, double, int, E*, E*, \
+                                              int32_t*, int32_t*, hipStream_t);
+SA_INSTANTIATE(bf16)
+SA_INSTANTIATE(f16)
+#undef SA_INSTANTIATE
 
 hipError_t launch_prologue_f32(const float* k, const float* v, const int32_t* cu,
                                const int32_t* cu_end, const float* knorm_w, int T, int D, int Hkv, int d,

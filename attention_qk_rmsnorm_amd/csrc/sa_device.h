@@ -69,4 +69,30 @@ __device__ __forceinline__ float lane_pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ---- 16-bit element helpers (E = bf16 or f16) -----------------------------
+
+// C += A B on the 32x32x16 MFMA of the element type (fp32 accumulation).
+template <typename E>
+__device__ __forceinline__ f32x16 mfma32(vec8<E> a, vec8<E> b, f32x16 c) {
+  if constexpr (is_f16<E>) return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// c + a0 b0 + a1 b1 in fp32 (v_dot2_f32_{bf16,f16}).
+template <typename E>
+__device__ __forceinline__ float dot2(vec2<E> a, vec2<E> b, float c) {
+  if constexpr (is_f16<E>) return __builtin_amdgcn_fdot2(a, b, c, false);
+  else return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+// A softmax reference point (log2 domain) that E represents exactly, so an
+// MFMA step with E operands can subtract it without error.  fp16 tops out at
+// 65504: references are held within +-2^15 there (scores and sinks beyond
+// about 22,700 in natural-log units are outside the fp16 path's range).
+template <typename E>
+__device__ __forceinline__ float ref_round(float x) {
+  if constexpr (is_f16<E>) return (float)(E)fminf(fmaxf(x, -32768.f), 32768.f);
+  else return (float)(E)x;
+}
+
 }  // namespace sa

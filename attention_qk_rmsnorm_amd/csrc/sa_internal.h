@@ -9,8 +9,16 @@
 namespace sa {
 
 typedef __bf16 bf16;
+typedef _Float16 f16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+// The 16-bit paths are templates over the storage/operand element E: bf16
+// (__bf16) or fp16 (_Float16).  Both feed the same MFMA shape
+// (v_mfma_f32_32x32x16_{bf16,f16}) with fp32 accumulation.
+template <typename E> using vec8 = E __attribute__((ext_vector_type(8)));
+template <typename E> using vec4 = E __attribute__((ext_vector_type(4)));
+template <typename E> using vec2 = E __attribute__((ext_vector_type(2)));
+template <typename E> constexpr bool is_f16 = __is_same(E, _Float16);
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -88,33 +96,38 @@ hipError_t launch_pad_fill(const int32_t* starts, const int32_t* ends, int D, in
 
 // ---- launch wrappers (return hipGetLastError after the launches) ----------
 
-hipError_t launch_prologue_bf16(const bf16* k, const bf16* v, const int32_t* cu,
+// The 16-bit launch wrappers are instantiated for E = bf16 and E = f16.
+template <typename E>
+hipError_t launch_prologue_bf16(const E* k, const E* v, const int32_t* cu,
                                 const int32_t* cu_end, const float* knorm_w, int T, int D, int Hkv,
                                 int64_t t_pad, int m_tok, int m_tok_wide, double eps,
-                                double theta, int use_rope, bf16* khat, bf16* vt,
+                                double theta, int use_rope, E* khat, E* vt,
                                 int32_t* sched, int32_t* sched_wide, hipStream_t stream);
 
-hipError_t launch_attention_bf16(const bf16* q, const bf16* khat, const bf16* vt,
+template <typename E>
+hipError_t launch_attention_bf16(const E* q, const E* khat, const E* vt,
                                  const int32_t* cu, const int32_t* cu_end, const int32_t* sched,
-                                 const float* sinks, const float* qnorm_w, bf16* out,
+                                 const float* sinks, const float* qnorm_w, E* out,
                                  float* lse, int T, int D, int Hq, int Hkv,
                                  int64_t t_pad, int64_t items_ub, int window,
                                  int use_rope, double eps, double theta,
                                  double scale, hipStream_t stream);
 
-hipError_t launch_attention_bf16_wide(const bf16* q, const bf16* khat, const bf16* vt,
+template <typename E>
+hipError_t launch_attention_bf16_wide(const E* q, const E* khat, const E* vt,
                                       const int32_t* cu, const int32_t* cu_end,
                                       const int32_t* sched,
-                                      const float* sinks, const float* qnorm_w, bf16* out,
+                                      const float* sinks, const float* qnorm_w, E* out,
                                       float* lse, int32_t* redo, int T, int D, int Hq,
                                       int Hkv, int64_t t_pad, int64_t items_ub, int window,
                                       int use_rope, double eps, double theta, double scale,
                                       bool exact_all, hipStream_t stream);
 
-hipError_t launch_bwd_bf16(const bf16* q, const bf16* k, const bf16* v, const int32_t* cu,
+template <typename E>
+hipError_t launch_bwd_bf16(const E* q, const E* k, const E* v, const int32_t* cu,
                            const int32_t* cu_end, const float* sinks, const float* qnorm_w, const float* knorm_w,
-                           const bf16* out, const float* lse, const bf16* dout, bf16* dq,
-                           bf16* dk, bf16* dv, float* dsinks, float* dqnorm_w,
+                           const E* out, const float* lse, const E* dout, E* dq,
+                           E* dk, E* dv, float* dsinks, float* dqnorm_w,
                            float* dknorm_w, int T, int D, int Hq, int Hkv, int window,
                            int use_rope, double eps, double theta, double scale, char* ws,
                            const BwdWorkspace& w, hipStream_t stream);

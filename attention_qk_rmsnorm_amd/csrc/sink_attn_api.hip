@@ -16,7 +16,7 @@ Workspace plan_workspace(int64_t T, int64_t D, int Hq, int Hkv, int d, int dtype
   if (T <= 0) return w;
   w.t_pad = round_up(T, kKeyTile);
   size_t off = 0;
-  if (dtype == SINK_ATTN_BF16) {
+  if (dtype != SINK_ATTN_F32) {  // 16-bit (bf16 or fp16) images
     const int G = Hq / Hkv;
     w.items_ub = T / tokens_per_block(G) + D;
     w.items_ub_wide = T / tokens_per_block_wide(G) + D;
@@ -102,7 +102,7 @@ hipError_t launch_pad_fill(const int32_t* starts, const int32_t* ends, int D, in
                            hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   const unsigned grid = (unsigned)((T + kFillTokens - 1) / kFillTokens);
-  const size_t row_bytes = (size_t)Hq * d * (dtype == SINK_ATTN_BF16 ? 2 : 4);
+  const size_t row_bytes = (size_t)Hq * d * (dtype == SINK_ATTN_F32 ? 4 : 2);
   if (row_bytes % 16 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0)
     pad_fill_kernel<uint4><<<dim3(grid), dim3(256), 0, stream>>>(
         starts, ends, D, T, Hq, (int)(row_bytes / 16), sinks, static_cast<uint4*>(out), lse);
@@ -220,7 +220,7 @@ int check_desc(const sink_attn_desc* d) {
   if (!(d->rms_eps >= 0.0) || !isfinite(d->rms_eps)) return SINK_ATTN_EINVAL;
   if (!(d->rope_theta > 0.0) || !isfinite(d->rope_theta)) return SINK_ATTN_EINVAL;
   if (!isfinite(d->softmax_scale)) return SINK_ATTN_EINVAL;
-  if (d->dtype == SINK_ATTN_BF16) {
+  if (d->dtype == SINK_ATTN_BF16 || d->dtype == SINK_ATTN_F16) {
     if (d->head_dim != sa::kHeadDim) return SINK_ATTN_EUNSUPPORTED;
     const int G = d->num_q_heads / d->num_kv_heads;
     if (G > sa::kMaxGroup || (G & (G - 1)) != 0) return SINK_ATTN_EUNSUPPORTED;
@@ -239,14 +239,14 @@ int check_workspace(const sink_attn_desc* d, const sa::Workspace& w) {
   return SINK_ATTN_OK;
 }
 
-uintptr_t io_align(const sink_attn_desc* d) { return d->dtype == SINK_ATTN_BF16 ? 16 : 4; }
+uintptr_t io_align(const sink_attn_desc* d) { return d->dtype == SINK_ATTN_F32 ? 4 : 16; }
 
 sa::Workspace plan(const sink_attn_desc* d) {
   return sa::plan_workspace(d->total_tokens, d->num_docs, d->num_q_heads, d->num_kv_heads,
                             d->head_dim, d->dtype);
 }
 
-// bf16 tile configuration of a call.  Wide tiles (64 columns per wave, one
+// 16-bit tile configuration of a call.  Wide tiles (64 columns per wave, one
 // workgroup per CU, half the LDS operand traffic per MFMA) win once a query
 // block visits many key tiles; narrow ones (32 columns, two workgroups per
 // CU, shorter blocks) win on short documents and narrow windows.  The
@@ -295,6 +295,46 @@ int check_attention(const sink_attn_desc* d, const void* q, const int32_t* cu,
   return check_workspace(d, plan(d));
 }
 
+template <typename E>
+hipError_t prologue16(const sink_attn_desc* d, const void* k, const void* v, const int32_t* cu,
+                      const int32_t* cu_end, const float* knorm_w, int32_t use_rope,
+                      hipStream_t stream) {
+  const sa::Workspace w = plan(d);
+  char* ws = static_cast<char*>(d->workspace);
+  const int G = d->num_q_heads / d->num_kv_heads;
+  return sa::launch_prologue_bf16<E>(
+      static_cast<const E*>(k), static_cast<const E*>(v), cu, cu_end, knorm_w, d->total_tokens,
+      d->num_docs, d->num_kv_heads, w.t_pad, sa::tokens_per_block(G),
+      sa::tokens_per_block_wide(G), d->rms_eps, d->rope_theta, use_rope,
+      reinterpret_cast<E*>(ws + w.khat_off), reinterpret_cast<E*>(ws + w.vt_off),
+      reinterpret_cast<int32_t*>(ws + w.sched_off),
+      reinterpret_cast<int32_t*>(ws + w.sched_wide_off), stream);
+}
+
+template <typename E>
+hipError_t attention16(const sink_attn_desc* d, int tile, const void* q, const int32_t* cu,
+                       const int32_t* cu_end, const float* sinks, const float* qnorm_w,
+                       int32_t window, int32_t use_rope, void* out, float* lse,
+                       hipStream_t stream) {
+  const sa::Workspace w = plan(d);
+  char* ws = static_cast<char*>(d->workspace);
+  if (tile == sa::kTileWide || tile == sa::kTileWideExact)
+    return sa::launch_attention_bf16_wide<E>(
+        static_cast<const E*>(q), reinterpret_cast<const E*>(ws + w.khat_off),
+        reinterpret_cast<const E*>(ws + w.vt_off), cu, cu_end,
+        reinterpret_cast<const int32_t*>(ws + w.sched_wide_off), sinks, qnorm_w,
+        static_cast<E*>(out), lse, reinterpret_cast<int32_t*>(ws + w.redo_off),
+        d->total_tokens, d->num_docs, d->num_q_heads, d->num_kv_heads, w.t_pad,
+        w.items_ub_wide, window, use_rope, d->rms_eps, d->rope_theta, softmax_scale(d),
+        tile == sa::kTileWideExact, stream);
+  return sa::launch_attention_bf16<E>(
+      static_cast<const E*>(q), reinterpret_cast<const E*>(ws + w.khat_off),
+      reinterpret_cast<const E*>(ws + w.vt_off), cu, cu_end,
+      reinterpret_cast<const int32_t*>(ws + w.sched_off), sinks, qnorm_w, static_cast<E*>(out),
+      lse, d->total_tokens, d->num_docs, d->num_q_heads, d->num_kv_heads, w.t_pad, w.items_ub,
+      window, use_rope, d->rms_eps, d->rope_theta, softmax_scale(d), stream);
+}
+
 int launch_prologue(const sink_attn_desc* d, const void* k, const void* v,
                     const int32_t* cu, const int32_t* cu_end, const float* knorm_w,
                     int32_t use_rope, hipStream_t stream) {
@@ -302,14 +342,9 @@ int launch_prologue(const sink_attn_desc* d, const void* k, const void* v,
   char* ws = static_cast<char*>(d->workspace);
   hipError_t e;
   if (d->dtype == SINK_ATTN_BF16) {
-    const int G = d->num_q_heads / d->num_kv_heads;
-    e = sa::launch_prologue_bf16(
-        static_cast<const sa::bf16*>(k), static_cast<const sa::bf16*>(v), cu, cu_end, knorm_w,
-        d->total_tokens, d->num_docs, d->num_kv_heads, w.t_pad, sa::tokens_per_block(G),
-        sa::tokens_per_block_wide(G), d->rms_eps, d->rope_theta, use_rope,
-        reinterpret_cast<sa::bf16*>(ws + w.khat_off), reinterpret_cast<sa::bf16*>(ws + w.vt_off),
-        reinterpret_cast<int32_t*>(ws + w.sched_off),
-        reinterpret_cast<int32_t*>(ws + w.sched_wide_off), stream);
+    e = prologue16<sa::bf16>(d, k, v, cu, cu_end, knorm_w, use_rope, stream);
+  } else if (d->dtype == SINK_ATTN_F16) {
+    e = prologue16<sa::f16>(d, k, v, cu, cu_end, knorm_w, use_rope, stream);
   } else {
     e = sa::launch_prologue_f32(static_cast<const float*>(k), static_cast<const float*>(v), cu,
                                 cu_end, knorm_w, d->total_tokens, d->num_docs, d->num_kv_heads,
@@ -327,24 +362,12 @@ int launch_attention(const sink_attn_desc* d, const void* q, const int32_t* cu,
   const sa::Workspace w = plan(d);
   char* ws = static_cast<char*>(d->workspace);
   hipError_t e;
-  const int tile = d->dtype == SINK_ATTN_BF16 ? select_tile(d, window) : 0;
-  if (tile == sa::kTileWide || tile == sa::kTileWideExact) {
-    e = sa::launch_attention_bf16_wide(
-        static_cast<const sa::bf16*>(q), reinterpret_cast<const sa::bf16*>(ws + w.khat_off),
-        reinterpret_cast<const sa::bf16*>(ws + w.vt_off), cu, cu_end,
-        reinterpret_cast<const int32_t*>(ws + w.sched_wide_off), sinks, qnorm_w,
-        static_cast<sa::bf16*>(out), lse, reinterpret_cast<int32_t*>(ws + w.redo_off),
-        d->total_tokens, d->num_docs, d->num_q_heads, d->num_kv_heads, w.t_pad,
-        w.items_ub_wide, window, use_rope, d->rms_eps, d->rope_theta, softmax_scale(d),
-        tile == sa::kTileWideExact, stream);
-  } else if (d->dtype == SINK_ATTN_BF16) {
-    e = sa::launch_attention_bf16(
-        static_cast<const sa::bf16*>(q), reinterpret_cast<const sa::bf16*>(ws + w.khat_off),
-        reinterpret_cast<const sa::bf16*>(ws + w.vt_off),
-        cu, cu_end, reinterpret_cast<const int32_t*>(ws + w.sched_off), sinks, qnorm_w,
-        static_cast<sa::bf16*>(out), lse, d->total_tokens, d->num_docs, d->num_q_heads,
-        d->num_kv_heads, w.t_pad, w.items_ub, window, use_rope, d->rms_eps, d->rope_theta,
-        softmax_scale(d), stream);
+  if (d->dtype == SINK_ATTN_BF16) {
+    e = attention16<sa::bf16>(d, select_tile(d, window), q, cu, cu_end, sinks, qnorm_w, window,
+                              use_rope, out, lse, stream);
+  } else if (d->dtype == SINK_ATTN_F16) {
+    e = attention16<sa::f16>(d, select_tile(d, window), q, cu, cu_end, sinks, qnorm_w, window,
+                             use_rope, out, lse, stream);
   } else {
     e = sa::launch_attention_f32(
         static_cast<const float*>(q), reinterpret_cast<const float*>(ws + w.khat_off),
@@ -368,7 +391,7 @@ int check_bwd(const sink_attn_desc* d, const void* q, const void* k, const void*
               const float* dknorm_w) {
   int rc = check_desc(d);
   if (rc) return rc;
-  if (d->dtype != SINK_ATTN_BF16) return SINK_ATTN_EUNSUPPORTED;
+  if (d->dtype == SINK_ATTN_F32) return SINK_ATTN_EUNSUPPORTED;
   if (window == 0) return SINK_ATTN_EINVAL;
   if (use_rope != 0 && use_rope != 1) return SINK_ATTN_EINVAL;
   if (cu == nullptr || !aligned(cu, 4)) return SINK_ATTN_EINVAL;
@@ -435,8 +458,8 @@ int fwd_impl(const sink_attn_desc* desc, const void* q, const void* k, const voi
   if (rc != SINK_ATTN_OK) return rc;
   rc = launch_attention(desc, q, docs.starts, docs.ends, sinks, qnorm_w, window, use_rope, out,
                         lse, s);
-  if (rc != SINK_ATTN_OK || cu_padded == nullptr || desc->dtype != SINK_ATTN_BF16) return rc;
-  // the fp32 kernel writes padding rows itself; the bf16 kernels never visit them
+  if (rc != SINK_ATTN_OK || cu_padded == nullptr || desc->dtype == SINK_ATTN_F32) return rc;
+  // the fp32 kernel writes padding rows itself; the 16-bit kernels never visit them
   return sa::launch_pad_fill(docs.starts, docs.ends, desc->num_docs, desc->total_tokens,
                              desc->num_q_heads, desc->head_dim, desc->dtype, sinks, out, lse,
                              s) == hipSuccess
@@ -465,14 +488,17 @@ int bwd_impl(const sink_attn_desc* desc, const void* q, const void* k, const voi
   Docs docs;
   if (doc_bounds(desc, cu_seqlens, cu_padded, w.ends_off, s, &docs) != hipSuccess)
     return SINK_ATTN_ELAUNCH;
-  using sa::bf16;
-  const hipError_t e = sa::launch_bwd_bf16(
-      static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-      docs.starts, docs.ends, sinks, qnorm_w, knorm_w, static_cast<const bf16*>(out), lse,
-      static_cast<const bf16*>(dout), static_cast<bf16*>(dq), static_cast<bf16*>(dk),
-      static_cast<bf16*>(dv), dsinks, dqnorm_w, dknorm_w, desc->total_tokens, desc->num_docs,
-      Hq, desc->num_kv_heads, window, use_rope, desc->rms_eps, desc->rope_theta,
-      softmax_scale(desc), static_cast<char*>(desc->workspace), w, s);
+  auto run = [&](auto elem) {
+    using E = decltype(elem);
+    return sa::launch_bwd_bf16<E>(
+        static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v),
+        docs.starts, docs.ends, sinks, qnorm_w, knorm_w, static_cast<const E*>(out), lse,
+        static_cast<const E*>(dout), static_cast<E*>(dq), static_cast<E*>(dk),
+        static_cast<E*>(dv), dsinks, dqnorm_w, dknorm_w, desc->total_tokens, desc->num_docs,
+        Hq, desc->num_kv_heads, window, use_rope, desc->rms_eps, desc->rope_theta,
+        softmax_scale(desc), static_cast<char*>(desc->workspace), w, s);
+  };
+  const hipError_t e = desc->dtype == SINK_ATTN_F16 ? run(sa::f16{}) : run(sa::bf16{});
   return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;
 }
 
@@ -524,7 +550,7 @@ int sink_attn_fwd_padded(const sink_attn_desc* desc, const void* q, const void* 
 }
 
 size_t sink_attn_bwd_workspace_bytes(const sink_attn_desc* desc) {
-  if (check_desc(desc) != SINK_ATTN_OK || desc->dtype != SINK_ATTN_BF16) return 0;
+  if (check_desc(desc) != SINK_ATTN_OK || desc->dtype == SINK_ATTN_F32) return 0;
   return plan_bwd(desc).total;
 }
 
@@ -572,7 +598,7 @@ int sink_attn_tile_config(const sink_attn_desc* desc, int32_t window) {
   const int rc = check_desc(desc);
   if (rc != SINK_ATTN_OK) return rc;
   if (window == 0) return SINK_ATTN_EINVAL;
-  if (desc->dtype != SINK_ATTN_BF16) return 0;
+  if (desc->dtype == SINK_ATTN_F32) return 0;
   return select_tile(desc, window);
 }
 

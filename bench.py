@@ -25,6 +25,9 @@ before the timed region (sink_attn_mask_to_seqlens, timed on its own); the
 step's events cover all of its launches (K prologue, attention, padding-row
 fill).  FLOP counts real visible entries only.
 
+--dtype f16 runs the same step on fp16 q, k, v and out (the fp16 I/O
+variant; fp16 and bf16 share the 2.5 PFLOP/s dense MFMA peak).
+
 --pass bwd times the backward instead: a step is one sink_attn_bwd call (key
 and column tile preparation, the dK/dV and dQ kernels, the final sums) on the
 out and lse of one forward, counted as 2.5 forward passes
@@ -33,6 +36,7 @@ out and lse of one forward, counted as 2.5 forward passes
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -239,7 +243,7 @@ def run_fwd_padded(args, A, w, inp, d_inp, dev):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: {w.description}",
@@ -313,7 +317,7 @@ def run_bwd(args, A, w, d_inp, call, dev):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {
             "workload": f"{w.name} backward: {w.description}",
@@ -350,6 +354,9 @@ def main():
                              "sliding_bshd"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target host time of the oracle sample (0 skips the CPU baseline)")
+    ap.add_argument("--dtype", default=None, choices=["bf16", "f16"],
+                    help="storage dtype of q, k, v, out (default: the workload's, bf16); f16 "
+                         "runs the fp16 I/O variant")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="time the forward (default) or the backward pass")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -386,6 +393,8 @@ def main():
     A.load_library()
 
     w = workloads.named_workloads()[args.workload]
+    if args.dtype:
+        w = dataclasses.replace(w, dtype=args.dtype)
     inp = workloads.make_inputs(w, seed=0)
     d_inp = {k: v.to(dev) for k, v in inp.items()}
     torch.cuda.synchronize()
@@ -442,7 +451,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: {w.description}",
@@ -460,7 +469,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": load_traffic(w.name, kernel, kernel_src),
+            "traffic": load_traffic(w.name if w.dtype == "bf16" else f"{w.name}/{w.dtype}",
+                                    kernel, kernel_src),
             "avg_launch_ms": attn_ms,
         },
         "kernels": {

@@ -76,10 +76,18 @@ typedef enum {
 
 typedef enum {
   SINK_ATTN_BF16 = 0,  /* q, k, v, out bf16; fp32 arithmetic and accumulation */
-  SINK_ATTN_F32 = 1    /* q, k, v, out fp32; fp32 arithmetic throughout (debug path) */
+  SINK_ATTN_F32 = 1,   /* q, k, v, out fp32; fp32 arithmetic throughout (debug path) */
+  SINK_ATTN_F16 = 2    /* q, k, v, out fp16: the fp16 I/O variant (flint.config,
+                          attention_compute_dtype = 'fp16': an fp16 QKV and
+                          kernel-output boundary).  Same kernels and limits as
+                          bf16 with fp16 MFMA operands (q_hat, k_hat, V, the
+                          weights P; dS and dout in the backward), fp32
+                          arithmetic and accumulation.  fp16's range bounds
+                          the softmax references: sinks and scores must stay
+                          within about 22,700 (natural-log units). */
 } sink_attn_dtype;
 
-/* Attention tile configuration of the bf16 path.  Both compute the same
+/* Attention tile configuration of the 16-bit paths.  Both compute the same
  * function to the same tolerance; they differ in speed.  Narrow: each wave
  * holds 32 (token, head) query columns, two workgroups share a compute unit;
  * best for short documents and narrow windows.  Wide: 64 columns per wave,
@@ -105,7 +113,7 @@ typedef struct {
   int32_t num_docs;       /* D >= 0; cu_seqlens has D + 1 entries */
   int32_t num_q_heads;    /* Hq > 0 */
   int32_t num_kv_heads;   /* Hkv > 0, Hq % Hkv == 0 */
-  int32_t head_dim;       /* d: 128 (bf16 and fp32) or 64 (fp32 only) */
+  int32_t head_dim;       /* d: 128 (bf16, fp16 and fp32) or 64 (fp32 only) */
   int32_t dtype;          /* sink_attn_dtype of q, k, v and out */
   int32_t max_seqlen;     /* optional hint (0 = unknown); not needed, not trusted */
   int32_t tile_config;    /* sink_attn_tile_config_t: 0 automatic (use this), 1-3 force */
@@ -200,19 +208,19 @@ int sink_attn_mask_to_seqlens(const uint8_t* attention_mask, int32_t batch, int3
  * not read what the forward left there. */
 size_t sink_attn_bwd_workspace_bytes(const sink_attn_desc* desc);
 
-/* Backward pass of sink_attn_fwd (bf16 only): the gradients of
+/* Backward pass of sink_attn_fwd (bf16 and fp16): the gradients of
  * L = sum(dout * out) with respect to every input of the forward.
  *   q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope
  *               exactly as passed to the forward
- *   out [T,Hq,d] bf16 and lse fp32 [Hq,T]: what that forward wrote (lse is
+ *   out [T,Hq,d] (desc->dtype) and lse fp32 [Hq,T]: what that forward wrote (lse is
  *               required here)
- *   dout        [T,Hq,d] bf16, the gradient of the loss with respect to out
- *   dq [T,Hq,d], dk [T,Hkv,d], dv [T,Hkv,d]   bf16, fully overwritten
+ *   dout        [T,Hq,d] desc->dtype, the gradient of the loss with respect to out
+ *   dq [T,Hq,d], dk [T,Hkv,d], dv [T,Hkv,d]   desc->dtype, fully overwritten
  *   dsinks fp32 [Hq], dqnorm_w fp32 [d], dknorm_w fp32 [d]   overwritten, not
  *               accumulated (zero when T == 0)
  * desc->workspace must hold sink_attn_bwd_workspace_bytes(desc) bytes
- * (256-byte aligned); every bf16 tensor 16-byte aligned.  Gradients through
- * the softmax use D = dout . out per (token, head) with the bf16 out.  The
+ * (256-byte aligned); every 16-bit tensor 16-byte aligned.  Gradients through
+ * the softmax use D = dout . out per (token, head) with the stored out.  The
  * sums over tokens (dsinks, norm weights) are added in a fixed order: equal
  * inputs give bitwise equal outputs.  fp32 descriptors return
  * SINK_ATTN_EUNSUPPORTED. */

@@ -313,3 +313,20 @@ def test_mask_to_seqlens_validates(A):
     assert lib.sink_attn_mask_to_seqlens(P(FAKE), 2, 4, P(0), P(FAKE), P(FAKE), None) == EINVAL
     assert lib.sink_attn_mask_to_seqlens(P(FAKE), 1 << 16, 1 << 16, P(FAKE), P(FAKE), P(FAKE),
                                          None) == EINVAL
+
+
+def test_fp16_descriptor(A):
+    # the fp16 I/O variant shares the bf16 layout: same workspaces, same
+    # tile rule, same shape limits; the backward accepts it too
+    f16 = A.SINK_ATTN_F16
+    for args in ((12450, 8), (32768, 1), (111378, 512)):
+        assert A.sink_attn_workspace_bytes(*args, 32, 4, 128, dtype=f16) == \
+            A.sink_attn_workspace_bytes(*args, 32, 4, 128)
+        assert A.sink_attn_bwd_workspace_bytes(*args, 32, 4, 128, dtype=f16) == \
+            A.sink_attn_bwd_workspace_bytes(*args, 32, 4, 128)
+    assert A.sink_attn_tile_config(32768, 1, 32, 4, 128, -1, dtype=f16) == 2
+    assert A.sink_attn_tile_config(12450, 8, 32, 4, 128, 1024, dtype=f16) == 1
+    assert _fwd(A, _desc(A, dtype=f16, d=64, ws_bytes=1 << 30)) == EUNSUPPORTED
+    assert _fwd(A, _desc(A, dtype=f16, Hq=12, Hkv=4, ws_bytes=1 << 30)) == EUNSUPPORTED
+    assert _fwd(A, _desc(A, dtype=f16), q=FAKE + 8) == EINVAL   # 16-byte alignment
+    assert _fwd(A, _desc(A, dtype=f16, ws_bytes=1024)) == EWORKSPACE

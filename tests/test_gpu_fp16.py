@@ -1,0 +1,128 @@
+"""GPU parity of the fp16 I/O variant (flint.config attention_compute_dtype =
+'fp16': q, k, v and out, and in the backward dout and the input gradients,
+stored in fp16) against the fp64 oracle on the same fp16 bits.
+
+The kernels are the bf16 ones instantiated with fp16 MFMA operands, so the
+cases mirror the bf16 tests: ragged documents, windows, RoPE, group sizes,
+sinks, both tile configurations, long documents, the backward, and the
+full-size causal workload on sampled rows.  fp16's narrow range adds one
+case: weights against the wide tiles' fixed reference overflow fp16 once a
+score is 16 log2 units above it (bf16 allows 90), which sends the block to
+the exact-max rerun; it must agree with the narrow tiles."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from _harness import (FP16_MAX, FP16_MEAN, check_bwd_parity, check_parity, custom_inputs,
+                      gpu_forward, require_gpu, to_device)
+
+pytestmark = pytest.mark.gpu
+
+NARROW, WIDE, WIDE_EXACT = 1, 2, 3
+RAGGED = [1, 2, 3, 17, 63, 64, 65, 127, 128, 129, 200, 0, 31, 300]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    return require_gpu()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _f16(lengths, **kw):
+    return custom_inputs(lengths, dtype="f16", **kw)
+
+
+@pytest.mark.parametrize("tile", [NARROW, WIDE, WIDE_EXACT])
+@pytest.mark.parametrize("window,use_rope", [(-1, False), (1, True), (65, False), (512, True)])
+def test_forward_ragged(tile, window, use_rope):
+    _say(f"case fp16 fwd tile={tile} W={window} rope={use_rope}")
+    check_parity(_f16(RAGGED), window, use_rope, label=f"fp16 tile{tile} W={window}",
+                 tile_config=tile)
+
+
+@pytest.mark.parametrize("heads", [(32, 4), (8, 8), (32, 1), (16, 16)])
+def test_forward_group_sizes(heads):
+    _say(f"case fp16 fwd heads={heads}")
+    inp = _f16([150, 33, 290], Hq=heads[0], Hkv=heads[1])
+    for tile in (NARROW, WIDE):
+        check_parity(inp, 100, True, label=f"fp16 {heads} tile{tile}", tile_config=tile)
+        check_parity(inp, -1, False, label=f"fp16 {heads} tile{tile}", tile_config=tile)
+
+
+def test_forward_long_document_and_sinks():
+    _say("case fp16 fwd one doc 2500, sinks")
+    inp = _f16([2500])
+    for tile in (NARROW, WIDE):
+        check_parity(inp, -1, False, label=f"fp16 causal tile{tile}", tile_config=tile)
+        check_parity(inp, 700, True, label=f"fp16 W=700 tile{tile}", tile_config=tile)
+    small = _f16([70, 130])
+    check_parity(dict(small, sinks=torch.full((32,), float("-inf"))), 40, True, label="-inf")
+    check_parity(_f16([70, 130], sink_mean=2.0), -1, False, label="N(2,1)")
+    big = to_device(dict(small, sinks=torch.full((32,), 60.0)))
+    for tile in (NARROW, WIDE):
+        out, lse = gpu_forward(big, -1, False, tile_config=tile)
+        assert out.float().abs().max().item() < 1e-6
+        assert torch.allclose(lse, torch.full_like(lse, 60.0), atol=1e-3)
+
+
+@pytest.mark.parametrize("window", [-1, 300])
+def test_weights_past_fp16_range_take_the_rerun(window):
+    # norm weights of 1.6 give scores a standard deviation of about 2.6 nats:
+    # a row's peak over hundreds of keys sits ~8 nats above the mean, and
+    # where the token's own score is low that peak is more than 16 log2 units
+    # (11 nats) above it -- past what an fp16 weight can hold -- so the wide
+    # main launch hands those blocks to the exact-max launch; the result must
+    # match the narrow tiles (running max) and the all-exact configuration
+    _say(f"case fp16 large scores W={window}")
+    inp = _f16([700, 1400])
+    inp = dict(inp, qnorm_w=torch.full((128,), 1.6), knorm_w=torch.full((128,), 1.6),
+               sinks=torch.full((32,), float("-inf")))
+    dev = to_device(inp)
+    outs = {t: gpu_forward(dev, window, False, tile_config=t) for t in (NARROW, WIDE, WIDE_EXACT)}
+    for t in (WIDE, WIDE_EXACT):
+        o, l = outs[t]
+        assert torch.isfinite(o.float()).all() and torch.isfinite(l).all()
+        d = (o.float() - outs[NARROW][0].float()).abs()
+        dl = (l - outs[NARROW][1]).abs()
+        _say(f"  tile {t} vs narrow: out max/mean {d.max().item():.3e}/{d.mean().item():.3e} "
+             f"lse max {dl.max().item():.3e}")
+        assert d.max().item() <= FP16_MAX and d.mean().item() <= FP16_MEAN
+        assert dl.max().item() <= 1e-3 * max(1.0, outs[NARROW][1].abs().max().item())
+
+
+@pytest.mark.parametrize("window,use_rope", [(-1, False), (1, True), (100, True), (512, True)])
+def test_backward_ragged(window, use_rope):
+    _say(f"case fp16 bwd ragged W={window} rope={use_rope}")
+    check_bwd_parity(_f16(RAGGED), window, use_rope, label=f"fp16 W={window}")
+
+
+@pytest.mark.parametrize("heads", [(32, 4), (8, 8), (32, 1)])
+def test_backward_group_sizes(heads):
+    _say(f"case fp16 bwd heads={heads}")
+    inp = _f16([150, 33, 290], Hq=heads[0], Hkv=heads[1])
+    check_bwd_parity(inp, 100, True, label=f"fp16 {heads} W=100")
+    check_bwd_parity(inp, -1, False, label=f"fp16 {heads} causal")
+
+
+def test_backward_long_document():
+    _say("case fp16 bwd one doc 1500")
+    inp = _f16([1500])
+    check_bwd_parity(inp, -1, False, label="fp16 causal 1500")
+    check_bwd_parity(inp, 700, True, label="fp16 W=700 1500")
+
+
+def test_full_workload_sampled_rows():
+    # the full-causal layer (one document of 32768 tokens) in fp16, in the
+    # launch configuration the benchmark times (automatic tile choice)
+    w = workloads.named_workloads()["full"]
+    w = workloads.Workload(w.name, w.lengths, w.num_q_heads, w.num_kv_heads, w.head_dim, "f16",
+                           w.window, w.use_rope, w.sink_mean)
+    _say(f"case fp16 full T={w.total_tokens}")
+    inp = workloads.make_inputs(w)
+    rows = workloads.sample_rows(w.lengths, w.window, 192)
+    eo, el = check_parity(inp, w.window, w.use_rope, rows=rows, label="fp16 full")
+    assert np.isfinite(eo[0])

@@ -14,8 +14,9 @@ import pytest
 import torch
 
 import workloads
-from _harness import (BF16_MAX, BF16_MEAN, BWD_REL_MAX, BWD_REL_MEAN, F32_MAX, GRAD_KEYS,
-                      check_parity, custom_inputs, errors, require_gpu, to_device)
+from _harness import (BF16_MAX, BF16_MEAN, BWD_REL_FP16, BWD_REL_MAX, BWD_REL_MEAN, GRAD_KEYS,
+                      check_parity, custom_inputs, errors, fwd_bounds, require_gpu,
+                      to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -66,21 +67,23 @@ def _check_fwd(inp, rows, pad, out, lse, window, use_rope, label):
     eo = errors(o[rows], ref_out[rows])
     el = errors(l[:, rows], ref_lse[:, rows])
     _say(f"  {label}: out max/mean {eo[0]:.3e}/{eo[1]:.3e} lse max {el[0]:.3e}")
+    bmax, bmean = fwd_bounds(inp["q"].dtype)
     if inp["q"].dtype == torch.float32:
-        assert eo[0] <= F32_MAX and el[0] <= F32_MAX, (label, eo, el)
+        assert eo[0] <= bmax and el[0] <= bmax, (label, eo, el)
     else:
-        assert eo[0] <= BF16_MAX and eo[1] <= BF16_MEAN and el[0] <= BF16_MAX, (label, eo, el)
+        assert eo[0] <= bmax and eo[1] <= bmean and el[0] <= bmax, (label, eo, el)
     assert np.all(o[pad] == 0.0), label
     assert np.array_equal(l[:, pad], np.repeat(inp["sinks"].numpy()[:, None], len(pad), 1)
                           .astype(np.float64)), label
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("tile", [0, 1, 2, 3])
 @pytest.mark.parametrize("window,use_rope", [(-1, False), (50, True)])
-def test_padded_thd_forward(tile, window, use_rope):
+def test_padded_thd_forward(tile, window, use_rope, dtype):
     import attention_qk_rmsnorm_amd as A
-    _say(f"case padded fwd tile={tile} W={window}")
-    inp, rows, pad = _padded_inputs(LENGTHS, SLOTS)
+    _say(f"case padded fwd tile={tile} W={window} {dtype}")
+    inp, rows, pad = _padded_inputs(LENGTHS, SLOTS, dtype=dtype)
     dev = to_device(inp)
     out, lse = A.sink_attn_fwd(dev["q"], dev["k"], dev["v"], dev["cu_seqlens"], dev["sinks"],
                                dev["qnorm_w"], dev["knorm_w"], window, use_rope,
@@ -113,6 +116,7 @@ def test_eps_zero_with_ragged_token_count():
 
 def _check_grads(g, ref, rows, pad, label):
     msg, bad = [], []
+    rmax, rmean = BWD_REL_FP16 if g["dq"].dtype == torch.float16 else (BWD_REL_MAX, BWD_REL_MEAN)
     for key in GRAD_KEYS:
         got = g[key].float().cpu().numpy().astype(np.float64)
         r = ref[key]
@@ -123,7 +127,7 @@ def _check_grads(g, ref, rows, pad, label):
         emax, emean = errors(got, r)
         smax, smean = float(np.abs(r).max()), float(np.abs(r).mean())
         msg.append(f"{key} {emax / smax:.2e}/{emean / smean:.2e}")
-        if emax > BWD_REL_MAX * smax or emean > BWD_REL_MEAN * smean:
+        if emax > rmax * smax or emean > rmean * smean:
             bad.append(key)
     _say(f"  {label}: rel max/mean " + ", ".join(msg))
     assert not bad, (label, bad)
@@ -141,13 +145,14 @@ def _oracle_bwd(inp, window, use_rope, rows, dout):
                                   f(inp["qnorm_w"]), f(inp["knorm_w"]), window, use_rope, do)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("window,use_rope", [(-1, False), (50, True)])
-def test_padded_thd_backward(window, use_rope):
+def test_padded_thd_backward(window, use_rope, dtype):
     import attention_qk_rmsnorm_amd as A
-    _say(f"case padded bwd W={window}")
-    inp, rows, pad = _padded_inputs(LENGTHS, SLOTS)
+    _say(f"case padded bwd W={window} {dtype}")
+    inp, rows, pad = _padded_inputs(LENGTHS, SLOTS, dtype=dtype)
     T = sum(SLOTS)
-    dout = workloads.make_grad_output(workloads.Workload("g", (T,)), 0)
+    dout = workloads.make_grad_output(workloads.Workload("g", (T,), dtype=dtype), 0)
     dout[torch.from_numpy(pad)] = float("nan")
     dev = to_device(inp)
     out, lse = A.sink_attn_fwd(dev["q"], dev["k"], dev["v"], dev["cu_seqlens"], dev["sinks"],

@@ -92,7 +92,7 @@ def named_workloads(seed: int = 0) -> dict:
     }
 
 
-_TORCH_DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32}
+_TORCH_DTYPES = {"bf16": torch.bfloat16, "f32": torch.float32, "f16": torch.float16}
 
 
 def cu_seqlens(lengths) -> np.ndarray:
