@@ -158,12 +158,11 @@ __device__ __forceinline__ void mask_half(int kh, const Cols& c, f32x16 (&s)[2])
 // Weights of keys 16jj .. 16jj + 15 of a half tile for column block cb:
 // B operand k-slot 8hf + e <-> key 16jj + 8(e/4) + 4hf + e%4, the order the
 // prologue stored V^T keys in.
+// (elements 4h .. 4h + 3 only: the exps are spread over the score MFMAs)
 template <typename E>
-__device__ __forceinline__ vec8<E> weights(const f32x16& sv, int jj) {
-  vec8<E> pb;
+__device__ __forceinline__ void weights_half(const f32x16& sv, int jj, int h, vec8<E>& pb) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) pb[e] = (E)__builtin_amdgcn_exp2f(sv[8 * jj + e]);
-  return pb;
+  for (int e = 4 * h; e < 4 * h + 4; ++e) pb[e] = (E)__builtin_amdgcn_exp2f(sv[8 * jj + e]);
 }
 
 template <typename E>
@@ -226,9 +225,11 @@ __device__ __forceinline__ void half_step(const char* lds, const int (&koff)[8],
     for (int kk = 0; kk < 8; ++kk) {
       __builtin_amdgcn_sched_barrier(0);
       sn[0] = mfma32(kf[kk], st.qf[0][kk], sn[0]);
-      if ((kk & 1) == 0) {
-        const int g = kk >> 1;  // weight group: cb = g >> 1, jj = g & 1
-        p[g >> 1][g & 1] = weights<E>(sc[g >> 1], g & 1);
+      {
+        // four weights per MFMA pair: group g = kk / 2 (cb = g / 2, jj = g % 2),
+        // elements 4 (kk % 2) .. + 3
+        const int g = kk >> 1;
+        weights_half<E>(sc[g >> 1], g & 1, kk & 1, p[g >> 1][g & 1]);
       }
       sn[1] = mfma32(kf[kk], st.qf[1][kk], sn[1]);
       __builtin_amdgcn_sched_barrier(0);
