@@ -64,41 +64,10 @@ constexpr float kRedo = 0x1p90f;  // denominator bound that sends a block to its
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// O^T accumulation kept in AGPRs: the accumulators are touched only by these
-// MFMAs, by their zeroing and by the epilogue (after agpr_fence()), which
-// leaves the 256 VGPRs to the scores, weights and operands.
-template <typename E>
-__device__ __forceinline__ void mfma32_acc(f32x16& acc, vec8<E> a, vec8<E> b) {
-  if constexpr (is_f16<E>)
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-  else
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// Zero an AGPR accumulator with an MFMA of zero operands, so that every
-// definition of the accumulators is an AGPR one and the register allocator
-// never moves them through VGPRs.
-template <typename E>
-__device__ __forceinline__ void zero_acc(f32x16& acc, vec8<E> zero) {
-  // s_nop 1: the zero operand was just written by VALU code, and an MFMA
-  // needs two wait states before reading such a register; the compiler does
-  // not count them for inline asm
-  if constexpr (is_f16<E>)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero));
-  else
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero));
-}
-
-// Wait states before VALU code reads or writes accumulators that an
-// inline-asm MFMA wrote (the compiler cannot see that hazard).
-__device__ __forceinline__ void agpr_fence() {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-}
-
-template <typename E>
-__device__ __forceinline__ vec8<E> rd(const char* p) {
-  return *reinterpret_cast<const vec8<E>*>(p);
-}
+// O^T lives in AGPRs: the accumulators are touched only by the inline-asm
+// MFMAs of sa_device.h (mfma32_acc), their zeroing (zero_acc) and the
+// epilogue (after agpr_fence()), which leaves the 256 VGPRs to the scores,
+// weights and operands.
 
 // Copy one 16 KiB tile image into LDS at dst: chunk 256 i + tid of the image
 // lands at byte 16 (256 i + tid), by global_load_lds_dwordx4.

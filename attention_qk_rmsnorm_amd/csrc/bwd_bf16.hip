@@ -83,39 +83,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// accumulation into AGPR-resident accumulators (see attn_bf16_wide.hip)
-template <typename E>
-__device__ __forceinline__ void mfma32_acc(f32x16& acc, vec8<E> a, vec8<E> b) {
-  if constexpr (is_f16<E>)
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-  else
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// The same with the two wait states a VALU write of a or b needs before an
-// MFMA reads it (the first use of an operand just converted from scores).
-template <typename E>
-__device__ __forceinline__ void mfma32_acc_nop(f32x16& acc, vec8<E> a, vec8<E> b) {
-  if constexpr (is_f16<E>)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-  else
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-template <typename E>
-__device__ __forceinline__ void zero_acc(f32x16& acc, vec8<E> zero) {
-  if constexpr (is_f16<E>)
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero));
-  else
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero));
-}
-__device__ __forceinline__ void agpr_fence() {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-}
-
-template <typename E>
-__device__ __forceinline__ vec8<E> rd(const char* p) {
-  return *reinterpret_cast<const vec8<E>*>(p);
-}
-
 // Chunk swizzle of the backward's row images.  Rows are 256 B, so every row
 // starts on LDS bank 0 and only the chunk position decides the banks.  The
 // MFMA operand read takes one chunk from each of 16 aligned rows: bswz is a

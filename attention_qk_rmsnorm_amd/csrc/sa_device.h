@@ -95,4 +95,51 @@ __device__ __forceinline__ float ref_round(float x) {
   else return (float)(E)x;
 }
 
+// ---- AGPR-resident accumulation by inline-asm MFMA -------------------------
+// C += A B into an accumulator the compiler keeps in AGPRs.  The compiler
+// cannot see the hazards of these inline-asm MFMAs: the caller inserts the
+// two wait states an MFMA needs after VALU code wrote a or b (mfma32_acc_nop,
+// or an explicit s_nop 1), and agpr_fence() before VALU code touches an
+// accumulator an MFMA just wrote.
+template <typename E>
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, vec8<E> a, vec8<E> b) {
+  if constexpr (is_f16<E>)
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// The same with the two wait states a VALU write of a or b needs first.
+template <typename E>
+__device__ __forceinline__ void mfma32_acc_nop(f32x16& acc, vec8<E> a, vec8<E> b) {
+  if constexpr (is_f16<E>)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Zero an AGPR accumulator with an MFMA of zero operands, so that every
+// definition of the accumulator is an AGPR one and the register allocator
+// never moves it through VGPRs (s_nop 1: the zero operand was just written
+// by VALU code).
+template <typename E>
+__device__ __forceinline__ void zero_acc(f32x16& acc, vec8<E> zero) {
+  if constexpr (is_f16<E>)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %1, 0" : "=a"(acc) : "v"(zero));
+}
+
+// Wait states before VALU code reads or writes accumulators that an
+// inline-asm MFMA wrote.
+__device__ __forceinline__ void agpr_fence() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+// One 16-byte MFMA operand (8 elements) from LDS or global memory.
+template <typename E>
+__device__ __forceinline__ vec8<E> rd(const char* p) {
+  return *reinterpret_cast<const vec8<E>*>(p);
+}
+
 }  // namespace sa
