@@ -1,5 +1,6 @@
-// attn_bf16.hip -- sink-aware GQA attention forward, 16-bit in/out (bf16, or
-// fp16 for the fp16 I/O variant), gfx950 MFMA.  The kernel is a template over
+// attn_narrow.hip -- sink-aware GQA attention forward, narrow tiles (32 query
+// columns per wave, two workgroups per CU), 16-bit in/out (bf16, or fp16 for the
+// fp16 I/O variant), gfx950 MFMA.  The kernel is a template over
 // the element type E; everything below says "E" where the two differ only in
 // the type of the operands (v_mfma_f32_32x32x16_bf16 or _f16).
 //
@@ -221,7 +222,7 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
 }
 
 template <typename E>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
     const E* __restrict__ q, const E* __restrict__ khat,
     const E* __restrict__ vt, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ cu_end, const int32_t* __restrict__ sched, const float* __restrict__ sinks,
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 }  // namespace
 
 template <typename E>
-hipError_t launch_attention_bf16(const E* q, const E* khat, const E* vt,
+hipError_t launch_attention_narrow(const E* q, const E* khat, const E* vt,
                                  const int32_t* cu, const int32_t* cu_end, const int32_t* sched,
                                  const float* sinks, const float* qnorm_w, E* out,
                                  float* lse, int T, int D, int Hq, int Hkv,
@@ -419,14 +420,14 @@ hipError_t launch_attention_bf16(const E* q, const E* khat, const E* vt,
   }
   if (grid <= 0) return hipSuccess;
   const float c_log2 = (float)(scale * 1.4426950408889634);
-  attn_fwd_bf16_kernel<E><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+  attn_fwd_narrow_kernel<E><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
       q, khat, vt, cu, cu_end, sched, sinks, qnorm_w, out, lse, T, Hq, Hkv, G, log2G, t_pad,
       window, use_rope, (float)eps, theta, c_log2, xcd_per);
   return hipGetLastError();
 }
 
 #define SA_INSTANTIATE(E)                                                                    \
-  template hipError_t launch_attention_bf16<E>(const E*, const E*, const E*, const int32_t*, \
+  template hipError_t launch_attention_narrow<E>(const E*, const E*, const E*, const int32_t*, \
                                                const int32_t*, const int32_t*, const float*,   \
                                                const float*, E*, float*, int, int, int, int,   \
                                                int64_t, int64_t, int, int, double, double,     \

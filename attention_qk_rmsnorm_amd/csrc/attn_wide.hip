@@ -1,4 +1,4 @@
-// attn_bf16_wide.hip -- sink-aware GQA attention forward, 16-bit in/out (bf16,
+// attn_wide.hip -- sink-aware GQA attention forward, 16-bit in/out (bf16,
 // or fp16 for the fp16 I/O variant: a template over the element type E),
 // gfx950 MFMA, wide tiles (64 query columns per wave, one workgroup per CU).
 //
@@ -350,7 +350,7 @@ __device__ __forceinline__ void attend_pass(char* lds, const int (&koff)[8], con
 // EXACT = true: the follow-up launch; only marked blocks run, with the exact
 // row max found by a scores-only pass first.
 template <bool EXACT, typename E>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_wide_kernel(
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_wide_kernel(
     const E* __restrict__ q, const E* __restrict__ khat,
     const E* __restrict__ vt, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ cu_end, const int32_t* __restrict__ sched, const float* __restrict__ sinks,
@@ -598,7 +598,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_wide_kernel(
 }  // namespace
 
 template <typename E>
-hipError_t launch_attention_bf16_wide(const E* q, const E* khat, const E* vt,
+hipError_t launch_attention_wide(const E* q, const E* khat, const E* vt,
                                       const int32_t* cu, const int32_t* cu_end,
                                       const int32_t* sched,
                                       const float* sinks, const float* qnorm_w, E* out,
@@ -617,17 +617,17 @@ hipError_t launch_attention_bf16_wide(const E* q, const E* khat, const E* vt,
   if (grid <= 0) return hipSuccess;
   const float c_log2 = (float)(scale * 1.4426950408889634);
   // main launch, then the follow-up that reruns the blocks it marked
-  attn_fwd_bf16_wide_kernel<false, E><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+  attn_fwd_wide_kernel<false, E><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
       q, khat, vt, cu, cu_end, sched, sinks, qnorm_w, out, lse, redo, T, Hq, Hkv, G, log2G, t_pad,
       window, use_rope, (float)eps, theta, c_log2, xcd_per, exact_all ? 1 : 0);
-  attn_fwd_bf16_wide_kernel<true, E><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+  attn_fwd_wide_kernel<true, E><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
       q, khat, vt, cu, cu_end, sched, sinks, qnorm_w, out, lse, redo, T, Hq, Hkv, G, log2G, t_pad,
       window, use_rope, (float)eps, theta, c_log2, xcd_per, 0);
   return hipGetLastError();
 }
 
 #define SA_INSTANTIATE(E)                                                                     \
-  template hipError_t launch_attention_bf16_wide<E>(                                          \
+  template hipError_t launch_attention_wide<E>(                                          \
       const E*, const E*, const E*, const int32_t*, const int32_t*, const int32_t*,           \
       const float*, const float*, E*, float*, int32_t*, int, int, int, int, int64_t, int64_t, \
       int, int, double, double, double, bool, hipStream_t);

@@ -1,8 +1,8 @@
-// bwd_bf16.hip -- backward pass of the sink-aware GQA attention, 16-bit in/out
+// bwd.hip -- backward pass of the sink-aware GQA attention, 16-bit in/out
 // (bf16, or fp16 for the fp16 I/O variant: the kernels are templates over the
 // element type E), gfx950 MFMA.
 //
-// Gradients of L = sum(dout * out) for the forward of attn_bf16*.hip
+// Gradients of L = sum(dout * out) for the forward of attn_narrow.hip / attn_wide.hip
 // (flint.layers FlintAttention: the sinks are trainable fp32 logits,
 // _FlintSinkParameters, and the q_norm / k_norm weights are RMSNorm
 // parameters).  Per (token t, query head h) with weights P_u = exp(s_u - lse)
@@ -1053,7 +1053,7 @@ BwdWorkspace plan_bwd_workspace(int64_t T, int64_t D, int Hq, int Hkv) {
 }
 
 template <typename E>
-hipError_t launch_bwd_bf16(const E* q, const E* k, const E* v, const int32_t* cu,
+hipError_t launch_bwd(const E* q, const E* k, const E* v, const int32_t* cu,
                            const int32_t* cu_end, const float* sinks, const float* qnorm_w, const float* knorm_w,
                            const E* out, const float* lse, const E* dout, E* dq,
                            E* dk, E* dv, float* dsinks, float* dqnorm_w,
@@ -1087,7 +1087,7 @@ hipError_t launch_bwd_bf16(const E* q, const E* k, const E* v, const int32_t* cu
 }
 
 #define SA_INSTANTIATE(E)                                                                     \
-  template hipError_t launch_bwd_bf16<E>(                                                     \
+  template hipError_t launch_bwd<E>(                                                     \
       const E*, const E*, const E*, const int32_t*, const int32_t*, const float*,             \
       const float*, const float*, const E*, const float*, const E*, E*, E*, E*, float*,       \
       float*, float*, int, int, int, int, int, int, double, double, double, char*,            \

@@ -85,7 +85,7 @@ __device__ void build_schedule(const int32_t* __restrict__ cu, const int32_t* __
 }
 
 template <typename E>
-__global__ __launch_bounds__(kThreads) void prologue_bf16_kernel(
+__global__ __launch_bounds__(kThreads) void prologue_16_kernel(
     const E* __restrict__ k, const E* __restrict__ v,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_end,
     const float* __restrict__ knorm_w, int T, int D,
@@ -255,21 +255,21 @@ __global__ __launch_bounds__(kThreads) void prologue_f32_kernel(
 }  // namespace
 
 template <typename E>
-hipError_t launch_prologue_bf16(const E* k, const E* v, const int32_t* cu,
+hipError_t launch_prologue_16(const E* k, const E* v, const int32_t* cu,
                                 const int32_t* cu_end, const float* knorm_w, int T, int D, int Hkv,
                                 int64_t t_pad, int m_tok, int m_tok_wide, double eps,
                                 double theta, int use_rope, E* khat, E* vt,
                                 int32_t* sched, int32_t* sched_wide, hipStream_t stream) {
   const int64_t n_tiles = t_pad / kKeyTile;
   const int64_t grid = 2 + n_tiles * Hkv;
-  prologue_bf16_kernel<E><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
+  prologue_16_kernel<E><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
       k, v, cu, cu_end, knorm_w, T, D, Hkv, t_pad, m_tok, m_tok_wide, (float)eps, theta, use_rope,
       khat, vt, sched, sched_wide);
   return hipGetLastError();
 }
 
 #define SA_INSTANTIATE(E)                                                                    \
-  template hipError_t launch_prologue_bf16<E>(const E*, const E*, const int32_t*,            \
+  template hipError_t launch_prologue_16<E>(const E*, const E*, const int32_t*,            \
                                               const int32_t*, const float*, int, int, int,   \
                                               int64_t, int, int, double, double, int, E*, E*, \
                                               int32_t*, int32_t*, hipStream_t);

@@ -98,14 +98,14 @@ hipError_t launch_pad_fill(const int32_t* starts, const int32_t* ends, int D, in
 
 // The 16-bit launch wrappers are instantiated for E = bf16 and E = f16.
 template <typename E>
-hipError_t launch_prologue_bf16(const E* k, const E* v, const int32_t* cu,
+hipError_t launch_prologue_16(const E* k, const E* v, const int32_t* cu,
                                 const int32_t* cu_end, const float* knorm_w, int T, int D, int Hkv,
                                 int64_t t_pad, int m_tok, int m_tok_wide, double eps,
                                 double theta, int use_rope, E* khat, E* vt,
                                 int32_t* sched, int32_t* sched_wide, hipStream_t stream);
 
 template <typename E>
-hipError_t launch_attention_bf16(const E* q, const E* khat, const E* vt,
+hipError_t launch_attention_narrow(const E* q, const E* khat, const E* vt,
                                  const int32_t* cu, const int32_t* cu_end, const int32_t* sched,
                                  const float* sinks, const float* qnorm_w, E* out,
                                  float* lse, int T, int D, int Hq, int Hkv,
@@ -114,7 +114,7 @@ hipError_t launch_attention_bf16(const E* q, const E* khat, const E* vt,
                                  double scale, hipStream_t stream);
 
 template <typename E>
-hipError_t launch_attention_bf16_wide(const E* q, const E* khat, const E* vt,
+hipError_t launch_attention_wide(const E* q, const E* khat, const E* vt,
                                       const int32_t* cu, const int32_t* cu_end,
                                       const int32_t* sched,
                                       const float* sinks, const float* qnorm_w, E* out,
@@ -124,7 +124,7 @@ hipError_t launch_attention_bf16_wide(const E* q, const E* khat, const E* vt,
                                       bool exact_all, hipStream_t stream);
 
 template <typename E>
-hipError_t launch_bwd_bf16(const E* q, const E* k, const E* v, const int32_t* cu,
+hipError_t launch_bwd(const E* q, const E* k, const E* v, const int32_t* cu,
                            const int32_t* cu_end, const float* sinks, const float* qnorm_w, const float* knorm_w,
                            const E* out, const float* lse, const E* dout, E* dq,
                            E* dk, E* dv, float* dsinks, float* dqnorm_w,

@@ -302,7 +302,7 @@ hipError_t prologue16(const sink_attn_desc* d, const void* k, const void* v, con
   const sa::Workspace w = plan(d);
   char* ws = static_cast<char*>(d->workspace);
   const int G = d->num_q_heads / d->num_kv_heads;
-  return sa::launch_prologue_bf16<E>(
+  return sa::launch_prologue_16<E>(
       static_cast<const E*>(k), static_cast<const E*>(v), cu, cu_end, knorm_w, d->total_tokens,
       d->num_docs, d->num_kv_heads, w.t_pad, sa::tokens_per_block(G),
       sa::tokens_per_block_wide(G), d->rms_eps, d->rope_theta, use_rope,
@@ -319,7 +319,7 @@ hipError_t attention16(const sink_attn_desc* d, int tile, const void* q, const i
   const sa::Workspace w = plan(d);
   char* ws = static_cast<char*>(d->workspace);
   if (tile == sa::kTileWide || tile == sa::kTileWideExact)
-    return sa::launch_attention_bf16_wide<E>(
+    return sa::launch_attention_wide<E>(
         static_cast<const E*>(q), reinterpret_cast<const E*>(ws + w.khat_off),
         reinterpret_cast<const E*>(ws + w.vt_off), cu, cu_end,
         reinterpret_cast<const int32_t*>(ws + w.sched_wide_off), sinks, qnorm_w,
@@ -327,7 +327,7 @@ hipError_t attention16(const sink_attn_desc* d, int tile, const void* q, const i
         d->total_tokens, d->num_docs, d->num_q_heads, d->num_kv_heads, w.t_pad,
         w.items_ub_wide, window, use_rope, d->rms_eps, d->rope_theta, softmax_scale(d),
         tile == sa::kTileWideExact, stream);
-  return sa::launch_attention_bf16<E>(
+  return sa::launch_attention_narrow<E>(
       static_cast<const E*>(q), reinterpret_cast<const E*>(ws + w.khat_off),
       reinterpret_cast<const E*>(ws + w.vt_off), cu, cu_end,
       reinterpret_cast<const int32_t*>(ws + w.sched_off), sinks, qnorm_w, static_cast<E*>(out),
@@ -490,7 +490,7 @@ int bwd_impl(const sink_attn_desc* desc, const void* q, const void* k, const voi
     return SINK_ATTN_ELAUNCH;
   auto run = [&](auto elem) {
     using E = decltype(elem);
-    return sa::launch_bwd_bf16<E>(
+    return sa::launch_bwd<E>(
         static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v),
         docs.starts, docs.ends, sinks, qnorm_w, knorm_w, static_cast<const E*>(out), lse,
         static_cast<const E*>(dout), static_cast<E*>(dq), static_cast<E*>(dk),

@@ -56,10 +56,10 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 CSRC = os.path.join(ROOT, "attention_qk_rmsnorm_amd", "csrc")
 # tile configuration -> (attention kernel, its source file)
-ATTN_KERNELS = {1: ("attn_fwd_bf16_kernel", "attn_bf16.hip"),
-                2: ("attn_fwd_bf16_wide_kernel", "attn_bf16_wide.hip"),
-                3: ("attn_fwd_bf16_wide_kernel", "attn_bf16_wide.hip")}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_traffic.json")
+ATTN_KERNELS = {1: ("attn_fwd_narrow_kernel", "attn_narrow.hip"),
+                2: ("attn_fwd_wide_kernel", "attn_wide.hip"),
+                3: ("attn_fwd_wide_kernel", "attn_wide.hip")}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_wide_traffic.json")
 
 
 def visible_entries(lengths, window: int) -> int:

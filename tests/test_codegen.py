@@ -65,7 +65,7 @@ def test_no_scratch_in_bf16_kernels(asm):
 
 
 def test_attention_two_waves_per_simd(asm):
-    text = asm["attn_bf16.hip"]
+    text = asm["attn_narrow.hip"]
     vgprs = [int(x) for x in re.findall(r"; NumVgprs: (\d+)", text)]
     assert vgprs and max(vgprs) <= 256, vgprs
     occ = [int(x) for x in re.findall(r"; Occupancy: (\d+)", text)]
@@ -78,7 +78,7 @@ def test_no_packed_fp32_valu(asm):
 
 
 def test_tile_copy_not_waited_before_reads(asm):
-    text = asm["attn_bf16.hip"]
+    text = asm["attn_narrow.hip"]
     lines = [l.strip() for l in text.splitlines()]
     lds_dma = [i for i, l in enumerate(lines) if l.startswith("global_load_lds_dwordx4")]
     assert lds_dma, "attention kernel copies tiles with global_load_lds_dwordx4"
@@ -122,7 +122,7 @@ def _main_loop(body):
 
 
 def test_wide_kernel_registers(asm):
-    text = asm["attn_bf16_wide.hip"]
+    text = asm["attn_wide.hip"]
     for key in ("NumVgprs", "NumAgprs"):
         vals = [int(x) for x in re.findall(rf"; {key}: (\d+)", text)]
         assert vals and max(vals) <= 256, (key, vals)
@@ -131,14 +131,14 @@ def test_wide_kernel_registers(asm):
 
 
 def test_wide_kernel_loop_keeps_accumulators_in_agprs(asm):
-    loop = _main_loop(_kernel(asm["attn_bf16_wide.hip"], "wide_kernelILb0"))
+    loop = _main_loop(_kernel(asm["attn_wide.hip"], "wide_kernelILb0"))
     assert sum(l.startswith("v_mfma") for l in loop) >= 64
     moves = [l for l in loop if l.startswith("v_accvgpr_")]
     assert not moves, moves[:4]
 
 
 def test_wide_kernel_waits_for_copies_only_at_barriers(asm):
-    loop = _main_loop(_kernel(asm["attn_bf16_wide.hip"], "wide_kernelILb0"))
+    loop = _main_loop(_kernel(asm["attn_wide.hip"], "wide_kernelILb0"))
     code = [l for l in loop if l and not l.startswith(";")]
     for i, l in enumerate(code):
         if l.startswith("s_waitcnt") and "vmcnt" in l:
@@ -153,7 +153,7 @@ def _regs(tok):
     return {(m.group(1), int(m.group(2)))} if m else set()
 
 
-@pytest.mark.parametrize("source, minimum", [("attn_bf16_wide.hip", 100), ("bwd_bf16.hip", 40)])
+@pytest.mark.parametrize("source, minimum", [("attn_wide.hip", 100), ("bwd.hip", 40)])
 def test_inline_asm_mfma_wait_states(asm, source, minimum):
     text = asm[source]
     lines = [l.strip() for l in text.splitlines()]
@@ -216,7 +216,7 @@ def _agpr_read_hazards(body):
 
 
 def test_agpr_reads_wait_for_mfma_results(asm):
-    for source in ("attn_bf16.hip", "attn_bf16_wide.hip", "bwd_bf16.hip"):
+    for source in ("attn_narrow.hip", "attn_wide.hip", "bwd.hip"):
         for kname, body in _kernels(asm[source]):
             hz = _agpr_read_hazards(body)
             assert not hz, (kname[:60], hz[:3])
@@ -227,7 +227,7 @@ def test_backward_loops_wait_for_copies_only_at_barriers(asm):
     # a vmcnt wait may only stand right before that barrier (the ring's own
     # wait): a wait between the copies and the step's LDS reads would drain
     # the copies just issued
-    text = asm["bwd_bf16.hip"]
+    text = asm["bwd.hip"]
     for marker in ("bwd_dkdv_kernel", "bwd_dq_kernel"):
         body = _kernel(text, marker)
         code = [l.split(";")[0].strip() for l in body.splitlines()]
