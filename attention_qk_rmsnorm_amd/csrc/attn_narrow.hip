@@ -139,26 +139,19 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
   if (!full) {
     // accumulator register r of chain i holds key kt + 32i + 4hf + k(r),
     // k(r) = 8(r/4) + r%4 in [0, 27]; the key is visible iff lo <= key <= tok
-    // (lo = document start, or tok - W + 1 under a window).  Bit k of vis[i]
-    // says whether offset k is visible (a run of ones: v_bfm), and each score
-    // takes a sign-extended bit extract and a bit select against -inf: no
-    // lane masks, so no VCC chain and no scalar-unit work per score.
+    // (lo = document start, or tok - W + 1 under a window)
     const int lo = window < 0 ? doc_start : max(doc_start, tok - window + 1);
     unsigned vis[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int base = kt + 32 * i + 4 * hf;
-      const int k0 = max(lo - base, 0), k1 = min(tok - base, 27);
-      vis[i] = (tok_ok && k1 >= k0) ? ((2u << (k1 - k0)) - 1u) << k0 : 0u;
+      vis[i] = tok_ok ? bit_run(max(lo - base, 0), min(tok - base, 27)) : 0u;
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int k = (r >> 2) * 8 + (r & 3);
-      // all ones for a visible key, zero for a masked one
-      const unsigned on0 = (unsigned)((int)(vis[0] << (31 - k)) >> 31);
-      const unsigned on1 = (unsigned)((int)(vis[1] << (31 - k)) >> 31);
-      s0[r] = __uint_as_float((__float_as_uint(s0[r]) & on0) | (~on0 & 0xff800000u));
-      s1[r] = __uint_as_float((__float_as_uint(s1[r]) & on1) | (~on1 & 0xff800000u));
+      s0[r] = keep_if(vis[0], k, s0[r]);
+      s1[r] = keep_if(vis[1], k, s1[r]);
     }
   }
   // column max of the raw scores (the lane pair l, l^32 holds one column)

@@ -106,24 +106,16 @@ __device__ __forceinline__ bool half_full(int kh, const Cols& c) {
 __device__ __forceinline__ void mask_half(int kh, const Cols& c, f32x16 (&s)[2]) {
   // accumulator register r holds key kh + 4hf + k(r), k(r) = 8(r/4) + r%4;
   // key u is visible to token t iff lo <= u <= t (lo = document start, or
-  // t - W + 1 under a window), i.e. lo - base <= k(r) <= t - base.  Bit k of
-  // vis says whether offset k is visible (a run of ones: v_bfm), and each
-  // score takes a sign-extended bit extract and a bit select against -inf: no
-  // lane masks, so no VCC chain and no scalar-unit work per score.  The key
-  // loop feeds the selected scores straight to v_exp_f32.
+  // t - W + 1 under a window), i.e. lo - base <= k(r) <= t - base.  The
+  // masked scores go straight to v_exp_f32 in the key loop.
   const int base = kh + 4 * c.hf;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int t = c.tok[cb];
     const int lo = c.window < 0 ? c.doc_start : max(c.doc_start, t - c.window + 1);
-    const int k0 = max(lo - base, 0), k1 = min(t - base, 27);
-    const unsigned vis = (c.ok[cb] && k1 >= k0) ? ((2u << (k1 - k0)) - 1u) << k0 : 0u;
+    const unsigned vis = c.ok[cb] ? bit_run(max(lo - base, 0), min(t - base, 27)) : 0u;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int k = (r >> 2) * 8 + (r & 3);
-      const unsigned on = (unsigned)((int)(vis << (31 - k)) >> 31);
-      s[cb][r] = __uint_as_float((__float_as_uint(s[cb][r]) & on) | (~on & 0xff800000u));
-    }
+    for (int r = 0; r < 16; ++r) s[cb][r] = keep_if(vis, (r >> 2) * 8 + (r & 3), s[cb][r]);
   }
 }
 

@@ -578,11 +578,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   auto mask = [&](int c, f32x16& s) {
     const int ta = c * tpt, tb = ta + tpt - 1;
     if (ta >= ub && tb <= ua_last) return;  // all visible (wave-uniform)
+    // column offset o in [0, 32) of the tile is token ta + (o >> log2G), seen
+    // by key u iff u <= token <= u_last: the offsets of one run, from
+    // (u - ta) << log2G to ((u_last - ta + 1) << log2G) - 1; register r of
+    // this lane holds offset 4hf + 8(r/4) + r%4
+    const int d0 = max(u - ta, 0), d1 = min(u_last - ta, 31);
+    const unsigned vis =
+        (u_ok && d1 >= d0) ? bit_run(d0 << log2G, min(((d1 + 1) << log2G) - 1, 31)) >> (4 * hf)
+                           : 0u;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = ta + ((8 * (r >> 2) + 4 * hf + (r & 3)) >> log2G);
-      s[r] += (u_ok && t >= u && t <= u_last) ? 0.f : -INFINITY;
-    }
+    for (int r = 0; r < 16; ++r) s[r] = keep_if(vis, 8 * (r >> 2) + (r & 3), s[r]);
   };
   // elements 2m, 2m + 1 of P and dS = P (dP - D), packed as B operands
   auto grads2 = [&](int m, const f32x16& s, const f32x16& dp, vec8<E> (&pb)[2],
@@ -903,11 +908,12 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
         dp = mfma32(rd<E>(buf + kKT + kh * 8192 + koff[kk]), dB[kk], dp);
       }
       if (!full) {
+        // key kt + 32kh + 4hf + 8(r/4) + r%4 is visible iff t_lo <= key <= t
+        // (t_lo is past every key for a padding token)
+        const int base = kt + 32 * kh + 4 * hf;
+        const unsigned vis = bit_run(max(t_lo - base, 0), min(t - base, 27));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
-          s[r] += (key >= t_lo && key <= t) ? 0.f : -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r) s[r] = keep_if(vis, 8 * (r >> 2) + (r & 3), s[r]);
       }
       vec8<E> sb[2];
 #pragma unroll

@@ -69,6 +69,27 @@ __device__ __forceinline__ float lane_pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// ---- band masks ------------------------------------------------------------
+// Register r of a lane's 32x32 MFMA accumulator holds row 8(r/4) + r%4 + 4hf
+// (hf = lane / 32) of its block.  A mask is built once per lane and block as
+// a word whose bit k says whether row offset k (from the lane's first row) is
+// visible; the visible rows of a causal, window or document band always form
+// one run of offsets.
+
+// Bits lo .. hi of a word, none when hi < lo (0 <= lo <= 31 when hi >= lo,
+// hi <= 31).
+__device__ __forceinline__ unsigned bit_run(int lo, int hi) {
+  return hi >= lo ? ((2u << (hi - lo)) - 1u) << lo : 0u;
+}
+
+// s when bit k of vis is set, -inf otherwise: a sign-extended bit extract
+// (v_bfe_i32) and a bit select (v_bitop3).  No lane mask is formed, so there
+// is neither a VCC dependency chain nor scalar-unit work per score.
+__device__ __forceinline__ float keep_if(unsigned vis, int k, float s) {
+  const unsigned on = (unsigned)((int)(vis << (31 - k)) >> 31);
+  return __uint_as_float((__float_as_uint(s) & on) | (~on & 0xff800000u));
+}
+
 // ---- 16-bit element helpers (E = bf16 or f16) -----------------------------
 
 // C += A B on the 32x32x16 MFMA of the element type (fp32 accumulation).
