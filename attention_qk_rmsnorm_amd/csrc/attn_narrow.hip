@@ -145,7 +145,7 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int base = kt + 32 * i + 4 * hf;
-      vis[i] = tok_ok ? bit_run(max(lo - base, 0), min(tok - base, 27)) : 0u;
+      vis[i] = bit_run(max(lo - base, 0), tok_ok ? min(tok - base, 27) : -1);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -280,8 +280,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
   // the compiler prove the next tile's LDS copy does not alias the buffer
   // being read, so it does not wait for that copy before the reads
   const int wave_u = __builtin_amdgcn_readfirstlane(wave) & (kWaves - 1);
-  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
-  __syncthreads();
+  // RoPE angles: a table of the block's tokens in the second tile buffer
+  // (unused until the key loop's first barrier) when it fits, i.e. for G >= 4;
+  // otherwise each lane computes its own from the frequencies in s_invf
+  const bool rope_tab = use_rope && m_tok * kRopeRow <= kBuf;
+  if (use_rope && !rope_tab) {
+    if (tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
+    __syncthreads();
+  }
 
   ColState<E> st;
   // ---- Q: load, RMSNorm, RoPE, round to E B operands -----------------------
@@ -304,36 +310,47 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
     if (kt_lo < hi)
       issue_tile(kimg + (size_t)kt_lo * 256, vimg + (size_t)kt_lo * 256, tid, wave_u, lds);
     __builtin_amdgcn_sched_barrier(0);
+    if (rope_tab) {
+      rope_table(lds + kBuf, tid, kThreads, m_tok, a, a_end, doc_start, theta);
+      barrier_keep_copies();
+    }
 
     float x[64];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[8 * kk + e] = tok_ok ? (float)qraw[kk][e] : 0.f;
+      for (int e = 0; e < 8; ++e) x[8 * kk + e] = (float)qraw[kk][e];
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
     ss = lane_pair_sum(ss);
-    const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
+    // the norm factor carries scale * log2(e) (RoPE is linear, so the order
+    // does not matter), and a padding column, which loaded a real token's
+    // row, gets a zero factor: zero operands
+    const float inv = tok_ok ? c_log2 / sqrtf(ss * (1.0f / kHeadDim) + eps) : 0.f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) x[i] *= inv * w[i];
     if (use_rope && tok_ok) {
-      const int p = tok - doc_start;
+      if (rope_tab) {
+        rope_from_table(lds + kBuf + (tok - a) * kRopeRow, hf, x);
+      } else {
+        const int p = tok - doc_start;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float sn, cs;
-          rope_sincos_rev(p, s_invf[16 * kk + 8 * hf + e], &sn, &cs);
-          const float x1 = x[8 * kk + e], x2 = x[8 * (kk + 4) + e];
-          x[8 * kk + e] = x1 * cs - x2 * sn;
-          x[8 * (kk + 4) + e] = x2 * cs + x1 * sn;
-        }
+          for (int e = 0; e < 8; ++e) {
+            float sn, cs;
+            rope_sincos_rev(p, s_invf[16 * kk + 8 * hf + e], &sn, &cs);
+            const float x1 = x[8 * kk + e], x2 = x[8 * (kk + 4) + e];
+            x[8 * kk + e] = x1 * cs - x2 * sn;
+            x[8 * (kk + 4) + e] = x2 * cs + x1 * sn;
+          }
+      }
     }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) st.qf[kk][e] = (E)(x[8 * kk + e] * c_log2);
+      for (int e = 0; e < 8; ++e) st.qf[kk][e] = (E)x[8 * kk + e];
   }
 
   // running state in the log2 domain: m = max(sink, scores) * log2(e) scaled,

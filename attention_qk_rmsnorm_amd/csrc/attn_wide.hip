@@ -113,7 +113,8 @@ __device__ __forceinline__ void mask_half(int kh, const Cols& c, f32x16 (&s)[2])
   for (int cb = 0; cb < 2; ++cb) {
     const int t = c.tok[cb];
     const int lo = c.window < 0 ? c.doc_start : max(c.doc_start, t - c.window + 1);
-    const unsigned vis = c.ok[cb] ? bit_run(max(lo - base, 0), min(t - base, 27)) : 0u;
+    // (a padding column sees nothing: an empty run)
+    const unsigned vis = bit_run(max(lo - base, 0), c.ok[cb] ? min(t - base, 27) : -1);
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[cb][r] = keep_if(vis, (r >> 2) * 8 + (r & 3), s[cb][r]);
   }
@@ -418,9 +419,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_wide_kernel(
   // the compiler prove a tile copy does not alias the slots being read, so it
   // does not wait for that copy before the reads
   const int wave_u = __builtin_amdgcn_readfirstlane(wave) & (kWaves - 1);
-  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
-  if (tid == 0) s_bad = 0;
-  __syncthreads();
+  // RoPE angles: a table of the block's tokens in the third LDS slot (its
+  // first copy is issued after the key loop's first barrier) when it fits,
+  // i.e. for G >= 8; otherwise each lane computes its own from the
+  // frequencies in s_invf
+  const bool rope_tab = use_rope && m_tok * kRopeRow <= kSlot;
+  if (tid == 0) s_bad = 0;  // read after the key loop's barriers
+  if (use_rope && !rope_tab) {
+    if (tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
+    __syncthreads();
+  }
 
   WaveState<E> st;
   float sink_raw[2], self_score[2];
@@ -466,6 +474,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_wide_kernel(
       }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (rope_tab) {
+      rope_table(lds + 2 * kSlot, tid, kThreads, m_tok, a, a_end, doc_start, theta);
+      barrier_keep_copies();
+    }
 
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
@@ -473,31 +485,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_wide_kernel(
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[8 * kk + e] = c.ok[cb] ? (float)qraw[cb][kk][e] : 0.f;
+        for (int e = 0; e < 8; ++e) x[8 * kk + e] = (float)qraw[cb][kk][e];
       float ss = 0.f;
 #pragma unroll
       for (int i = 0; i < 64; ++i) ss += x[i] * x[i];
       ss = lane_pair_sum(ss);
-      const float inv = 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps);
+      // the norm factor carries scale * log2(e) (RoPE is linear, so the order
+      // does not matter), and a padding column, which loaded a real token's
+      // row, gets a zero factor: zero operands and a zero self score
+      const float inv = c.ok[cb] ? c_log2 / sqrtf(ss * (1.0f / kHeadDim) + eps) : 0.f;
 #pragma unroll
       for (int i = 0; i < 64; ++i) x[i] *= inv * w[i];
       if (use_rope && c.ok[cb]) {
-        const int p = c.tok[cb] - doc_start;
+        if (rope_tab) {
+          rope_from_table(lds + 2 * kSlot + (c.tok[cb] - a) * kRopeRow, hf, x);
+        } else {
+          const int p = c.tok[cb] - doc_start;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+          for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            float sn, cs;
-            rope_sincos_rev(p, s_invf[16 * kk + 8 * hf + e], &sn, &cs);
-            const float x1 = x[8 * kk + e], x2 = x[8 * (kk + 4) + e];
-            x[8 * kk + e] = x1 * cs - x2 * sn;
-            x[8 * (kk + 4) + e] = x2 * cs + x1 * sn;
-          }
+            for (int e = 0; e < 8; ++e) {
+              float sn, cs;
+              rope_sincos_rev(p, s_invf[16 * kk + 8 * hf + e], &sn, &cs);
+              const float x1 = x[8 * kk + e], x2 = x[8 * (kk + 4) + e];
+              x[8 * kk + e] = x1 * cs - x2 * sn;
+              x[8 * (kk + 4) + e] = x2 * cs + x1 * sn;
+            }
+        }
       }
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st.qf[cb][kk][e] = (E)(x[8 * kk + e] * c_log2);
+        for (int e = 0; e < 8; ++e) st.qf[cb][kk][e] = (E)x[8 * kk + e];
         // park the Q operands in AGPRs (MFMAs read them from there), which
         // leaves the VGPRs to the scores, weights and operand prefetch
         asm volatile("" : "+a"(st.qf[cb][kk]));
@@ -508,7 +527,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_wide_kernel(
         for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
           for (int e = 0; e < 8; ++e) dot += x[8 * kk + e] * (float)kself[cb][kk][e];
-        self_score[cb] = lane_pair_sum(dot) * c_log2;
+        self_score[cb] = lane_pair_sum(dot);
       }
     }
   }

@@ -68,14 +68,6 @@ constexpr int kColBufs = 8;
 constexpr int kColCopyOps = 2 * kCT / (16 * kThreads) + 1;
 static_assert(kColCopyOps * (kColBufs - 2) < 64, "vmcnt holds 6 bits");
 
-// Workgroup barrier that leaves outstanding global loads (the LDS copies of
-// later tiles) in flight.  The LDS reads of the finished tile have all been
-// consumed by MFMAs before it is reached; lgkmcnt(0) makes that explicit.
-// The memory clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void barrier_keep_copies() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // s_waitcnt vmcnt(N) (other counters untouched); N < 64
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -582,10 +574,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     // by key u iff u <= token <= u_last: the offsets of one run, from
     // (u - ta) << log2G to ((u_last - ta + 1) << log2G) - 1; register r of
     // this lane holds offset 4hf + 8(r/4) + r%4
-    const int d0 = max(u - ta, 0), d1 = min(u_last - ta, 31);
+    // (d0 and d1 are clamped before the shifts; a key no column sees, or a
+    // padding key, gets an empty run)
+    const int d0 = min(max(u - ta, 0), 32), d1 = u_ok ? min(u_last - ta, 31) : -1;
     const unsigned vis =
-        (u_ok && d1 >= d0) ? bit_run(d0 << log2G, min(((d1 + 1) << log2G) - 1, 31)) >> (4 * hf)
-                           : 0u;
+        bit_run(d0 << log2G, d1 >= 0 ? min(((d1 + 1) << log2G) - 1, 31) : -1) >> (4 * hf);
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = keep_if(vis, 8 * (r >> 2) + (r & 3), s[r]);
   };

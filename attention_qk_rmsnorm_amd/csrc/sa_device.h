@@ -42,6 +42,60 @@ __device__ inline void rope_sincos_rev(int p, double inv_freq_rev, float* s, flo
   *c = __builtin_amdgcn_cosf(rf);
 }
 
+// Workgroup barrier that leaves outstanding global loads (LDS copies of later
+// tiles, operand loads) in flight: it waits only for the wave's own LDS
+// accesses (lgkmcnt(0)), whose results the code before it has consumed or
+// stored.  The memory clobber keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void barrier_keep_copies() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---- RoPE angles of a block of query tokens --------------------------------
+// The G query heads of a token rotate by the same angles, so a workgroup
+// writes (cos, sin) of each (token, frequency) pair of its tokens once into an
+// LDS table and every lane reads its 32 pairs from there.  Row r (token a + r)
+// is kRopeRow bytes: 64 pairs and 16 bytes more, so that the rows of the
+// different tokens a wave reads start 4 banks apart.
+constexpr int kRopeRow = 64 * 8 + 16;
+
+// Fill rows [0, rows) of the table for the tokens a + r < a_end of a document
+// that starts at doc_start (positions a + r - doc_start), head_dim 128:
+// thread tid computes frequency i = tid % 64, theta^(-i/64) in revolutions,
+// for rows tid / 64, tid / 64 + nthreads / 64, ...
+__device__ inline void rope_table(char* tab, int tid, int nthreads, int rows, int a, int a_end,
+                                  int doc_start, double theta) {
+  const int i = tid & 63;
+  const double invf = pow(theta, -(double)i / 64.0) * kInvTwoPi;
+  for (int r = tid >> 6; r < rows && a + r < a_end; r += nthreads >> 6) {
+    float sn, cs;
+    rope_sincos_rev(a + r - doc_start, invf, &sn, &cs);
+    *reinterpret_cast<float2*>(tab + r * kRopeRow + 8 * i) = make_float2(cs, sn);
+  }
+}
+
+// Rotate the 64 channels a lane holds (x[8kk + e] = channel 16kk + 8hf + e,
+// NeoX partners kk and kk + 4) by the angles of table row `row`.
+__device__ __forceinline__ void rope_from_table(const char* row, int hf, float (&x)[64]) {
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    // pairs 16kk + 8hf + e, e < 8: four 16-byte reads of (cos, sin, cos, sin)
+    const char* p = row + 128 * kk + 64 * hf;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 cs = *reinterpret_cast<const float4*>(p + 16 * j);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = 2 * j + u;
+        const float c = u ? cs.z : cs.x, sn = u ? cs.w : cs.y;
+        const float x1 = x[8 * kk + e], x2 = x[8 * (kk + 4) + e];
+        x[8 * kk + e] = x1 * c - x2 * sn;
+        x[8 * (kk + 4) + e] = x2 * c + x1 * sn;
+      }
+    }
+  }
+}
+
 // Layout of the key/value tiles the prologue writes and the attention kernel
 // copies verbatim into LDS (64 keys per tile, 16-byte chunks XOR-swizzled so
 // the MFMA operand reads, 32 lanes on 32 rows at one column, hit distinct
@@ -77,9 +131,11 @@ __device__ __forceinline__ float lane_pair_sum(float x) {
 // one run of offsets.
 
 // Bits lo .. hi of a word, none when hi < lo (0 <= lo <= 31 when hi >= lo,
-// hi <= 31).
+// hi <= 31).  The shift counts are masked so that both sides of the final
+// select are defined and the compiler forms a select, not a branch.
 __device__ __forceinline__ unsigned bit_run(int lo, int hi) {
-  return hi >= lo ? ((2u << (hi - lo)) - 1u) << lo : 0u;
+  const unsigned run = ((2u << ((hi - lo) & 31)) - 1u) << (lo & 31);
+  return hi >= lo ? run : 0u;
 }
 
 // s when bit k of vis is set, -inf otherwise: a sign-extended bit extract

@@ -113,12 +113,15 @@ def _kernel(text, marker):
 
 
 def _main_loop(body):
-    """Lines of the first loop (from its header label to the branch back)."""
+    """Lines of the first loop with MFMAs in it (from its header label to the
+    branch back): the key loop, past any set-up loops."""
     lines = [l.strip() for l in body.splitlines()]
-    head = next(i for i, l in enumerate(lines) if "Loop Header" in l)
-    label = lines[head].split(":")[0]
-    back = max(i for i, l in enumerate(lines) if l.startswith("s_") and l.endswith(" " + label))
-    return lines[head:back + 1]
+    for head in (i for i, l in enumerate(lines) if "Loop Header" in l):
+        label = lines[head].split(":")[0]
+        back = max(i for i, l in enumerate(lines) if l.startswith("s_") and l.endswith(" " + label))
+        if any(l.startswith("v_mfma") for l in lines[head:back + 1]):
+            return lines[head:back + 1]
+    raise AssertionError("no loop with MFMAs")
 
 
 def test_wide_kernel_registers(asm):
