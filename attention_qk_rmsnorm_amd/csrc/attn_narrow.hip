@@ -92,8 +92,13 @@ __device__ __forceinline__ vec8<E> neg_ref_operand(float m_ref, int hf) {
 // One 64-key tile for one wave: S^T = K Q^T, masked online softmax with the
 // sink-seeded state, O^T += V^T P^T.  LDS operand reads are issued one step
 // ahead of the MFMAs that consume them; sched_barrier keeps the compiler from
-// sinking them back next to their use.
-template <typename E, int BUF>
+// sinking them back next to their use.  HALVES says which 32-key halves hold
+// a key any of the wave's tokens can see (bit 0: keys kt .. kt + 31, bit 1:
+// kt + 32 .. kt + 63): a dead half gets no MFMAs, exps or PV steps, which is
+// exact, as its weights would all be zero.  On short documents a block's first
+// tile often starts half a tile before the document and its last ends half a
+// tile past the wave's tokens.
+template <typename E, int BUF, int HALVES>
 __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8],
                                             const int (&voff)[4], ColState<E>& st, int kt,
                                             int hf, int tok, bool tok_ok, int tw0, int tw1,
@@ -102,35 +107,41 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
   const char* vbuf = kbuf + kTileK;
   auto rd = [](const char* p) { return *reinterpret_cast<const vec8<E>*>(p); };
 
+  constexpr bool kL0 = HALVES & 1, kL1 = HALVES & 2;
+  // PV steps [kJ0, kJ1): step j covers keys 16j .. 16j + 15
+  constexpr int kJ0 = kL0 ? 0 : 2, kJ1 = kL1 ? 4 : 2;
+
   // ---- S^T = K Q^T: two 32-key chains, K fragments one step ahead --------
   f32x16 s0, s1;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    s0[r] = 0.f;
-    s1[r] = 0.f;
+    s0[r] = kL0 ? 0.f : -INFINITY;
+    s1[r] = kL1 ? 0.f : -INFINITY;
   }
-  vec8<E> a0 = rd(kbuf + koff[0]), a1 = rd(kbuf + 8192 + koff[0]);
+  vec8<E> a0, a1;
+  if constexpr (kL0) a0 = rd(kbuf + koff[0]);
+  if constexpr (kL1) a1 = rd(kbuf + 8192 + koff[0]);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     vec8<E> n0 = a0, n1 = a1;
     if (kk < 7) {
-      n0 = rd(kbuf + koff[kk + 1]);
-      n1 = rd(kbuf + 8192 + koff[kk + 1]);
+      if constexpr (kL0) n0 = rd(kbuf + koff[kk + 1]);
+      if constexpr (kL1) n1 = rd(kbuf + 8192 + koff[kk + 1]);
     }
     __builtin_amdgcn_sched_barrier(0);
-    s0 = mfma32(a0, st.qf[kk], s0);
-    s1 = mfma32(a1, st.qf[kk], s1);
+    if constexpr (kL0) s0 = mfma32(a0, st.qf[kk], s0);
+    if constexpr (kL1) s1 = mfma32(a1, st.qf[kk], s1);
     a0 = n0;
     a1 = n1;
   }
   // reference step: every score of a column minus m_ref (exact: m_ref is an
   // E value), so the accumulators hold s * scale * log2e - m_ref
-  s0 = mfma32(st.ones_a, st.negm_b, s0);
-  s1 = mfma32(st.ones_a, st.negm_b, s1);
+  if constexpr (kL0) s0 = mfma32(st.ones_a, st.negm_b, s0);
+  if constexpr (kL1) s1 = mfma32(st.ones_a, st.negm_b, s1);
   // V fragments of the first PV step, read while the softmax runs
   vec8<E> va[4];
 #pragma unroll
-  for (int dd = 0; dd < 4; ++dd) va[dd] = rd(vbuf + dd * 4096 + voff[0]);
+  for (int dd = 0; dd < 4; ++dd) va[dd] = rd(vbuf + dd * 4096 + voff[kJ0]);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- band mask, only on tiles that cross a document, causal or window edge
@@ -150,16 +161,20 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int k = (r >> 2) * 8 + (r & 3);
-      s0[r] = keep_if(vis[0], k, s0[r]);
-      s1[r] = keep_if(vis[1], k, s1[r]);
+      if constexpr (kL0) s0[r] = keep_if(vis[0], k, s0[r]);
+      if constexpr (kL1) s1[r] = keep_if(vis[1], k, s1[r]);
     }
   }
   // column max of the raw scores (the lane pair l, l^32 holds one column)
   float mx = -INFINITY;
+  if constexpr (kL0) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+  }
+  if constexpr (kL1) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
+  }
   mx = lane_pair_max(mx);  // relative to the reference (or absolute while none)
 
   // Lazy rescale: the reference point m_run moves only when a score exceeds
@@ -182,8 +197,8 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
       for (int r = 0; r < 16; ++r) st.o[dd][r] *= alpha;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      s0[r] -= delta;
-      s1[r] -= delta;
+      if constexpr (kL0) s0[r] -= delta;
+      if constexpr (kL1) s1[r] -= delta;
     }
   }
 
@@ -207,18 +222,18 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
     }
     return pb;
   };
-  vec8<E> pb = weights(0);
+  vec8<E> pb = weights(kJ0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = kJ0; j < kJ1; ++j) {
     vec8<E> vn[4];
-    if (j < 3) {
+    if (j + 1 < kJ1) {
 #pragma unroll
       for (int dd = 0; dd < 4; ++dd) vn[dd] = rd(vbuf + dd * 4096 + voff[j + 1]);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dd = 0; dd < 4; ++dd) st.o[dd] = mfma32(va[dd], pb, st.o[dd]);
-    if (j < 3) {
+    if (j + 1 < kJ1) {
       pb = weights(j + 1);
 #pragma unroll
       for (int dd = 0; dd < 4; ++dd) va[dd] = vn[dd];
@@ -388,12 +403,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
       if (kt + kKeyTile < hi)
         issue_tile(kimg + (size_t)(kt + kKeyTile) * 256, vimg + (size_t)(kt + kKeyTile) * 256, tid,
                    wave_u, lds + (b ^ 1) * kBuf);
+      // the wave's visible keys are [wlo, tw1 - 1]; a tile that reaches them
+      // has at least one live half
       const bool active = (tw0 < tw1) && (kt < tw1) && (kt + kKeyTile > wlo);
       if (active) {
-        if (b == 0)
-          attend_tile<E, 0>(lds, koff, voff, st, kt, hf, tok, tok_ok, tw0, tw1, doc_start, window);
-        else
-          attend_tile<E, 1>(lds, koff, voff, st, kt, hf, tok, tok_ok, tw0, tw1, doc_start, window);
+        const bool live0 = kt + 31 >= wlo, live1 = kt + 32 < tw1;
+#define SA_TILE(B, H) \
+  attend_tile<E, B, H>(lds, koff, voff, st, kt, hf, tok, tok_ok, tw0, tw1, doc_start, window)
+        if (b == 0) {
+          if (live0 && live1) SA_TILE(0, 3);
+          else if (live0) SA_TILE(0, 1);
+          else SA_TILE(0, 2);
+        } else {
+          if (live0 && live1) SA_TILE(1, 3);
+          else if (live0) SA_TILE(1, 1);
+          else SA_TILE(1, 2);
+        }
+#undef SA_TILE
       }
       kt += kKeyTile;
     }
