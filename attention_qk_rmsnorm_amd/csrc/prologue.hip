@@ -33,13 +33,12 @@ constexpr int kLdsPrefix = 4096;  // documents whose prefix fits in LDS
 
 // Varlen schedule.  sched[0] = number of items; items (int2 at sched + 4) hold
 // (document, block index in document) in descending order of block position.
-// prefix_g is global scratch of D + 1 ints used when D + 1 > kLdsPrefix.
+// s_scan (kThreads ints) and s_pref (kLdsPrefix ints) are LDS arrays; prefix_g
+// is global scratch of D + 1 ints used when D + 1 > kLdsPrefix.
 __device__ void build_schedule(const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_end,
                                int D, int m_tok,
                                int32_t* __restrict__ sched, int64_t items_ub,
-                               int32_t* __restrict__ prefix_g) {
-  __shared__ int s_scan[kThreads];
-  __shared__ int s_pref[kLdsPrefix];
+                               int32_t* __restrict__ prefix_g, int* s_scan, int* s_pref) {
   const int tid = threadIdx.x;
   const bool in_lds = D + 1 <= kLdsPrefix;
   int* pref = in_lds ? s_pref : prefix_g;
@@ -92,16 +91,24 @@ __global__ __launch_bounds__(kThreads) void prologue_16_kernel(
     int Hkv, int64_t t_pad, int m_tok, int m_tok_wide, float eps, double theta,
     int use_rope, E* __restrict__ khat, E* __restrict__ vt,
     int32_t* __restrict__ sched, int32_t* __restrict__ sched_wide) {
+  // One LDS buffer: the V tile of a key-tile block, or the scan and prefix
+  // arrays of the two schedule blocks (so the key-tile blocks, nearly all of
+  // the grid, do not reserve the schedule's arrays: 8 blocks fit on a CU).
+  constexpr int kVBytes = kKeyTile * (kHeadDim + 8) * (int)sizeof(E);
+  constexpr int kSchedBytes = (kThreads + kLdsPrefix) * (int)sizeof(int);
+  __shared__ __attribute__((aligned(16))) char s_mem[kVBytes > kSchedBytes ? kVBytes : kSchedBytes];
   if (blockIdx.x < 2) {
     const bool wide = blockIdx.x == 1;
     const int mt = wide ? m_tok_wide : m_tok;
     const int64_t items_ub = T / mt + D;
     int32_t* sc = wide ? sched_wide : sched;
-    build_schedule(cu, cu_end, D, mt, sc, items_ub, sc + 4 + 2 * items_ub);
+    int* s_scan = reinterpret_cast<int*>(s_mem);
+    build_schedule(cu, cu_end, D, mt, sc, items_ub, sc + 4 + 2 * items_ub, s_scan,
+                   s_scan + kThreads);
     return;
   }
   __shared__ double s_invf[64];
-  __shared__ __attribute__((aligned(16))) E s_v[kKeyTile][kHeadDim + 8];
+  auto s_v = reinterpret_cast<E(*)[kHeadDim + 8]>(s_mem);
 
   const int tid = threadIdx.x;
   const int blk = blockIdx.x - 2;
@@ -110,15 +117,61 @@ __global__ __launch_bounds__(kThreads) void prologue_16_kernel(
   const int t0 = tile * kKeyTile;
 
   // inv_freq_i / 2pi with inv_freq_i = theta^(-2i/128), i < 64: NeoX pairs
-  // channel i with i + 64
-  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
+  // channel i with i + 64 (wave 1: wave 0 runs the document search below)
+  if (use_rope && tid >= 64 && tid < 128)
+    s_invf[tid - 64] = pow(theta, -(double)(tid - 64) / 64.0) * kInvTwoPi;
 
-  // real tokens of the tile: inside [0, T) and not document padding (padded
-  // rows are written as zeros, whatever the input holds there)
-  __shared__ int s_real[kKeyTile];
+  // Documents of the tile's tokens.  Wave 0 finds the document d0 of the
+  // first token (the largest d < D with cu[d] <= t0) level by level: each
+  // lane tests one of 64 evenly spaced candidates and a ballot keeps the last
+  // one that passes (cu is non-decreasing), so D <= 4096 takes two dependent
+  // loads instead of a binary search's 12.  cu[d0 .. d0 + 64] then go to LDS,
+  // where each token finds its own document; a tile that crosses more than 64
+  // document starts (empty documents) falls back to a search in memory.
+  __shared__ int s_d0;
+  __shared__ int s_cu[kKeyTile + 1];
+  __shared__ int s_real[kKeyTile];  // token inside [0, T) and not document padding
+  __shared__ int s_pos0[kKeyTile];  // start of the token's document (RoPE positions)
+  if (tid < 64) {
+    int lo = 0, hi = D - 1;  // cu[lo] <= t0 (cu[0] == 0)
+    const int tq = min(t0, T - 1);
+    while (hi > lo) {
+      const int step = (hi - lo + 64) / 64;
+      const int idx = lo + tid * step;
+      const bool le = idx <= hi && cu[idx] <= tq;
+      const int cnt = __popcll(__ballot(le));
+      lo += (cnt - 1) * step;
+      hi = min(hi, lo + step - 1);
+    }
+    if (tid == 0) s_d0 = lo;
+  }
+  __syncthreads();
+  const int d0 = s_d0;
+  if (tid <= kKeyTile) s_cu[tid] = d0 + tid <= D ? cu[d0 + tid] : INT_MAX;
+  __syncthreads();
   if (tid < kKeyTile) {
     const int t = t0 + tid;
-    s_real[tid] = t < T && t < cu_end[doc_of_token(cu, D, t)];
+    int real = 0, pos0 = 0;
+    if (t < T) {
+      const int jmax = min(kKeyTile, D - 1 - d0);  // documents d0 .. d0 + jmax
+      int d;
+      if (jmax == kKeyTile && s_cu[kKeyTile] <= t) {
+        d = doc_of_token(cu, D, t);
+        pos0 = cu[d];
+      } else {
+        int a = 0, b = jmax;  // largest j <= jmax with s_cu[j] <= t
+        while (a < b) {
+          const int mid = (a + b + 1) >> 1;
+          if (s_cu[mid] <= t) a = mid;
+          else b = mid - 1;
+        }
+        d = d0 + a;
+        pos0 = s_cu[a];
+      }
+      real = t < cu_end[d];
+    }
+    s_real[tid] = real;
+    s_pos0[tid] = pos0;
   }
   __syncthreads();
 
@@ -169,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void prologue_16_kernel(
       x[8 + e] *= inv * knorm_w[64 + 8 * c + e];
     }
     if (use_rope && real) {
-      const int p = t - cu[doc_of_token(cu, D, t)];
+      const int p = t - s_pos0[tt];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float sn, cs;

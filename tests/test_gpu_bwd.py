@@ -31,6 +31,13 @@ def test_ragged_documents(window, use_rope):
     check_bwd_parity(custom_inputs(RAGGED), window, use_rope, label=f"W={window}")
 
 
+def test_many_and_empty_documents():
+    # a run of 80 empty documents inside one key tile and 4,315 documents in all
+    lengths = [37] + [0] * 80 + [1] * 20 + [0] * 3 + [5] * 10 + [2, 0, 3] * 1400 + [90]
+    _say(f"case bwd many documents ({len(lengths)})")
+    check_bwd_parity(custom_inputs(lengths), 3, True, label="many docs W=3")
+
+
 @pytest.mark.parametrize("heads", [(32, 4), (8, 8), (32, 1), (4, 2), (16, 16)])
 def test_group_sizes(heads):
     _say(f"case bwd heads={heads}")

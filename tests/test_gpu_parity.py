@@ -54,6 +54,22 @@ def test_bf16_ragged_documents(window, use_rope):
     check_parity(inp, window, use_rope, label=f"ragged W={window}")
 
 
+# 80 empty documents inside one 64-token key tile (more document starts than
+# tokens: the prologue's per-tile document lookup leaves its window of 65
+# starts and searches memory) and 4,315 documents in all (more than the 4,096
+# starts the schedule keeps in LDS, and a third level of the lookup's search)
+MANY_DOCS = [37] + [0] * 80 + [1] * 20 + [0] * 3 + [5] * 10 + [2, 0, 3] * 1400 + [90]
+
+
+@pytest.mark.parametrize("window,use_rope", [(-1, False), (3, True)])
+@pytest.mark.parametrize("tile", [1, 2])  # narrow, wide
+def test_bf16_many_and_empty_documents(window, use_rope, tile):
+    _say(f"case bf16 many documents ({len(MANY_DOCS)}) W={window} rope={use_rope} tile={tile}")
+    inp = custom_inputs(MANY_DOCS)
+    check_parity(inp, window, use_rope, label=f"many docs W={window} tile={tile}",
+                 tile_config=tile)
+
+
 @pytest.mark.parametrize("heads", [(32, 4), (8, 8), (16, 4), (32, 1), (16, 1), (4, 2)])
 def test_bf16_group_sizes(heads):
     _say(f"case bf16 heads={heads}")
