@@ -257,12 +257,20 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
     int Hkv, int n_kt, float eps, double theta, int use_rope, char* __restrict__ keys) {
   __shared__ double s_invf[64];
   __shared__ int s_real[kKeyTile];  // inside [0, T) and not document padding
+  __shared__ int s_pos0[kKeyTile];  // start of the token's document (RoPE positions)
   const int tid = threadIdx.x;
   const int tile = blockIdx.x / Hkv, g = blockIdx.x - tile * Hkv;
   const int t0 = tile * kKeyTile;
   char* img = keys + ((size_t)g * n_kt + tile) * kKeyTileBytes;
-  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
-  if (tid < kKeyTile) s_real[tid] = t0 + tid < T && t0 + tid < cu_end[doc_of_token(cu, D, t0 + tid)];
+  // (wave 1: wave 0 looks up the documents)
+  if (use_rope && tid >= 64 && tid < 128)
+    s_invf[tid - 64] = pow(theta, -(double)(tid - 64) / 64.0) * kInvTwoPi;
+  if (tid < kKeyTile) {
+    const int t = t0 + tid, t_hi = min(t0 + kKeyTile, T) - 1;
+    const int n = t0 < T ? doc_of_token_wave(cu, D, min(t, t_hi), min(t0, t_hi), t_hi) : 0;
+    s_real[tid] = t < T && t < cu_end[n];
+    s_pos0[tid] = t < T ? cu[n] : 0;
+  }
   __syncthreads();
   // V rows straight into the V image
 #pragma unroll
@@ -308,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
       x[8 + e] *= inv * knorm_w[64 + 8 * c + e];
     }
     if (use_rope && real) {
-      const int p = t - cu[doc_of_token(cu, D, t)];
+      const int p = t - s_pos0[r];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float sn, cs;
@@ -346,16 +354,24 @@ __global__ __launch_bounds__(kThreads) void bwd_cols_kernel(
   const int ct = blockIdx.x / Hkv, g = blockIdx.x - ct * Hkv;
   const int tpt = 32 >> log2G;
   char* img = cols + ((size_t)g * n_ct + ct) * kColTileBytes;
-  if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
+  // (wave 1, so that wave 0's document lookup below does not wait behind it)
+  if (use_rope && tid >= 64 && tid < 128)
+    s_invf[tid - 64] = pow(theta, -(double)(tid - 64) / 64.0) * kInvTwoPi;
   __syncthreads();
 
   // column col = 8 lanes: lane c holds channels 8c.. and 64+8c..
   const int col = tid >> 3, c = tid & 7;
   const int t = ct * tpt + (col >> log2G);
   const int h = g * G + (col & (G - 1));
+  // the token's document; wave w holds columns 8w .. 8w + 7, so its tokens lie
+  // in [ct * tpt + (8w >> log2G), ct * tpt + ((8w + 7) >> log2G)]
+  const int w8 = (tid >> 6) * 8;
+  const int tw_lo = min(ct * tpt + (w8 >> log2G), T - 1);
+  const int tw_hi = min(ct * tpt + ((w8 + 7) >> log2G), T - 1);
+  const int n = doc_of_token_wave(cu, D, min(t, T - 1), tw_lo, tw_hi);
   // a real query: inside [0, T) and not document padding (padded rows have no
   // gradient: their out is the constant 0)
-  const bool ok = t < T && t < cu_end[doc_of_token(cu, D, t)];
+  const bool ok = t < T && t < cu_end[n];
   float x[16], y[16], o[16];
   if (ok) {
     const size_t row = ((size_t)t * Hq + h) * kHeadDim;
@@ -397,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void bwd_cols_kernel(
     x[8 + e] *= inv * qnorm_w[64 + 8 * c + e];
   }
   if (use_rope && ok) {
-    const int p = t - cu[doc_of_token(cu, D, t)];
+    const int p = t - cu[n];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float sn, cs;

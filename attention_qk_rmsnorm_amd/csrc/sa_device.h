@@ -18,6 +18,42 @@ __device__ inline int doc_of_token(const int32_t* __restrict__ cu, int D, int t)
   return lo;
 }
 
+// Document of token t for the lanes of one wave, called by all 64 lanes, with
+// every lane's t inside [t_lo, t_hi] (wave-uniform bounds in [0, T)).  Lanes
+// 0-31 narrow down the document of t_lo and lanes 32-63 that of t_hi: each
+// lane tests one of 32 evenly spaced document starts per level and a ballot
+// keeps the last one that passes (cu is non-decreasing), so up to 1,024
+// documents take two dependent loads and up to 32,768 three, where a binary
+// search takes 10 or 15.  Each lane then searches between the two results,
+// which for a wave's few consecutive tokens are mostly the same document.
+__device__ inline int doc_of_token_wave(const int32_t* __restrict__ cu, int D, int t, int t_lo,
+                                        int t_hi) {
+  const int lane = __lane_id();
+  const int half = lane >> 5, sub = lane & 31;
+  const int tq = half ? t_hi : t_lo;
+  int lo = 0, hi = D - 1;  // cu[lo] <= tq (cu[0] == 0); uniform within a half
+  for (;;) {
+    const bool busy = hi > lo;
+    if (!__any(busy)) break;
+    const int step = (hi - lo + 32) / 32;
+    const int idx = lo + sub * step;
+    const bool le = busy && idx <= hi && cu[idx] <= tq;
+    const unsigned long long m = __ballot(le);
+    const unsigned mh = half ? (unsigned)(m >> 32) : (unsigned)m;
+    if (busy) {
+      lo += (__popc(mh) - 1) * step;
+      hi = min(hi, lo + step - 1);
+    }
+  }
+  int a = __shfl(lo, 0), b = __shfl(lo, 32);
+  while (a < b) {
+    const int mid = (a + b + 1) >> 1;
+    if (cu[mid] <= t) a = mid;
+    else b = mid - 1;
+  }
+  return a;
+}
+
 // sin and cos of the NeoX RoPE angle p * inv_freq (flint.layers,
 // FlintAttention._apply_rope).  The product is formed and reduced modulo 2*pi
 // in fp64 so positions up to 2^31 keep a fp32-accurate angle; the reduced
