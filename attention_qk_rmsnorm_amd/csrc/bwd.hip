@@ -142,52 +142,6 @@ __device__ __forceinline__ void copy_col_tile(const char* __restrict__ src, int 
                                      (lds_void*)(uintptr_t)a, 16, 0, 0);
 }
 
-// Latest token that key u is visible to: min(document's real end, u + W) - 1
-// (below u when u is document padding).
-__device__ __forceinline__ int last_viewer(const int32_t* __restrict__ cu,
-                                           const int32_t* __restrict__ cu_end, int D, int u,
-                                           int window) {
-  const int n = doc_of_token(cu, D, u);
-  int e = cu_end[n];
-  if (window > 0 && u + window < e) e = u + window;
-  return e - 1;
-}
-
-// First and last real token in [a, b] (real: inside some document's
-// [start, real end)); first > last when the range holds none.  Without
-// padding every token is real and this returns [a, b].
-__device__ __forceinline__ void real_span(const int32_t* __restrict__ cu,
-                                          const int32_t* __restrict__ cu_end, int D, int a,
-                                          int b, int& first, int& last) {
-  first = b + 1;
-  const int n = doc_of_token(cu, D, a);
-  if (a < cu_end[n]) {
-    first = a;
-  } else {
-    for (int m = n + 1; m < D && cu[m] <= b; ++m)
-      if (cu_end[m] > cu[m]) {
-        first = cu[m];
-        break;
-      }
-  }
-  last = a - 1;
-  for (int m = doc_of_token(cu, D, b);; --m) {
-    if (cu_end[m] > cu[m]) {
-      last = min(b, cu_end[m] - 1);
-      break;
-    }
-    if (m == 0 || cu[m] <= a) break;
-  }
-  if (first > last) first = last + 1;
-}
-
-// Earliest key visible to token t: max(document start, t - W + 1).
-__device__ __forceinline__ int first_key(const int32_t* __restrict__ cu, int D, int t,
-                                         int window) {
-  const int s = cu[doc_of_token(cu, D, t)];
-  return window > 0 ? max(s, t - window + 1) : s;
-}
-
 // Backward of the rotation and the RMSNorm for one head vector held by a lane
 // pair: lane half hf holds the gradient w.r.t. the normalised, rotated vector
 // for channels 32dd + 8rq + 4hf + e at dy[16dd + 4rq + e] (dd, rq, e < 4).
@@ -501,13 +455,26 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   const bool u_ok = u < T;
   const int uc = u_ok ? u : T - 1;
   const int ua = kb0 + 32 * wave, ub = min(ua + 31, T - 1);
-  const int u_last = u_ok ? last_viewer(cu, cu_end, D, u, window) : -1;  // visible tokens [u, u_last]
+  // the key's document by one wave-level lookup (lanes past T look up the
+  // wave's last key); the latest token that sees the key is
+  // min(document's real end, u + W) - 1, below u for document padding
+  const int n_u = doc_of_token_wave(cu, D, uc, min(ua, T - 1), ub);
+  const int u_start = cu[n_u];
+  int u_last = -1;  // visible tokens [u, u_last]
+  if (u_ok) {
+    const int e = cu_end[n_u];
+    u_last = (window > 0 && u + window < e ? u + window : e) - 1;
+  }
   const bool u_real = u_ok && u_last >= u;  // else document padding: no gradient
-  const int ua_last = ua < T ? last_viewer(cu, cu_end, D, ua, window) : -1;
-  // the block's column tiles: tokens [kb0, last viewer of its last key]
-  const int kmax = min(kb0 + 127, T - 1);
+  const int ua_last = __shfl(u_last, 0);  // lane 0 holds key ua
+  // the block's column tiles: tokens [kb0, last viewer of its last key]; the
+  // last viewer is non-decreasing in the key, so that is the block's maximum
   // (a block of padding keys only still walks one, fully masked, tile)
-  const int t_hi = max(last_viewer(cu, cu_end, D, kmax, window), kb0);
+  __shared__ int s_last[4];
+  const int w_last = wave_max(u_last);
+  if (lane == 0) s_last[wave] = w_last;
+  __syncthreads();
+  const int t_hi = max(max(max(s_last[0], s_last[1]), max(s_last[2], s_last[3])), kb0);
   const int c_lo = kb0 / tpt, c_hi = t_hi / tpt;
   const char* ctiles = cols + (size_t)g * n_ct * kColTileBytes;
 
@@ -751,7 +718,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
     for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
       for (int r = 0; r < 16; ++r) dy[16 * dd + r] = acc_dk[dd][r] * kLn2;
-    const int pos = u_real && use_rope ? u - cu[doc_of_token(cu, D, u)] : 0;
+    const int pos = u_real && use_rope ? u - u_start : 0;
     float wsum[64];
     norm_rope_bwd(dy, k + ((size_t)uc * Hkv + g) * kHeadDim + 4 * hf, knorm_w, u_real, u_ok,
                   use_rope != 0, pos, s_invf, eps, hf,
@@ -816,11 +783,38 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
   const int t = ct * tpt + (col >> log2G);
   const int h = g * G + (col & (G - 1));
   const bool t_in = ct < n_ct && t < T;
-  // the block's real tokens [a0, a1]; a block of document padding only
-  // (block-uniform) writes zero dq and no weight gradient, and leaves
-  int a0 = 0, a1 = -1;
-  if (qb * kDqWaves * tpt < T)
-    real_span(cu, cu_end, D, qb * kDqWaves * tpt, min((qb + 1) * kDqWaves * tpt, T) - 1, a0, a1);
+  // Documents by one wave-level lookup per lane (lanes past T look up the
+  // wave's last token), then everything else by reductions: t_lo, the first
+  // key token t sees, is non-decreasing in t, so the wave's real tokens
+  // [ta, tb] and their first keys are minima and maxima over its lanes, and
+  // the block's over its waves.
+  const int w_first = min(ct * tpt, T - 1), w_last = min(ct * tpt + tpt - 1, T - 1);
+  const int n_t = doc_of_token_wave(cu, D, t_in ? t : w_last, w_first, w_last);
+  const bool t_ok = t_in && t < cu_end[n_t];  // a real query
+  const int t_start = cu[n_t];
+  const int t_lo = t_ok ? (window > 0 ? max(t_start, t - window + 1) : t_start)
+                        : 1 << 30;  // visible keys [t_lo, t]
+  const int ta = wave_min(t_ok ? t : INT_MAX), tb = wave_max(t_ok ? t : -1);
+  const bool wave_ok = ta <= tb;
+  const int wa_lo = wave_ok ? wave_min(t_ok ? t_lo : INT_MAX) : 0;
+  const int wb_lo = wave_ok ? wave_max(t_ok ? t_lo : -1) : 0;
+  __shared__ int s_span[kDqWaves][3];
+  if (lane == 0) {
+    s_span[wave][0] = ta;
+    s_span[wave][1] = tb;
+    s_span[wave][2] = wave_ok ? wa_lo : INT_MAX;
+  }
+  __syncthreads();
+  // the block's real tokens [a0, a1] and the first key they see; a block of
+  // document padding only (block-uniform) writes zero dq and no weight
+  // gradient, and leaves
+  int a0 = INT_MAX, a1 = -1, lo = INT_MAX;
+#pragma unroll
+  for (int w = 0; w < kDqWaves; ++w) {
+    a0 = min(a0, s_span[w][0]);
+    a1 = max(a1, s_span[w][1]);
+    lo = min(lo, s_span[w][2]);
+  }
   if (a0 > a1) {
     if (t_in) {
       E* dz = dq + ((size_t)t * Hq + h) * kHeadDim + 4 * hf;
@@ -832,20 +826,11 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
     return;
   }
   if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
-  const bool t_ok = t_in && t < cu_end[doc_of_token(cu, D, t)];  // a real query
   const int tcl = t_in ? t : 0;
-  const int t_lo = t_ok ? first_key(cu, D, t, window) : 1 << 30;  // visible keys [t_lo, t]
-  // the wave's real tokens [ta, tb] and the block's key range (the keys its
-  // real tokens see; document padding sees none)
-  int ta = 0, tb = -1;
-  if (ct < n_ct && ct * tpt < T)
-    real_span(cu, cu_end, D, ct * tpt, min(ct * tpt + tpt, T) - 1, ta, tb);
-  const bool wave_ok = ta <= tb;
-  const int lo = first_key(cu, D, a0, window);
+  // the block's key range: the keys its real tokens see (document padding
+  // sees none)
   const int kt_lo = lo & ~(kKeyTile - 1);
   const int n_tiles = (a1 + 1 - kt_lo + kKeyTile - 1) / kKeyTile;
-  const int wa_lo = wave_ok ? first_key(cu, D, ta, window) : 0;
-  const int wb_lo = wave_ok ? first_key(cu, D, tb, window) : 0;
   const char* ktiles = keys + (size_t)g * n_kt * kKeyTileBytes;
 
   // q (scaled) and dout rows of this lane's column as B operands, -lse*log2e, -D
@@ -969,7 +954,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
     for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
       for (int r = 0; r < 16; ++r) dy[16 * dd + r] = acc[dd][r] * scale;
-    const int pos = t_ok && use_rope ? t - cu[doc_of_token(cu, D, t)] : 0;
+    const int pos = t_ok && use_rope ? t - t_start : 0;
     float wsum[64];
     norm_rope_bwd(dy, q + ((size_t)tcl * Hq + h) * kHeadDim + 4 * hf, qnorm_w, t_ok, t_in,
                   use_rope != 0, pos, s_invf, eps, hf,

@@ -54,6 +54,18 @@ __device__ inline int doc_of_token_wave(const int32_t* __restrict__ cu, int D, i
   return a;
 }
 
+// Minimum / maximum of x over the 64 lanes of a wave (all lanes active).
+__device__ __forceinline__ int wave_min(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = min(x, __shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = max(x, __shfl_xor(x, m));
+  return x;
+}
+
 // sin and cos of the NeoX RoPE angle p * inv_freq (flint.layers,
 // FlintAttention._apply_rope).  The product is formed and reduced modulo 2*pi
 // in fp64 so positions up to 2^31 keep a fp32-accurate angle; the reduced
