@@ -38,6 +38,14 @@ def test_many_and_empty_documents():
     check_bwd_parity(custom_inputs(lengths), 3, True, label="many docs W=3")
 
 
+def test_forty_thousand_documents():
+    # 40,002 documents of 0-2 tokens (more than 32,768: the deepest levels of
+    # the wave-level document lookup)
+    lengths = [1, 2, 0] * 13334
+    _say(f"case bwd {len(lengths)} documents")
+    check_bwd_parity(custom_inputs(lengths), -1, True, label="40k docs")
+
+
 @pytest.mark.parametrize("heads", [(32, 4), (8, 8), (32, 1), (4, 2), (16, 16)])
 def test_group_sizes(heads):
     _say(f"case bwd heads={heads}")

@@ -70,6 +70,16 @@ def test_bf16_many_and_empty_documents(window, use_rope, tile):
                  tile_config=tile)
 
 
+def test_bf16_forty_thousand_documents():
+    # 40,002 documents of 0-2 tokens: more than 32,768, so the document
+    # lookups take their deepest search levels
+    lengths = [1, 2, 0] * 13334
+    _say(f"case bf16 {len(lengths)} documents")
+    inp = custom_inputs(lengths)
+    check_parity(inp, -1, False, label="40k docs causal")
+    check_parity(inp, 2, True, label="40k docs W=2")
+
+
 @pytest.mark.parametrize("heads", [(32, 4), (8, 8), (16, 4), (32, 1), (16, 1), (4, 2)])
 def test_bf16_group_sizes(heads):
     _say(f"case bf16 heads={heads}")
