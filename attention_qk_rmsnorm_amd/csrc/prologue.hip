@@ -140,7 +140,9 @@ __global__ __launch_bounds__(kThreads) void prologue_16_kernel(
       const int idx = lo + tid * step;
       const bool le = idx <= hi && cu[idx] <= tq;
       const int cnt = __popcll(__ballot(le));
-      lo += (cnt - 1) * step;
+      // (cnt is 0 only for a malformed cu with cu[0] > t0; clamping keeps
+      // every read in bounds whatever cu holds)
+      lo += max(cnt - 1, 0) * step;
       hi = min(hi, lo + step - 1);
     }
     if (tid == 0) s_d0 = lo;

@@ -41,7 +41,9 @@ __device__ inline int doc_of_token_wave(const int32_t* __restrict__ cu, int D, i
     const unsigned long long m = __ballot(le);
     const unsigned mh = half ? (unsigned)(m >> 32) : (unsigned)m;
     if (busy) {
-      lo += (__popc(mh) - 1) * step;
+      // (a count of 0 is possible only for a malformed cu with cu[0] > t;
+      // clamping keeps every read in bounds whatever cu holds)
+      lo += max(__popc(mh) - 1, 0) * step;
       hi = min(hi, lo + step - 1);
     }
   }
