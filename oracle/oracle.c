@@ -327,10 +327,14 @@ static void rmsnorm_vec_bwd(int d, const double* x, const double* w, double eps,
 
 /* Public: gradients of sum(dout * out) for the whole forward pass.
  *   q, dout, dq [T, Hq, d]; k, v, dk, dv [T, Hkv, d]; dsinks [Hq];
- *   dqnorm_w, dknorm_w [d].  Every output is overwritten.  Work is split
- *   over (document, kv head) pairs, whose gradients do not overlap, and the
- *   shared sums (sinks, norm weights) are added in a fixed order, so the
- *   result does not depend on the thread count. */
+ *   dqnorm_w, dknorm_w [d].  Every output is overwritten.  Two passes, each
+ *   split over independent outputs: pass 1 over (token, query head) rows
+ *   (the forward row, D, the row's sink term and dq_hat), pass 2 over (key,
+ *   kv head) pairs (dk_hat and dv, from the rows' stored lse and D).  Every
+ *   sum is added in a fixed order -- dq_hat over keys in token order; dk_hat
+ *   and dv over queries in token order, then head order; dsink and the norm
+ *   weights over tokens in order -- so the result does not depend on the
+ *   thread count. */
 int oracle_sink_attn_bwd(int T, int num_docs, const int32_t* cu, int Hq, int Hkv,
                          int d, const double* q, const double* k, const double* v,
                          const double* sinks, const double* qnorm_w,
@@ -352,16 +356,18 @@ int oracle_sink_attn_bwd(int T, int num_docs, const int32_t* cu, int Hq, int Hkv
   }
   const int group = Hq / Hkv;
   const size_t nq = (size_t)T * Hq * d, nk = (size_t)T * Hkv * d;
+  const size_t nrow = (size_t)T * Hq;
   double* qh = (double*)malloc(sizeof(double) * (nq + 1));
   double* kh = (double*)malloc(sizeof(double) * (nk + 1));
   double* dqh = (double*)calloc(nq + 1, sizeof(double));
   double* dkh = (double*)calloc(nk + 1, sizeof(double));
-  double* sink_part = (double*)calloc((size_t)num_docs * Hq + 1, sizeof(double));
+  double* row_lse = (double*)malloc(sizeof(double) * (nrow + 1));
+  double* row_D = (double*)malloc(sizeof(double) * (nrow + 1));
+  double* row_sink = (double*)malloc(sizeof(double) * (nrow + 1));
   prologue_rows(T, pos_of, Hq, d, q, qnorm_w, eps, theta, use_rope, qh);
   prologue_rows(T, pos_of, Hkv, d, k, knorm_w, eps, theta, use_rope, kh);
   for (size_t i = 0; i < nk; ++i) dv[i] = 0.0;
 
-  const long items = (long)num_docs * Hkv;
 #ifdef _OPENMP
   int nt = nthreads > 0 ? nthreads : omp_get_max_threads();
 #pragma omp parallel num_threads(nt)
@@ -369,46 +375,82 @@ int oracle_sink_attn_bwd(int T, int num_docs, const int32_t* cu, int Hq, int Hkv
   {
     double* scores = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
     double* out_row = (double*)malloc(sizeof(double) * (size_t)d);
+    /* pass 1: per (token t, query head h) row -- steps 3-5 forward, then
+     * D = dout . out, the row's term of dsink, and dq_hat over the visible keys
+     * in token order */
 #ifdef _OPENMP
 #pragma omp for schedule(dynamic, 1)
 #endif
-    for (long item = 0; item < items; ++item) {
-      const int n = (int)(item / Hkv), g = (int)(item % Hkv);
-      for (int t = cu[n]; t < cu[n + 1]; ++t)
+    for (long r = 0; r < (long)nrow; ++r) {
+      const int t = (int)(r / Hq), h = (int)(r % Hq), g = h / group;
+      const int n = doc_of[t];
+      const double* qrow = qh + (size_t)r * d;
+      const double* dorow = dout + (size_t)r * d;
+      double lse;
+      attend_row(t, T, Hkv, g, d, qrow, kh, v, sinks[h], scale, window, doc_of, pos_of,
+                 scores, out_row, &lse);
+      double D = 0.0;
+      for (int i = 0; i < d; ++i) D += dorow[i] * out_row[i];
+      row_lse[r] = lse;
+      row_D[r] = D;
+      row_sink[r] = exp(sinks[h] - lse) * D;
+      double* dqrow = dqh + (size_t)r * d;
+      for (int u = cu[n]; u <= t; ++u) {
+        if (scores[u] == -INFINITY) continue;
+        const double P = exp(scores[u] - lse);
+        const double* vu = v + ((size_t)u * Hkv + g) * d;
+        const double* ku = kh + ((size_t)u * Hkv + g) * d;
+        double dP = 0.0;
+        for (int i = 0; i < d; ++i) dP += dorow[i] * vu[i];
+        const double dS = P * (dP - D);
+        for (int i = 0; i < d; ++i) dqrow[i] += scale * dS * ku[i];
+      }
+    }
+    /* pass 2: per (key u, kv head g) -- dk_hat and dv over the queries that
+     * see u, in token order, then head order (the scores, weights and dS are
+     * the same expressions as in pass 1 and attend_row) */
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+    for (long c = 0; c < (long)T * Hkv; ++c) {
+      const int u = (int)(c / Hkv), g = (int)(c % Hkv);
+      const int n = doc_of[u];
+      const double* vu = v + (size_t)c * d;
+      const double* ku = kh + (size_t)c * d;
+      double* dku = dkh + (size_t)c * d;
+      double* dvu = dv + (size_t)c * d;
+      for (int t = u; t < cu[n + 1]; ++t) {
+        if (!visible(t, u, doc_of, pos_of, window)) continue;
         for (int h = g * group; h < (g + 1) * group; ++h) {
-          const double* qrow = qh + ((size_t)t * Hq + h) * d;
-          const double* dorow = dout + ((size_t)t * Hq + h) * d;
-          double lse;
-          attend_row(t, T, Hkv, g, d, qrow, kh, v, sinks[h], scale, window, doc_of,
-                     pos_of, scores, out_row, &lse);
-          double D = 0.0;
-          for (int i = 0; i < d; ++i) D += dorow[i] * out_row[i];
-          sink_part[(size_t)n * Hq + h] -= exp(sinks[h] - lse) * D;
-          double* dqrow = dqh + ((size_t)t * Hq + h) * d;
-          for (int u = cu[n]; u <= t; ++u) {
-            if (scores[u] == -INFINITY) continue;
-            const double P = exp(scores[u] - lse);
-            const double* vu = v + ((size_t)u * Hkv + g) * d;
-            const double* ku = kh + ((size_t)u * Hkv + g) * d;
-            double dP = 0.0;
-            for (int i = 0; i < d; ++i) dP += dorow[i] * vu[i];
-            const double dS = P * (dP - D);
-            double* dku = dkh + ((size_t)u * Hkv + g) * d;
-            double* dvu = dv + ((size_t)u * Hkv + g) * d;
-            for (int i = 0; i < d; ++i) {
-              dqrow[i] += scale * dS * ku[i];
-              dku[i] += scale * dS * qrow[i];
-              dvu[i] += P * dorow[i];
-            }
+          const size_t r = (size_t)t * Hq + h;
+          const double* qrow = qh + r * d;
+          const double* dorow = dout + r * d;
+          double dot = 0.0;
+          for (int i = 0; i < d; ++i) dot += qrow[i] * ku[i];
+          const double s = scale * dot;
+          const double P = exp(s - row_lse[r]);
+          double dP = 0.0;
+          for (int i = 0; i < d; ++i) dP += dorow[i] * vu[i];
+          const double dS = P * (dP - row_D[r]);
+          for (int i = 0; i < d; ++i) {
+            dku[i] += scale * dS * qrow[i];
+            dvu[i] += P * dorow[i];
           }
         }
+      }
     }
     free(scores);
     free(out_row);
   }
+  /* dsink_h = -sum over the tokens of each document, in token order, then
+   * over documents in order */
   for (int h = 0; h < Hq; ++h) {
     dsinks[h] = 0.0;
-    for (int n = 0; n < num_docs; ++n) dsinks[h] += sink_part[(size_t)n * Hq + h];
+    for (int n = 0; n < num_docs; ++n) {
+      double part = 0.0;
+      for (int t = cu[n]; t < cu[n + 1]; ++t) part -= row_sink[(size_t)t * Hq + h];
+      dsinks[h] += part;
+    }
   }
   /* steps 2 and 1 backwards, token by token in order (fixed summation order
    * for the norm weights) */
@@ -431,7 +473,9 @@ int oracle_sink_attn_bwd(int T, int num_docs, const int32_t* cu, int Hq, int Hkv
   free(kh);
   free(dqh);
   free(dkh);
-  free(sink_part);
+  free(row_lse);
+  free(row_D);
+  free(row_sink);
   free(doc_of);
   free(pos_of);
   return ORACLE_OK;

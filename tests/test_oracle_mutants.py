@@ -37,10 +37,15 @@ MUTANTS = {
 }
 
 
+# A mutant is one substitution, or a list of them when the mistake concerns a
+# quantity the oracle's two backward passes both form (the softmax gradient's
+# D term is used by the row pass for dq and by the key pass for dk).
 BWD_MUTANTS = {
-    "bwd_D_term_dropped": ("const double dS = P * (dP - D);", "const double dS = P * dP;"),
-    "bwd_sink_sign": ("sink_part[(size_t)n * Hq + h] -= exp(sinks[h] - lse) * D;",
-                      "sink_part[(size_t)n * Hq + h] += exp(sinks[h] - lse) * D;"),
+    "bwd_D_term_dropped": [("const double dS = P * (dP - D);", "const double dS = P * dP;"),
+                           ("const double dS = P * (dP - row_D[r]);",
+                            "const double dS = P * dP;")],
+    "bwd_sink_sign": ("part -= row_sink[(size_t)t * Hq + h];",
+                      "part += row_sink[(size_t)t * Hq + h];"),
     "bwd_sink_not_normalised": ("exp(sinks[h] - lse) * D", "exp(sinks[h]) * D"),
     "bwd_dq_scale_dropped": ("dqrow[i] += scale * dS * ku[i];", "dqrow[i] += dS * ku[i];"),
     "bwd_dk_from_key": ("dku[i] += scale * dS * qrow[i];", "dku[i] += scale * dS * ku[i];"),
@@ -53,11 +58,12 @@ BWD_MUTANTS = {
 }
 
 
-def _run_mutant(name, old, new, pins, tmp_path):
+def _run_mutant(name, subs, pins, tmp_path):
     import oracle.oracle as O
-    src = open(SRC).read()
-    assert src.count(old) >= 1, f"mutation site for {name} not found"
-    mutated = src.replace(old, new)
+    mutated = open(SRC).read()
+    for old, new in (subs if isinstance(subs, list) else [subs]):
+        assert mutated.count(old) >= 1, f"mutation site for {name} not found: {old}"
+        mutated = mutated.replace(old, new)
     csrc = tmp_path / "oracle_mutant.c"
     csrc.write_text(mutated)
     lib = O.build(force=True, src=str(csrc), out=str(tmp_path / "liboracle_mutant.so"))
@@ -70,9 +76,9 @@ def _run_mutant(name, old, new, pins, tmp_path):
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name, tmp_path):
-    _run_mutant(name, *MUTANTS[name], "test_oracle_pins.py", tmp_path)
+    _run_mutant(name, MUTANTS[name], "test_oracle_pins.py", tmp_path)
 
 
 @pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
 def test_backward_pins_catch_planted_mistake(name, tmp_path):
-    _run_mutant(name, *BWD_MUTANTS[name], "test_oracle_bwd_pins.py", tmp_path)
+    _run_mutant(name, BWD_MUTANTS[name], "test_oracle_bwd_pins.py", tmp_path)
