@@ -85,6 +85,8 @@ def load_library():
     lib.sink_attn_attention.restype = ctypes.c_int
     lib.sink_attn_tile_config.argtypes = [DP, I32]
     lib.sink_attn_tile_config.restype = ctypes.c_int
+    lib.sink_attn_fwd_noalloc.argtypes = [DP, P, P, P, P, P, P, P, I32, I32, P, P, P]
+    lib.sink_attn_fwd_noalloc.restype = ctypes.c_int
     lib.sink_attn_fwd_padded.argtypes = [DP, P, P, P, P, P, P, P, P, I32, I32, P, P, P]
     lib.sink_attn_fwd_padded.restype = ctypes.c_int
     lib.sink_attn_bwd_padded.argtypes = [DP, P, P, P, P, P, P, P, P, I32, I32, P, P, P, P, P, P,
@@ -170,7 +172,7 @@ class Call:
     def __init__(self, q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope,
                  out=None, lse=None, *, rms_eps=1e-6, rope_theta=1e6, softmax_scale=None,
                  workspace=None, stream=None, return_lse=True, tile_config=SINK_ATTN_TILE_AUTO,
-                 cu_seqlens_padded=None):
+                 cu_seqlens_padded=None, library_scratch=False):
         if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
             raise ValueError("q, k, v must be THD tensors [tokens, heads, head_dim]")
         dev = q.device
@@ -192,7 +194,9 @@ class Call:
         self.desc = make_desc(T, cu_seqlens.numel() - 1, Hq, Hkv, d, q.dtype, rms_eps,
                               rope_theta, softmax_scale or 0.0, tile_config=tile_config)
         self.cu_padded = cu_seqlens_padded
-        need = workspace_bytes(self.desc)
+        # library_scratch: the call goes to sink_attn_fwd_noalloc, which works in
+        # the library's own device array, so no workspace is allocated here
+        need = 0 if library_scratch else workspace_bytes(self.desc)
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         if workspace is not None:
@@ -234,6 +238,17 @@ class Call:
         if rc:
             raise SinkAttnError(rc, "sink_attn_fwd")
 
+    def fwd_noalloc(self):
+        """The forward through sink_attn_fwd_noalloc (unpadded THD only)."""
+        if self.cu_padded is not None:
+            raise ValueError("sink_attn_fwd_noalloc takes unpadded THD only")
+        rc = load_library().sink_attn_fwd_noalloc(
+            ctypes.byref(self.desc), _ptr(self.q), _ptr(self.k), _ptr(self.v), _ptr(self.cu),
+            _ptr(self.sinks), _ptr(self.qnorm_w), _ptr(self.knorm_w), self.window,
+            self.use_rope, _ptr(self.out), _ptr(self.lse), self.stream)
+        if rc:
+            raise SinkAttnError(rc, "sink_attn_fwd_noalloc")
+
     def prologue(self):
         if self.cu_padded is not None:
             raise ValueError("the two-stage entry points take unpadded THD only")
@@ -261,6 +276,21 @@ def sink_attn_fwd(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope
     c = Call(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope, out, lse, **kw)
     c.fwd()
     return c.out, c.lse
+
+
+def sink_attn_fwd_noalloc(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope,
+                          out=None, lse=None, **kw):
+    """Forward pass through sink_attn_fwd_noalloc: the library works in its own
+    device array (SINK_ATTN_NOALLOC_SCRATCH_BYTES per device) instead of a
+    workspace.  Pass out (and lse) to keep the call free of allocations; torch
+    allocates them here otherwise.  Returns (out, lse)."""
+    c = Call(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope, out, lse,
+             library_scratch=True, **kw)
+    c.fwd_noalloc()
+    return c.out, c.lse
+
+
+NOALLOC_SCRATCH_BYTES = 80 << 20   # SINK_ATTN_NOALLOC_SCRATCH_BYTES of include/sink_attn.h
 
 
 def sink_attn_prologue(q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope,

@@ -7,7 +7,18 @@
 
 #include <math.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "sa_device.h"
+
+// Device memory sink_attn_fwd_noalloc works in, in place of a caller's
+// workspace.  Each device the library runs on holds its own copy for the life
+// of the process.  Host code never uses this name as an address (on the host
+// it is only a handle the runtime maps to a device address): the entry point
+// asks the runtime once per device for that device's address
+// (scratch_address below) and every later use goes through that pointer.
+static __device__ __align__(256) char scratch[SINK_ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace sa {
 
@@ -264,8 +275,11 @@ double softmax_scale(const sink_attn_desc* d) {
   return d->softmax_scale > 0.0 ? d->softmax_scale : 1.0 / sqrt((double)d->head_dim);
 }
 
+// Argument checks of each stage; check_ws = false leaves out the workspace
+// (the no-alloc entry point supplies its own).
 int check_prologue(const sink_attn_desc* d, const void* k, const void* v,
-                   const int32_t* cu, const float* knorm_w, int32_t use_rope) {
+                   const int32_t* cu, const float* knorm_w, int32_t use_rope,
+                   bool check_ws = true) {
   int rc = check_desc(d);
   if (rc) return rc;
   if (use_rope != 0 && use_rope != 1) return SINK_ATTN_EINVAL;
@@ -274,12 +288,13 @@ int check_prologue(const sink_attn_desc* d, const void* k, const void* v,
   if (k == nullptr || v == nullptr || knorm_w == nullptr) return SINK_ATTN_EINVAL;
   const uintptr_t al = io_align(d);
   if (!aligned(k, al) || !aligned(v, al) || !aligned(knorm_w, 4)) return SINK_ATTN_EINVAL;
-  return check_workspace(d, plan(d));
+  return check_ws ? check_workspace(d, plan(d)) : SINK_ATTN_OK;
 }
 
 int check_attention(const sink_attn_desc* d, const void* q, const int32_t* cu,
                     const float* sinks, const float* qnorm_w, int32_t window,
-                    int32_t use_rope, const void* out, const float* lse) {
+                    int32_t use_rope, const void* out, const float* lse,
+                    bool check_ws = true) {
   int rc = check_desc(d);
   if (rc) return rc;
   if (window == 0) return SINK_ATTN_EINVAL;
@@ -292,7 +307,7 @@ int check_attention(const sink_attn_desc* d, const void* q, const int32_t* cu,
   if (!aligned(q, al) || !aligned(out, al) || !aligned(sinks, 4) || !aligned(qnorm_w, 4) ||
       (lse != nullptr && !aligned(lse, 4)))
     return SINK_ATTN_EINVAL;
-  return check_workspace(d, plan(d));
+  return check_ws ? check_workspace(d, plan(d)) : SINK_ATTN_OK;
 }
 
 template <typename E>
@@ -440,16 +455,26 @@ hipError_t doc_bounds(const sink_attn_desc* d, const int32_t* cu, const int32_t*
   return sa::launch_doc_ends(cu, cu_padded, d->num_docs, ends, s);
 }
 
-int fwd_impl(const sink_attn_desc* desc, const void* q, const void* k, const void* v,
-             const int32_t* cu_seqlens, const int32_t* cu_padded, const float* sinks,
-             const float* qnorm_w, const float* knorm_w, int32_t window, int32_t use_rope,
-             void* out, float* lse, void* stream) {
-  int rc = check_prologue(desc, k, v, cu_seqlens, knorm_w, use_rope);
+int check_fwd(const sink_attn_desc* desc, const void* q, const void* k, const void* v,
+              const int32_t* cu_seqlens, const int32_t* cu_padded, const float* sinks,
+              const float* qnorm_w, const float* knorm_w, int32_t window, int32_t use_rope,
+              const void* out, const float* lse, bool check_ws) {
+  int rc = check_prologue(desc, k, v, cu_seqlens, knorm_w, use_rope, check_ws);
   if (rc != SINK_ATTN_OK) return rc;
-  rc = check_attention(desc, q, cu_seqlens, sinks, qnorm_w, window, use_rope, out, lse);
+  rc = check_attention(desc, q, cu_seqlens, sinks, qnorm_w, window, use_rope, out, lse,
+                       check_ws);
   if (rc != SINK_ATTN_OK) return rc;
   if (cu_padded != nullptr && !aligned(cu_padded, 4)) return SINK_ATTN_EINVAL;
+  return SINK_ATTN_OK;
+}
+
+// The forward's launches, after check_fwd passed.
+int fwd_launch(const sink_attn_desc* desc, const void* q, const void* k, const void* v,
+               const int32_t* cu_seqlens, const int32_t* cu_padded, const float* sinks,
+               const float* qnorm_w, const float* knorm_w, int32_t window, int32_t use_rope,
+               void* out, float* lse, void* stream) {
   if (desc->total_tokens == 0) return SINK_ATTN_OK;
+  int rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Docs docs;
   if (doc_bounds(desc, cu_seqlens, cu_padded, plan(desc).ends_off, s, &docs) != hipSuccess)
@@ -465,6 +490,63 @@ int fwd_impl(const sink_attn_desc* desc, const void* q, const void* k, const voi
                              s) == hipSuccess
              ? SINK_ATTN_OK
              : SINK_ATTN_ELAUNCH;
+}
+
+int fwd_impl(const sink_attn_desc* desc, const void* q, const void* k, const void* v,
+             const int32_t* cu_seqlens, const int32_t* cu_padded, const float* sinks,
+             const float* qnorm_w, const float* knorm_w, int32_t window, int32_t use_rope,
+             void* out, float* lse, void* stream) {
+  const int rc = check_fwd(desc, q, k, v, cu_seqlens, cu_padded, sinks, qnorm_w, knorm_w,
+                           window, use_rope, out, lse, true);
+  if (rc != SINK_ATTN_OK) return rc;
+  return fwd_launch(desc, q, k, v, cu_seqlens, cu_padded, sinks, qnorm_w, knorm_w, window,
+                    use_rope, out, lse, stream);
+}
+
+// ---- forward without a caller workspace (sink_attn_fwd_noalloc) -----------
+// `scratch` (top of this file) is the memory it works in.
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<char*> g_scratch_addr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device that runs the work of `stream` (the current device for the null stream).
+hipError_t stream_device(hipStream_t stream, int* dev) {
+  if (stream == nullptr) return hipGetDevice(dev);
+  hipDevice_t d = 0;
+  const hipError_t e = hipStreamGetDevice(stream, &d);
+  *dev = d;
+  return e;
+}
+
+// Address of `scratch` on device dev: looked up on the first call for that
+// device with the device current (the caller's current device is restored),
+// then kept.
+hipError_t scratch_address(int dev, char** addr) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  char* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      int cur = 0;
+      hipError_t e = hipGetDevice(&cur);
+      if (e != hipSuccess) return e;
+      if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+      void* sym = nullptr;
+      e = hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch));
+      if (cur != dev) {
+        const hipError_t back = hipSetDevice(cur);
+        if (e == hipSuccess) e = back;
+      }
+      if (e != hipSuccess) return e;
+      if (sym == nullptr || !aligned(sym, 256)) return hipErrorInvalidSymbol;
+      p = static_cast<char*>(sym);
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return hipSuccess;
 }
 
 int bwd_impl(const sink_attn_desc* desc, const void* q, const void* k, const void* v,
@@ -549,6 +631,28 @@ int sink_attn_fwd_padded(const sink_attn_desc* desc, const void* q, const void* 
                   window, use_rope, out, lse, stream);
 }
 
+int sink_attn_fwd_noalloc(const sink_attn_desc* desc, const void* q, const void* k,
+                          const void* v, const int32_t* cu_seqlens, const float* sinks,
+                          const float* qnorm_w, const float* knorm_w, int32_t window,
+                          int32_t use_rope, void* out, float* lse, void* stream) {
+  int rc = check_fwd(desc, q, k, v, cu_seqlens, nullptr, sinks, qnorm_w, knorm_w, window,
+                     use_rope, out, lse, false);
+  if (rc != SINK_ATTN_OK) return rc;
+  const size_t need = plan(desc).total;
+  if (need > SINK_ATTN_NOALLOC_SCRATCH_BYTES) return SINK_ATTN_ESCRATCH;
+  if (desc->total_tokens == 0) return SINK_ATTN_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  char* ws = nullptr;
+  if (stream_device(s, &dev) != hipSuccess || scratch_address(dev, &ws) != hipSuccess)
+    return SINK_ATTN_ELAUNCH;
+  sink_attn_desc d = *desc;
+  d.workspace = ws;
+  d.workspace_bytes = SINK_ATTN_NOALLOC_SCRATCH_BYTES;
+  return fwd_launch(&d, q, k, v, cu_seqlens, nullptr, sinks, qnorm_w, knorm_w, window,
+                    use_rope, out, lse, stream);
+}
+
 size_t sink_attn_bwd_workspace_bytes(const sink_attn_desc* desc) {
   if (check_desc(desc) != SINK_ATTN_OK || desc->dtype == SINK_ATTN_F32) return 0;
   return plan_bwd(desc).total;
@@ -609,6 +713,8 @@ const char* sink_attn_status_string(int status) {
     case SINK_ATTN_EUNSUPPORTED: return "unsupported configuration";
     case SINK_ATTN_EWORKSPACE: return "workspace missing, too small or misaligned";
     case SINK_ATTN_ELAUNCH: return "kernel launch failed";
+    case SINK_ATTN_ESCRATCH:
+      return "call needs more than the no-alloc scratch (SINK_ATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

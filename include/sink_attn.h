@@ -36,7 +36,8 @@
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller, on the
  *     device that owns `stream`.  The library never allocates, frees or
- *     synchronises, never writes q, k or v, and keeps no state between calls.
+ *     synchronises, never writes q, k or v, and keeps no state between calls
+ *     (one exception: the device array of sink_attn_fwd_noalloc, below).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     the call returns at once.  Buffers must stay alive until it completes.
  *   - Arguments are checked on the host before any HIP call; a failed check
@@ -71,7 +72,9 @@ typedef enum {
   SINK_ATTN_EINVAL = -1,        /* invalid argument: null pointer, bad size, window == 0 */
   SINK_ATTN_EUNSUPPORTED = -2,  /* well-formed but not provided (head_dim, dtype, group) */
   SINK_ATTN_EWORKSPACE = -3,    /* workspace missing or smaller than required */
-  SINK_ATTN_ELAUNCH = -4        /* a kernel launch failed (hipGetLastError) */
+  SINK_ATTN_ELAUNCH = -4,       /* a kernel launch failed (hipGetLastError) */
+  SINK_ATTN_ESCRATCH = -5       /* sink_attn_fwd_noalloc: the call needs more device
+                                   memory than SINK_ATTN_NOALLOC_SCRATCH_BYTES */
 } sink_attn_status;
 
 typedef enum {
@@ -241,6 +244,34 @@ int sink_attn_bwd_padded(const sink_attn_desc* desc, const void* q, const void* 
                          int32_t use_rope, const void* out, const float* lse,
                          const void* dout, void* dq, void* dk, void* dv, float* dsinks,
                          float* dqnorm_w, float* dknorm_w, void* stream);
+
+/* Device memory the library keeps for sink_attn_fwd_noalloc: 80 MiB, once per
+ * device it runs on, held until the process ends.  That covers a forward of
+ * up to about 40,000 tokens at 4 kv heads and head_dim 128 in bf16 or fp16
+ * (sink_attn_workspace_bytes(desc) <= this). */
+#define SINK_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)80 << 20)
+
+/* sink_attn_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, kernels and results as sink_attn_fwd (bitwise), except that
+ * desc->workspace and desc->workspace_bytes are ignored: the call runs in a
+ * device array of SINK_ATTN_NOALLOC_SCRATCH_BYTES that the library holds,
+ * and never allocates or frees anything itself.
+ *   - A descriptor whose sink_attn_workspace_bytes() exceeds
+ *     SINK_ATTN_NOALLOC_SCRATCH_BYTES returns SINK_ATTN_ESCRATCH and enqueues
+ *     nothing; argument errors return as for sink_attn_fwd.
+ *   - The array of the stream's device is looked up on the first call on
+ *     that device (hipGetSymbolAddress, which is not an allocation);
+ *     SINK_ATTN_ELAUNCH if that fails.
+ *   - Every call on one device uses that device's one array, which keeps the
+ *     last call's contents (a call rewrites all it reads, so nothing needs
+ *     clearing).  Calls whose stream work overlaps on one device -- different
+ *     streams, or host threads without ordering -- race on the array and give
+ *     undefined results; order them on one stream. */
+int sink_attn_fwd_noalloc(const sink_attn_desc* desc, const void* q, const void* k,
+                          const void* v, const int32_t* cu_seqlens, const float* sinks,
+                          const float* qnorm_w, const float* knorm_w, int32_t window,
+                          int32_t use_rope, void* out, float* lse, void* stream);
 
 /* Static text for a status code (never NULL). */
 const char* sink_attn_status_string(int status);

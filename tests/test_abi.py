@@ -8,7 +8,7 @@ import ctypes
 
 import pytest
 
-OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH = 0, -1, -2, -3, -4
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH, ESCRATCH = 0, -1, -2, -3, -4, -5
 
 
 @pytest.fixture(scope="module")
@@ -28,7 +28,8 @@ def test_every_declared_symbol_is_exported(A):
                           "sink_attn_status_string", "sink_attn_prologue",
                           "sink_attn_attention", "sink_attn_version", "sink_attn_tile_config",
                           "sink_attn_bwd", "sink_attn_bwd_workspace_bytes", "sink_attn_fwd_padded",
-                          "sink_attn_bwd_padded", "sink_attn_mask_to_seqlens"}
+                          "sink_attn_bwd_padded", "sink_attn_mask_to_seqlens",
+                          "sink_attn_fwd_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -41,7 +42,7 @@ def test_descriptor_layout_matches_header(A):
 
 
 def test_status_strings(A):
-    for code in (OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH, 12345):
+    for code in (OK, EINVAL, EUNSUPPORTED, EWORKSPACE, ELAUNCH, ESCRATCH, 12345):
         s = A.status_string(code)
         assert isinstance(s, str) and s
     assert A.status_string(12345) == "unknown status"
@@ -330,3 +331,46 @@ def test_fp16_descriptor(A):
     assert _fwd(A, _desc(A, dtype=f16, Hq=12, Hkv=4, ws_bytes=1 << 30)) == EUNSUPPORTED
     assert _fwd(A, _desc(A, dtype=f16), q=FAKE + 8) == EINVAL   # 16-byte alignment
     assert _fwd(A, _desc(A, dtype=f16, ws_bytes=1024)) == EWORKSPACE
+
+
+def _noalloc(A, desc, window=-1, **ptrs):
+    names = ["q", "k", "v", "cu", "sinks", "qw", "kw", "out", "lse"]
+    p = {n: FAKE for n in names}
+    p.update(ptrs)
+    P = ctypes.c_void_p
+    return A.load_library().sink_attn_fwd_noalloc(
+        ctypes.byref(desc) if desc is not None else None, P(p["q"]), P(p["k"]), P(p["v"]),
+        P(p["cu"]), P(p["sinks"]), P(p["qw"]), P(p["kw"]), window, 0, P(p["out"]),
+        P(p["lse"]), None)
+
+
+def test_noalloc_entry_point_validates_before_any_hip_call(A):
+    # the no-alloc forward ignores the descriptor's workspace, checks every
+    # argument as sink_attn_fwd does, and rejects a call whose workspace would
+    # exceed the library's scratch array -- all before touching the device
+    limit = A.NOALLOC_SCRATCH_BYTES
+    import os
+    import re
+    with open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "include", "sink_attn.h")) as f:
+        m = re.search(r"#define SINK_ATTN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)",
+                      f.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == limit
+    fits = _desc(A, T=36000, D=1)
+    assert 0 < A.workspace_bytes(fits) <= limit
+    too_big = _desc(A, T=45000, D=1)
+    assert A.workspace_bytes(too_big) > limit
+    assert _noalloc(A, too_big) == ESCRATCH
+    assert "scratch" in A.status_string(ESCRATCH)
+    f32 = _desc(A, T=30000, D=1, Hq=4, Hkv=4, dtype=A.SINK_ATTN_F32)
+    assert A.workspace_bytes(f32) > limit and _noalloc(A, f32) == ESCRATCH
+    assert _noalloc(A, None) == EINVAL
+    assert _noalloc(A, _desc(A), window=0) == EINVAL
+    assert _noalloc(A, _desc(A), q=0) == EINVAL
+    assert _noalloc(A, _desc(A), out=FAKE + 8) == EINVAL
+    assert _noalloc(A, _desc(A, d=96)) == EUNSUPPORTED
+    # argument errors win over the size check
+    assert _noalloc(A, too_big, cu=0) == EINVAL
+    # an empty batch needs nothing and enqueues nothing
+    assert _noalloc(A, _desc(A, T=0, D=0), q=0, k=0, v=0, sinks=0, qw=0, kw=0, out=0,
+                    lse=0) == OK
