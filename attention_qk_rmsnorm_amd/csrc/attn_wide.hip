@@ -33,8 +33,9 @@
 // visible).  Weights may exceed 1 -- exp2 of up to 90 keeps bf16 weights and
 // the fp32 sums finite and exact to their usual relative precision -- so the
 // loop never rescales O.  A block where some denominator passes 2^90 (a score
-// more than 90 log2 units above the reference) hands itself to a second
-// launch that finds the exact row max with a scores-only pass first.  fp16
+// more than 90 log2 units above the reference), or some O accumulator is not
+// finite (values beyond about 2^38 times such weights), hands itself to a
+// second launch that finds the exact row max with a scores-only pass first.  fp16
 // weights overflow past 2^16 instead: such a weight rounds to inf, its
 // denominator is no longer finite, and the same rerun takes the block.  Band
 // masks run only on half tiles that cross a document, causal or window edge;
@@ -579,16 +580,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_wide_kernel(
     l[cb] = lane_pair_sum(st.l_part[cb]);
     bad |= c.ok[cb] && !(l[cb] < kRedo);
   }
+  agpr_fence();
   if (!EXACT) {
     // a denominator at or past 2^90 (or not finite) hands the block to the
-    // follow-up launch
+    // follow-up launch; so does an O accumulator that is not finite, which
+    // huge values can cause first (weights up to 2^90 times |v| past about
+    // 2^38 overflow fp32 while the denominator is still in range).  The
+    // denominator is at least 1 (the reference's own weight), so a finite O
+    // gives a finite output.
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bad |= c.ok[cb] && !__builtin_isfinite(st.o[cb][dd][r]);
     if (__any(bad) && lane == 0) s_bad = 1;
     __syncthreads();
     const int block_bad = s_bad;
     if (tid == 0) redo[bid] = block_bad;
     if (block_bad) return;
   }
-  agpr_fence();
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     if (c.ok[cb]) {

@@ -190,3 +190,42 @@ def check_bwd_parity(inp: dict, window: int, use_rope: bool, label="", seed=0, *
     print(f"  {label}: rel max/mean " + ", ".join(msg), flush=True)
     assert not bad, f"{label}: " + "; ".join(bad)
     return g
+
+
+# ---- the wide tiles' redo table ----------------------------------------------
+# The forward workspace (16-bit paths) holds, in order and each 256-byte
+# aligned: the k_hat and V^T tile images (Hkv * t_pad * 128 elements each,
+# t_pad = T rounded up to 64), the narrow and the wide schedules (int32:
+# 4 + 2 * items_ub + D + 1 each, items_ub = T / tokens_per_block + D with
+# 128 / G and 256 / G tokens per block), then one int32 per wide workgroup:
+# 1 if the main launch handed the block to the exact-max launch.  A test that
+# reads it also checks the offset (every block marked when all are forced
+# through the exact pass, none on moderate inputs).
+
+def _round_up(x, m):
+    return (x + m - 1) // m * m
+
+
+def redo_table(call):
+    """(marked, blocks): the redo flags the last wide-tile forward of `call`
+    left in its workspace, and the number of workgroups that hold an item."""
+    d = call.desc
+    T, D, Hq, Hkv = d.total_tokens, d.num_docs, d.num_q_heads, d.num_kv_heads
+    G = Hq // Hkv
+    t_pad = _round_up(T, 64)
+    items_ub = T // (128 // G) + D
+    items_ub_wide = T // (256 // G) + D
+    off = _round_up(Hkv * t_pad * 128 * 2, 256)
+    off = _round_up(off + Hkv * t_pad * 128 * 2, 256)
+    off = _round_up(off + 4 * (4 + 2 * items_ub + D + 1), 256)
+    sched_wide_off = off
+    off = _round_up(off + 4 * (4 + 2 * items_ub_wide + D + 1), 256)
+    if Hkv <= 8 and 8 % Hkv == 0:
+        per = 8 // Hkv
+        grid = 8 * ((items_ub_wide + per - 1) // per)
+    else:
+        grid = items_ub_wide * Hkv
+    ws = call.workspace
+    redo = ws[off:off + 4 * grid].view(torch.int32).cpu().numpy()
+    n_items = int(ws[sched_wide_off:sched_wide_off + 4].view(torch.int32).item())
+    return redo, n_items * Hkv

@@ -31,6 +31,60 @@ def test_ragged_documents(window, use_rope):
     check_bwd_parity(custom_inputs(RAGGED), window, use_rope, label=f"W={window}")
 
 
+@pytest.mark.parametrize("use_rope", [False, True])
+def test_default_window_513(use_rope):
+    # the pages' default sliding window (flint.config FlintConfig
+    # sliding_window = 513 = 8 * 64 + 1) on documents longer than it
+    _say(f"case bwd W=513 rope={use_rope}")
+    check_bwd_parity(custom_inputs([1100, 513, 514, 37, 1040, 2]), 513, use_rope,
+                     label=f"W=513 rope={use_rope}")
+
+
+def test_causal_document_of_8192_tokens():
+    # one causal document of 8,192 tokens against the fp64 backward oracle,
+    # every element: key blocks deep in the document walk up to 2,048 column
+    # tiles through the dK/dV ring, and dQ blocks up to 128 key tiles.  One
+    # kv head with its 8 query heads (group size 8, as Flint's 32 / 4): the
+    # kernels treat every kv head alike and on their own.
+    _say("case bwd one causal doc 8192, 8q/1kv")
+    check_bwd_parity(custom_inputs([8192], Hq=8, Hkv=1), -1, False, label="causal 8192")
+
+
+def test_outputs_fully_written():
+    # NaN guard bands around dq, dk, dv and the parameter gradients: every
+    # element is written, nothing outside
+    _say("case bwd poison guards")
+    import attention_qk_rmsnorm_amd as A
+    inp = to_device(custom_inputs([333, 1, 90, 0, 700]))
+    T = 1124
+    nan = float("nan")
+    ref = gpu_backward(inp, 64, True)
+    out, lse = A.sink_attn_fwd(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"], inp["sinks"],
+                               inp["qnorm_w"], inp["knorm_w"], 64, True)
+    grads, bufs = {}, {}
+    for key, shape, dt in (("dq", (T, 32, 128), torch.bfloat16),
+                           ("dk", (T, 4, 128), torch.bfloat16),
+                           ("dv", (T, 4, 128), torch.bfloat16),
+                           ("dsinks", (32,), torch.float32),
+                           ("dqnorm_w", (128,), torch.float32),
+                           ("dknorm_w", (128,), torch.float32)):
+        n = int(np.prod(shape))
+        buf = torch.full((n + 256,), nan, dtype=dt, device="cuda:0")
+        bufs[key] = (buf, n)
+        grads[key] = buf[128:128 + n].view(shape)
+    import workloads
+    dout = workloads.make_grad_output(workloads.Workload("g", (T,), 32, 4, 128, "bf16"), 0)
+    g = A.sink_attn_bwd(inp["q"], inp["k"], inp["v"], inp["cu_seqlens"], inp["sinks"],
+                        inp["qnorm_w"], inp["knorm_w"], 64, True, out, lse,
+                        dout.to("cuda:0"), grads=grads)
+    torch.cuda.synchronize()
+    for key, (buf, n) in bufs.items():
+        assert torch.isfinite(g[key].float()).all(), key
+        assert torch.isnan(buf[:128].float()).all(), key
+        assert torch.isnan(buf[128 + n:].float()).all(), key
+        assert torch.equal(g[key], ref[key]), key
+
+
 def test_many_and_empty_documents():
     # a run of 80 empty documents inside one key tile and 4,315 documents in all
     lengths = [37] + [0] * 80 + [1] * 20 + [0] * 3 + [5] * 10 + [2, 0, 3] * 1400 + [90]

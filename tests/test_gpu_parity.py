@@ -54,6 +54,20 @@ def test_bf16_ragged_documents(window, use_rope):
     check_parity(inp, window, use_rope, label=f"ragged W={window}")
 
 
+# The pages' default sliding window, 513 = 8 * 64 + 1 (flint.config
+# FlintConfig sliding_window): a window edge one key past a tile boundary, on
+# documents longer than the window (shorter ones see the whole causal range).
+W513_LENGTHS = [1100, 513, 514, 37, 1040, 2]
+
+
+@pytest.mark.parametrize("use_rope", [False, True])
+@pytest.mark.parametrize("tile", [0, 1, 2])  # automatic, narrow, wide
+def test_bf16_default_window_513(tile, use_rope):
+    _say(f"case bf16 W=513 rope={use_rope} tile={tile}")
+    check_parity(custom_inputs(W513_LENGTHS), 513, use_rope, label=f"W=513 tile={tile}",
+                 tile_config=tile)
+
+
 # 80 empty documents inside one 64-token key tile (more document starts than
 # tokens: the prologue's per-tile document lookup leaves its window of 65
 # starts and searches memory) and 4,315 documents in all (more than the 4,096
@@ -194,7 +208,7 @@ def test_bf16_lse_optional_and_empty_batch():
 
 # ------------------------------------------------- full-size workloads ---
 
-def _sampled(name, n_random=192):
+def _sampled(name, n_random):
     w = workloads.named_workloads()[name]
     _say(f"case {name} T={w.total_tokens} D={w.num_docs} W={w.window} rope={w.use_rope}")
     inp = workloads.make_inputs(w)
@@ -212,6 +226,19 @@ def test_sliding_all_rows():
     _say(f"  sliding: out max/mean {eo[0]:.3e}/{eo[1]:.3e} lse {el[0]:.3e}/{el[1]:.3e}")
 
 
-@pytest.mark.parametrize("name", ["full", "long", "mixed_sliding", "mixed_causal"])
-def test_full_size_sampled_rows(name):
-    _sampled(name)
+# Full and Long: every document's first and last 64 rows, the rows around the
+# window edge and 4,096 seeded random rows; Mixed (whose rows are short):
+# the same edges and 1,024 random rows.
+@pytest.mark.parametrize("name,n_random", [("full", 4096), ("long", 4096),
+                                           ("mixed_sliding", 1024), ("mixed_causal", 1024)])
+def test_full_size_sampled_rows(name, n_random):
+    _sampled(name, n_random)
+
+
+def test_sliding_workload_at_window_513_all_rows():
+    # the sliding workload's documents (8 x U[256, 4096], RoPE) at the pages'
+    # default window of 513 instead of its 1024, every row
+    w = workloads.named_workloads()["sliding"]
+    _say(f"case sliding W=513 all rows T={w.total_tokens}")
+    inp = workloads.make_inputs(w)
+    check_parity(inp, 513, w.use_rope, label="sliding W=513")
