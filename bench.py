@@ -28,6 +28,17 @@ fill).  FLOP counts real visible entries only.
 --dtype f16 runs the same step on fp16 q, k, v and out (the fp16 I/O
 variant; fp16 and bf16 share the 2.5 PFLOP/s dense MFMA peak).
 
+Timing.  value = FLOP / (wall time of the K timed steps / K), the steps
+bracketed by torch.cuda.synchronize().  Each step also carries HIP events on
+its stream, which give the median and minimum per-call time ("timing").  The
+default run then times the other forward workloads (sliding, long,
+mixed_sliding, mixed_causal) as extra keys of the same line ("workloads"),
+each by the protocol: 3 warm-up calls, then max(10, ceil(200 ms / t)) calls
+with HIP events, median and minimum of the whole call and of each stage.
+These have no CPU leg.  The CPU leg's parity sample (out and lse against
+the oracle) must meet the bf16 bounds (max-abs 2e-2, mean-abs 2e-3):
+otherwise the line is still printed and bench.py exits with status 3.
+
 --pass bwd times the backward instead: a step is one sink_attn_bwd call (key
 and column tile preparation, the dK/dV and dQ kernels, the final sums) on the
 out and lse of one forward, counted as 2.5 forward passes
@@ -39,6 +50,7 @@ import argparse
 import dataclasses
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -59,7 +71,96 @@ CSRC = os.path.join(ROOT, "attention_qk_rmsnorm_amd", "csrc")
 ATTN_KERNELS = {1: ("attn_fwd_narrow_kernel", "attn_narrow.hip"),
                 2: ("attn_fwd_wide_kernel", "attn_wide.hip"),
                 3: ("attn_fwd_wide_kernel", "attn_wide.hip")}
+TILE_NAMES = {1: "narrow", 2: "wide", 3: "wide_exact"}
+TILE_CHOICES = {"auto": 0, "narrow": 1, "wide": 2, "wide_exact": 3}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_wide_traffic.json")
+PARITY_MAX, PARITY_MEAN = 2e-2, 2e-3   # bf16 bounds against the fp64 oracle
+OTHER_WORKLOADS = ("sliding", "long", "mixed_sliding", "mixed_causal")
+
+
+def protocol_calls(t_ms: float) -> int:
+    """Timed calls of the measurement protocol: max(10, ceil(200 ms / t))."""
+    return max(10, math.ceil(200.0 / max(t_ms, 1e-3)))
+
+
+def library_record(A) -> dict:
+    """Which build of the library this process loaded (path and sha256)."""
+    path = os.path.realpath(A.library_path())
+    return {"path": os.path.relpath(path, ROOT) if path.startswith(ROOT) else path,
+            "sha256": source_digest(path)[:16]}
+
+
+def stats_ms(xs) -> dict:
+    xs = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(xs)), "min": float(xs.min()), "mean": float(xs.mean())}
+
+
+def time_forward_stages(call, stream, n: int):
+    """n forward calls, each with HIP events around its two stages (K prologue
+    and schedule; attention) on the launch stream.  Returns per-call lists of
+    (prologue ms, attention ms)."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(stream)
+        call.prologue()
+        ev[i][1].record(stream)
+        call.attention()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    return ([e[0].elapsed_time(e[1]) for e in ev], [e[1].elapsed_time(e[2]) for e in ev])
+
+
+def other_workloads(A, dev, names) -> dict:
+    """The other forward workloads by the timing protocol (no CPU leg)."""
+    import torch
+    import workloads
+    res = {}
+    stream = torch.cuda.current_stream(dev)
+    ws = workloads.named_workloads()
+    cache = {}
+    for name in names:
+        w = ws[name]
+        key = (w.lengths, w.dtype)
+        if key not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            cache[key] = {k: v.to(dev) for k, v in workloads.make_inputs(w, seed=0).items()}
+        d = cache[key]
+        call = A.Call(d["q"], d["k"], d["v"], d["cu_seqlens"], d["sinks"], d["qnorm_w"],
+                      d["knorm_w"], w.window, w.use_rope, rms_eps=w.rms_eps,
+                      rope_theta=w.rope_theta)
+        for _ in range(3):
+            call.fwd()
+        torch.cuda.synchronize()
+        pro, attn = time_forward_stages(call, stream, 3)
+        n = protocol_calls(float(np.median(np.add(pro, attn))))
+        pro, attn = time_forward_stages(call, stream, n)
+        tot = np.add(pro, attn)
+        flop = 4.0 * w.head_dim * w.num_q_heads * visible_entries(w.lengths, w.window)
+        med = float(np.median(tot))
+        res[name] = {
+            "workload": w.description, "tokens": w.total_tokens, "docs": w.num_docs,
+            "window": w.window, "rope": w.use_rope,
+            "tile_config": TILE_NAMES[A.tile_config(call.desc, w.window)],
+            "flop": flop, "calls": n,
+            "call_ms": stats_ms(tot), "prologue_ms": stats_ms(pro), "attention_ms": stats_ms(attn),
+            "tflops_median": flop / (med * 1e-3) / 1e12,
+            "pct_bf16_peak_median": 100.0 * flop / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "attention_tflops_median": flop / (float(np.median(attn)) * 1e-3) / 1e12,
+        }
+        del call
+    cache.clear()
+    torch.cuda.empty_cache()
+    return res
+
+
+def parity_ok(base) -> bool:
+    p = (base or {}).get("parity_on_sample")
+    if not p:
+        return True
+    return (p["out_max_abs"] <= PARITY_MAX and p["out_mean_abs"] <= PARITY_MEAN
+            and p["lse_max_abs"] <= PARITY_MAX and p["lse_mean_abs"] <= PARITY_MEAN)
 
 
 def visible_entries(lengths, window: int) -> int:
@@ -139,7 +240,9 @@ def cpu_baseline(inp, w, out_gpu, lse_gpu, target_seconds: float):
                    f"{flop:.3e} FLOP), fp64, {dt:.1f} s"),
         "seconds": dt,
         "parity_on_sample": {"out_max_abs": float(err.max()), "out_mean_abs": float(err.mean()),
-                             "lse_max_abs": float(lerr.max())},
+                             "lse_max_abs": float(lerr.max()),
+                             "lse_mean_abs": float(lerr.mean()),
+                             "bounds": {"max_abs": PARITY_MAX, "mean_abs": PARITY_MEAN}},
     }
 
 
@@ -264,6 +367,7 @@ def run_fwd_padded(args, A, w, inp, d_inp, dev):
             "avg_launch_ms": call_ms,
         },
         "kernels": {"mask_to_seqlens_ms": float(np.median(mask_ms))},
+        "library": library_record(A),
     }
     if args.cpu_seconds > 0:
         call.fwd()
@@ -275,6 +379,10 @@ def run_fwd_padded(args, A, w, inp, d_inp, dev):
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+    if not parity_ok(result["cpu_baseline"]):
+        print("bench.py: the GPU result misses the bf16 bounds on the oracle's sample",
+              file=sys.stderr)
+        sys.exit(3)
 
 
 def run_bwd(args, A, w, d_inp, call, dev):
@@ -301,7 +409,19 @@ def run_bwd(args, A, w, d_inp, call, dev):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
-    call_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    call_l = [e[0].elapsed_time(e[1]) for e in ev]
+    n_proto = protocol_calls(float(np.median(call_l)))
+    if n_proto > args.steps and not args.quick:
+        # more calls for the per-call statistics, after the timed region
+        ev2 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+               for _ in range(n_proto - args.steps)]
+        for e in ev2:
+            e[0].record(stream)
+            bc.run()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        call_l += [e[0].elapsed_time(e[1]) for e in ev2]
+    call_ms = float(np.mean(call_l[:args.steps]))
     n_vis = visible_entries(w.lengths, w.window)
     flop = 10.0 * w.head_dim * w.num_q_heads * n_vis
     value = flop / (ms_step * 1e-3) / 1e12
@@ -337,6 +457,10 @@ def run_bwd(args, A, w, d_inp, call, dev):
             "traffic": None,
             "avg_launch_ms": call_ms,
         },
+        "timing": {"calls": len(call_l), "protocol_calls": n_proto,
+                   "call_ms": stats_ms(call_l),
+                   "tflops_median": flop / (float(np.median(call_l)) * 1e-3) / 1e12},
+        "library": library_record(A),
     }
     result["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_seconds) if args.cpu_seconds > 0
                               else None)
@@ -361,6 +485,14 @@ def main():
                     help="time the forward (default) or the backward pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--tile", default="auto", choices=list(TILE_CHOICES),
+                    help="attention tile configuration (default: the library's automatic "
+                         "choice)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other forward workloads the default run also times")
+    ap.add_argument("--quick", action="store_true",
+                    help="time exactly the K steps (no extra calls for the per-call "
+                         "statistics, no other workloads): for runs under a profiler")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -401,7 +533,8 @@ def main():
     call = A.Call(d_inp["q"], d_inp["k"], d_inp["v"], d_inp["cu_seqlens"], d_inp["sinks"],
                   d_inp["qnorm_w"], d_inp["knorm_w"], w.window, w.use_rope,
                   rms_eps=w.rms_eps, rope_theta=w.rope_theta,
-                  cu_seqlens_padded=d_inp.get("cu_seqlens_padded"))
+                  cu_seqlens_padded=d_inp.get("cu_seqlens_padded"),
+                  tile_config=TILE_CHOICES[args.tile])
     if args.which == "bwd":
         run_bwd(args, A, w, d_inp, call, dev)
         return
@@ -431,8 +564,17 @@ def main():
     elapsed = time.perf_counter() - t0
 
     ms_step = elapsed * 1e3 / args.steps
-    pro_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    pro_l = [e[0].elapsed_time(e[1]) for e in ev]
+    attn_l = [e[1].elapsed_time(e[2]) for e in ev]
+    pro_ms = float(np.mean(pro_l))
+    attn_ms = float(np.mean(attn_l))
+    call_l = np.add(pro_l, attn_l)
+    n_proto = protocol_calls(float(np.median(call_l)))
+    if n_proto > args.steps and not args.quick:
+        # more calls for the per-call statistics, after the timed region
+        p2, a2 = time_forward_stages(call, stream, n_proto - args.steps)
+        pro_l, attn_l = pro_l + p2, attn_l + a2
+        call_l = np.add(pro_l, attn_l)
     n_vis = visible_entries(w.lengths, w.window)
     flop = 4.0 * w.head_dim * w.num_q_heads * n_vis
     value = flop / (ms_step * 1e-3) / 1e12
@@ -458,7 +600,7 @@ def main():
             "tokens": T, "docs": w.num_docs, "q_heads": w.num_q_heads,
             "kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "window": w.window,
             "rope": w.use_rope, "visible_entries": n_vis, "flop_per_step": flop,
-            "tile_config": {1: "narrow", 2: "wide", 3: "wide_exact"}[tile],
+            "tile_config": TILE_NAMES[tile],
             "parallelism": "single GPU",
         },
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
@@ -479,6 +621,16 @@ def main():
             "prologue_frac_hbm": pro_bytes / (pro_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "attention_ms": attn_ms,
         },
+        # per-call HIP-event times of the K timed steps (the protocol asks for
+        # max(10, ceil(200 ms / t)) calls: protocol_calls)
+        "timing": {
+            "calls": len(call_l), "protocol_calls": n_proto,
+            "call_ms": stats_ms(call_l), "prologue_ms": stats_ms(pro_l),
+            "attention_ms": stats_ms(attn_l),
+            "tflops_median": flop / (float(np.median(call_l)) * 1e-3) / 1e12,
+            "tflops_min_time": flop / (float(np.min(call_l)) * 1e-3) / 1e12,
+        },
+        "library": library_record(A),
     }
     if args.cpu_seconds > 0:
         call.fwd()
@@ -486,7 +638,16 @@ def main():
         result["cpu_baseline"] = cpu_baseline(inp, w, call.out, call.lse, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
+    if (not args.no_others and not args.quick and args.workload == "full"
+            and args.dtype in (None, "bf16") and args.tile == "auto"):
+        del call, d_inp
+        torch.cuda.empty_cache()
+        result["workloads"] = other_workloads(A, dev, OTHER_WORKLOADS)
     print(json.dumps(result), flush=True)
+    if not parity_ok(result["cpu_baseline"]):
+        print("bench.py: the GPU result misses the bf16 bounds on the oracle's sample "
+              f"({result['cpu_baseline']['parity_on_sample']})", file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":
