@@ -719,6 +719,6 @@ const char* sink_attn_status_string(int status) {
   }
 }
 
-int sink_attn_version(void) { return 400; }
+int sink_attn_version(void) { return 500; }
 
 }  // extern "C"

@@ -56,6 +56,16 @@
  *     category per query head whose logit is sinks[h] (used as given, not
  *     multiplied by softmax_scale) and whose value is zero.
  *     lse[h, i] = log of the full denominator, sink included (natural log).
+ *   - Accuracy of the 16-bit paths against an exact (fp64) evaluation of the
+ *     same definition: max-abs 2e-2 and mean-abs 2e-3 on out and lse for
+ *     bf16 storage (4e-3 and 3e-4 for fp16) at Flint's settings -- scores
+ *     scale * <q_hat, k_hat> of unit-RMS heads with norm weights near 1 and
+ *     the default scale 1/sqrt(128).  The rounding of q_hat and k_hat to the
+ *     storage type moves a score by up to 2 * 2^-9 (bf16; 2^-11 fp16) of
+ *     scale * sum_i |q_hat_i k_hat_i|, so that error grows in proportion to
+ *     softmax_scale and to the product of the two norm weights: at a scale
+ *     of 0.2 (1.8 times the default) one bf16 case measured 0.022.  The fp32
+ *     path agrees within 1e-5.
  */
 #ifndef SINK_ATTN_H
 #define SINK_ATTN_H
@@ -128,6 +138,9 @@ typedef struct {
 } sink_attn_desc;
 
 /* Bytes of device workspace a call with this descriptor needs (0 when T == 0).
+ * Not on the pages: the library's own scratch (normalised keys, the value
+ * layout the attention stage reads, the work schedule), which the caller
+ * allocates so that the library never allocates device memory.
  * Depends only on total_tokens, num_docs, num_q_heads, num_kv_heads, head_dim
  * and dtype (not on tile_config).
  * Returns 0 for a NULL or invalid descriptor. */
@@ -136,6 +149,13 @@ size_t sink_attn_workspace_bytes(const sink_attn_desc* desc);
 /* The whole forward pass: normalised/rotated Q and K, band-limited attention
  * with the sink, out and lse.  Equivalent to sink_attn_prologue followed by
  * sink_attn_attention on the same stream.
+ * Defined by "flint.layers" FlintAttention.forward (causal attention with a
+ * zero-value sink category over document-local positions), FlintAttention's
+ * q_norm / k_norm and _apply_rope, _FlintSinkParameters (unscaled fp32
+ * logits, one per query head), "flint.config" FlintConfig (sliding window
+ * counting the current token; RoPE on sliding layers only; rms_norm_eps) and
+ * "attention.utils" preprocess_args_and_kwargs_for_attn (THD layout,
+ * cu_seqlens, window_size).
  *   q [T,Hq,d], k [T,Hkv,d], v [T,Hkv,d]   inputs in desc->dtype (16-byte aligned)
  *   cu_seqlens  int32 [D+1]
  *   sinks       fp32 [Hq], unscaled logits (finite, or -inf to disable a head's sink)
@@ -152,14 +172,19 @@ int sink_attn_fwd(const sink_attn_desc* desc, const void* q, const void* k,
 
 /* First stage of sink_attn_fwd: RMSNorm (+ RoPE) of K into the workspace, the
  * value layout the attention stage reads, and the varlen work schedule derived
- * from cu_seqlens.  Writes only the workspace. */
+ * from cu_seqlens.  Writes only the workspace.
+ * Defined by "flint.layers" FlintAttention (k_norm, _apply_rope: the two
+ * halves of each head rotated together) and "attention.utils"
+ * preprocess_args_and_kwargs_for_attn (cu_seqlens document boundaries). */
 int sink_attn_prologue(const sink_attn_desc* desc, const void* k, const void* v,
                        const int32_t* cu_seqlens, const float* knorm_w,
                        int32_t use_rope, void* stream);
 
 /* Second stage of sink_attn_fwd: RMSNorm (+ RoPE) of Q fused with the
  * attention itself.  Reads the workspace a preceding sink_attn_prologue with
- * the same descriptor, k, v, cu_seqlens, knorm_w and use_rope filled. */
+ * the same descriptor, k, v, cu_seqlens, knorm_w and use_rope filled.
+ * Defined by "flint.layers" FlintAttention.forward (the sink category) with
+ * q_norm and _apply_rope, and _FlintSinkParameters. */
 int sink_attn_attention(const sink_attn_desc* desc, const void* q,
                         const int32_t* cu_seqlens, const float* sinks,
                         const float* qnorm_w, int32_t window, int32_t use_rope,
@@ -167,13 +192,19 @@ int sink_attn_attention(const sink_attn_desc* desc, const void* q,
 
 /* The tile configuration (SINK_ATTN_TILE_NARROW, _WIDE or _WIDE_EXACT) that
  * sink_attn_attention would use for this descriptor and window, 0 for the fp32
- * path, or a negative status for an invalid descriptor or window == 0.  The
+ * path, or a negative status for an invalid descriptor or window == 0.
+ * Not on the pages: a choice between two kernels of this library that
+ * compute the same function.  The
  * automatic choice takes the wide tiles when the window (capped by the mean
  * document length T / D), or half the mean length when causal, is at least
  * 2048 keys.  Reads no device memory. */
 int sink_attn_tile_config(const sink_attn_desc* desc, int32_t window);
 
-/* Padded THD.  cu_seqlens holds the real document lengths (as prefix sums)
+/* Padded THD.  Defined by "flint.layers" FlintAttention.forward
+ * (attention_mask: padded queries and keys leave the real attention, the
+ * sink stays valid) and "attention.utils" (packed inputs may carry
+ * cu_seqlens_padded beside cu_seqlens).
+ * cu_seqlens holds the real document lengths (as prefix sums)
  * and cu_seqlens_padded, also int32 [D+1], where each document starts in the
  * packed tensors: document n's real tokens are
  *   [cu_seqlens_padded[n], cu_seqlens_padded[n] + cu_seqlens[n+1] - cu_seqlens[n])
@@ -192,7 +223,9 @@ int sink_attn_fwd_padded(const sink_attn_desc* desc, const void* q, const void* 
                          const float* qnorm_w, const float* knorm_w, int32_t window,
                          int32_t use_rope, void* out, float* lse, void* stream);
 
-/* Padded-THD boundaries of a BSHD attention mask: attention_mask is a device
+/* Padded-THD boundaries of a BSHD attention mask ("flint.layers"
+ * FlintAttention.forward: BSHD takes trailing padding, other padding is
+ * packed as THD): attention_mask is a device
  * uint8 [batch][seq] (nonzero = real token) whose rows must be a run of real
  * tokens followed by padding (trailing padding, as Transformer Engine's BSHD
  * takes; other padding has to be packed as THD).  Writes cu_seqlens and
@@ -206,13 +239,18 @@ int sink_attn_mask_to_seqlens(const uint8_t* attention_mask, int32_t batch, int3
                               int32_t* bad_rows, void* stream);
 
 /* Bytes of device workspace sink_attn_bwd needs for this descriptor (0 when
- * T == 0, for the fp32 path, or for an invalid descriptor).  The forward's
+ * T == 0, for the fp32 path, or for an invalid descriptor).  Not on the
+ * pages: the backward's own scratch (key and column tile images, partial
+ * sums), which the caller allocates.  The forward's
  * workspace can be reused once the forward has completed; the backward does
  * not read what the forward left there. */
 size_t sink_attn_bwd_workspace_bytes(const sink_attn_desc* desc);
 
 /* Backward pass of sink_attn_fwd (bf16 and fp16): the gradients of
  * L = sum(dout * out) with respect to every input of the forward.
+ * Defined by the forward's pages plus "flint.layers" _FlintSinkParameters
+ * (the sinks are trainable parameters) and FlintAttention's q_norm / k_norm
+ * (RMSNorm modules with weights).
  *   q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope
  *               exactly as passed to the forward
  *   out [T,Hq,d] (desc->dtype) and lse fp32 [Hq,T]: what that forward wrote (lse is
@@ -235,7 +273,7 @@ int sink_attn_bwd(const sink_attn_desc* desc, const void* q, const void* k,
                   float* dqnorm_w, float* dknorm_w, void* stream);
 
 /* Backward of sink_attn_fwd_padded: as sink_attn_bwd, with padded-THD
- * boundaries.  Padding rows of dq, dk and dv are written as zeros; padding
+ * boundaries ("flint.layers" FlintAttention.forward attention_mask).  Padding rows of dq, dk and dv are written as zeros; padding
  * rows contribute nothing to dsinks and the norm-weight gradients. */
 int sink_attn_bwd_padded(const sink_attn_desc* desc, const void* q, const void* k,
                          const void* v, const int32_t* cu_seqlens,
@@ -273,10 +311,12 @@ int sink_attn_fwd_noalloc(const sink_attn_desc* desc, const void* q, const void*
                           const float* qnorm_w, const float* knorm_w, int32_t window,
                           int32_t use_rope, void* out, float* lse, void* stream);
 
-/* Static text for a status code (never NULL). */
+/* Static text for a status code (never NULL).  Errors are returned, never
+ * worked around ("flint.layers" _validate_backend rejects an unsupported
+ * backend; "attention.utils" raises when a layout cannot be consumed). */
 const char* sink_attn_status_string(int status);
 
-/* Library version as major * 10000 + minor * 100 + patch. */
+/* Library version as major * 10000 + minor * 100 + patch (not on the pages). */
 int sink_attn_version(void);
 
 #ifdef __cplusplus
