@@ -124,11 +124,12 @@ __device__ __forceinline__ void mask_half(int kh, const Cols& c, f32x16 (&s)[2])
 // Weights of keys 16jj .. 16jj + 15 of a half tile for column block cb:
 // B operand k-slot 8hf + e <-> key 16jj + 8(e/4) + 4hf + e%4, the order the
 // prologue stored V^T keys in.
-// (elements 4h .. 4h + 3 only: the exps are spread over the score MFMAs)
+// (elements 2q, 2q + 1 only: the exps are spread over the score MFMAs, two
+// behind each, about as many issue cycles as the MFMA itself)
 template <typename E>
-__device__ __forceinline__ void weights_half(const f32x16& sv, int jj, int h, vec8<E>& pb) {
+__device__ __forceinline__ void weights_pair(const f32x16& sv, int jj, int q, vec8<E>& pb) {
 #pragma unroll
-  for (int e = 4 * h; e < 4 * h + 4; ++e) pb[e] = (E)__builtin_amdgcn_exp2f(sv[8 * jj + e]);
+  for (int e = 2 * q; e < 2 * q + 2; ++e) pb[e] = (E)__builtin_amdgcn_exp2f(sv[8 * jj + e]);
 }
 
 template <typename E>
@@ -178,26 +179,38 @@ __device__ __forceinline__ void half_step(const char* lds, const int (&koff)[8],
   // fragments, are read up front: with one wave per SIMD nothing else hides
   // LDS latency, so each MFMA waits only for its own fragment.
   const char* vbuf = lds + VS * kSlot + kTileK;
-  vec8<E> va[4];
+  vec8<E> va[4], vn[4];
   vec8<E> p[2][2];
   {
     // kf: this half tile's K fragments (K slot KS, half KH), read during the
-    // previous half step
-#pragma unroll
-    for (int dd = 0; dd < 4; ++dd) va[dd] = rd<E>(vbuf + dd * 4096 + voff[2 * VH]);
+    // previous half step.  Both PV steps' V^T fragments are read here, after
+    // the first score MFMA: the compiler waits for every LDS read in flight
+    // before an MFMA whose operand an LDS read returns, so reads issued just
+    // before the score chain (which needs kf) or in the middle of the PV
+    // steps would be waited for there; issued here, they land behind 15 score
+    // MFMAs, and phase B's K reads land behind the PV MFMAs
     sn[0] = st.negm[0];  // the chains start from -m_ref: no separate subtraction
     sn[1] = st.negm[1];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
+      // two weights behind each MFMA: group g = kk / 2 (cb = g / 2,
+      // jj = g % 2), elements 4 (kk % 2) .. + 3.  Four exps take longer to
+      // issue than one MFMA runs, so four behind one MFMA of the pair would
+      // hold back the next
+      const int g = kk >> 1;
       __builtin_amdgcn_sched_barrier(0);
       sn[0] = mfma32(kf[kk], st.qf[0][kk], sn[0]);
-      {
-        // four weights per MFMA pair: group g = kk / 2 (cb = g / 2, jj = g % 2),
-        // elements 4 (kk % 2) .. + 3
-        const int g = kk >> 1;
-        weights_half<E>(sc[g >> 1], g & 1, kk & 1, p[g >> 1][g & 1]);
+      if (kk == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) va[dd] = rd<E>(vbuf + dd * 4096 + voff[2 * VH]);
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) vn[dd] = rd<E>(vbuf + dd * 4096 + voff[2 * VH + 1]);
       }
+      weights_pair<E>(sc[g >> 1], g & 1, 2 * (kk & 1), p[g >> 1][g & 1]);
+      __builtin_amdgcn_sched_barrier(0);
       sn[1] = mfma32(kf[kk], st.qf[1][kk], sn[1]);
+      weights_pair<E>(sc[g >> 1], g & 1, 2 * (kk & 1) + 1, p[g >> 1][g & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -206,7 +219,6 @@ __device__ __forceinline__ void half_step(const char* lds, const int (&koff)[8],
   // the weights were just written by VALU code; the inline-asm MFMAs below
   // read them, and the compiler does not count wait states for inline asm
   asm volatile("s_nop 1");
-  vec8<E> vn[4];
 #pragma unroll
   for (int jj = 0; jj < 2; ++jj) {
     __builtin_amdgcn_sched_barrier(0);
@@ -215,10 +227,8 @@ __device__ __forceinline__ void half_step(const char* lds, const int (&koff)[8],
       mfma32_acc(st.o[0][dd], va[dd], p[0][jj]);
       mfma32_acc(st.o[1][dd], va[dd], p[1][jj]);
       if (jj == 0 && dd == 0) {
-        // the second PV step's fragments, and the next half step's K
-        // fragments (K slot KSN, half KHN), behind the first MFMAs
-#pragma unroll
-        for (int d2 = 0; d2 < 4; ++d2) vn[d2] = rd<E>(vbuf + d2 * 4096 + voff[2 * VH + 1]);
+        // the next half step's K fragments (K slot KSN, half KHN), behind
+        // the first MFMAs
         const char* knext = lds + KSN * kSlot + KHN * 8192;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) kf[kk] = rd<E>(knext + koff[kk]);
