@@ -113,14 +113,31 @@ def _kernel(text, marker):
 
 
 def _main_loop(body):
-    """Lines of the first loop with MFMAs in it (from its header label to the
-    branch back): the key loop, past any set-up loops."""
+    """Lines of the first loop with MFMAs in it: the blocks the compiler
+    annotates as that loop's header or as lying in it (LLVM places latch
+    blocks before the header, so the loop is not one contiguous range from the
+    header to a branch back to it)."""
     lines = [l.strip() for l in body.splitlines()]
-    for head in (i for i, l in enumerate(lines) if "Loop Header" in l):
-        label = lines[head].split(":")[0]
-        back = max(i for i, l in enumerate(lines) if l.startswith("s_") and l.endswith(" " + label))
-        if any(l.startswith("v_mfma") for l in lines[head:back + 1]):
-            return lines[head:back + 1]
+    blocks, cur = [], None
+    for l in lines:
+        m = re.match(r"^(?:\.L(BB\d+_\d+):|; %bb\.\d+:)(.*)$", l)
+        if m:
+            own = m.group(1)
+            note = m.group(2)
+            if "Loop Header" in note:
+                hdr = own
+            else:
+                h = re.search(r"Header=(BB\d+_\d+)", note)
+                hdr = h.group(1) if h else None
+            cur = [hdr, own, []]
+            blocks.append(cur)
+        elif cur is not None:
+            cur[2].append(l)
+    headers = [b[1] for b in blocks if b[0] is not None and b[0] == b[1]]
+    for h in headers:
+        loop = [x for b in blocks if b[0] == h for x in b[2]]
+        if any(x.startswith("v_mfma") for x in loop):
+            return loop
     raise AssertionError("no loop with MFMAs")
 
 
@@ -143,9 +160,15 @@ def test_wide_kernel_loop_keeps_accumulators_in_agprs(asm):
 def test_wide_kernel_waits_for_copies_only_at_barriers(asm):
     loop = _main_loop(_kernel(asm["attn_wide.hip"], "wide_kernelILb0"))
     code = [l for l in loop if l and not l.startswith(";")]
+    waits = 0
     for i, l in enumerate(code):
         if l.startswith("s_waitcnt") and "vmcnt" in l:
-            assert any(x.startswith("s_barrier") for x in code[i + 1:i + 3]), code[i:i + 4]
+            waits += 1
+            # the next barrier comes before any LDS read or MFMA
+            nxt = next((x for x in code[i + 1:]
+                        if x.startswith(("s_barrier", "ds_read", "v_mfma"))), None)
+            assert nxt is not None and nxt.startswith("s_barrier"), code[i:i + 6]
+    assert waits >= 2
 
 
 def _regs(tok):
