@@ -426,21 +426,44 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
   }
 
   // ---- epilogue: out = O / l in E, lse = ln2 * (m + log2 l) ----------------
+  // A lane holds 4-channel pieces of one output row, so storing from the
+  // accumulators would write 16 bytes into each of 32 rows per instruction.
+  // The wave's 32 rows go through LDS instead -- the tile buffer the last tile
+  // did not use: no copy is in flight into it, and every wave has passed the
+  // barrier of the last tile, so no wave still reads it -- and each store
+  // instruction then writes 4 whole 256-byte rows.  Row r sits at r * 256 with
+  // its 16-byte chunk c at position c ^ (r % 16).
   const float l = lane_pair_sum(st.l_part);
-  if (tok_ok) {
+  const int n_tiles = kt_lo < hi ? (hi - kt_lo + kKeyTile - 1) / kKeyTile : 0;
+  char* obuf = lds + (n_tiles & 1) * kBuf + wave * (32 * 256);
+  {
     const float inv_l = 1.0f / l;
-    E* op = out + ((size_t)tok * Hq + hq) * kHeadDim + 4 * hf;
 #pragma unroll
     for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
+        // channels 32dd + 8rq + 4hf .. + 3: chunk 4dd + rq, bytes 8hf .. + 7
         vec4<E> w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = (E)(st.o[dd][4 * rq + e] * inv_l);
-        *reinterpret_cast<vec4<E>*>(op + 32 * dd + 8 * rq) = w;
+        const int pos = ((4 * dd + rq) ^ (col & 15)) << 4;
+        *reinterpret_cast<vec4<E>*>(obuf + col * 256 + pos + 8 * hf) = w;
       }
-    if (lse != nullptr && hf == 0) lse[(size_t)hq * T + tok] = (st.m_ref + __log2f(l)) * kLn2;
   }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    // row r = 4j + lane/16 of the wave (column r: token tw0 + r/G, head g G + r%G),
+    // chunk lane % 16
+    const int r = 4 * j + (lane >> 4), c = lane & 15;
+    const vec8<E> v = *reinterpret_cast<const vec8<E>*>(obuf + r * 256 + ((c ^ (r & 15)) << 4));
+    const int tr = tw0 + (r >> log2G);
+    if (tr < a_end)
+      *reinterpret_cast<vec8<E>*>(out + ((size_t)tr * Hq + g * G + (r & (G - 1))) * kHeadDim +
+                                  8 * c) = v;
+  }
+  if (tok_ok && lse != nullptr && hf == 0)
+    lse[(size_t)hq * T + tok] = (st.m_ref + __log2f(l)) * kLn2;
 }
 
 }  // namespace
