@@ -610,24 +610,47 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_wide_kernel(
     if (tid == 0) redo[bid] = block_bad;
     if (block_bad) return;
   }
+  // A lane holds 4-channel pieces of its two columns' output rows, so storing
+  // from the accumulators would write 16 bytes into each of 32 rows per
+  // instruction.  The wave's 64 rows go through LDS instead (16 KiB per wave
+  // in the first two slots: past the barrier above, or the one below in the
+  // follow-up launch, no wave reads a tile and no copy is in flight), and each
+  // store instruction writes 4 whole 256-byte rows.  Row r sits at r * 256
+  // with its 16-byte chunk k at position k ^ (r % 16).
+  if (EXACT) __syncthreads();
+  char* obuf = lds + wave * (64 * 256);
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    if (c.ok[cb]) {
-      const float inv_l = 1.0f / l[cb];
-      E* op = out + ((size_t)c.tok[cb] * Hq + hq[cb]) * kHeadDim + 4 * hf;
+    const float inv_l = 1.0f / l[cb];
+    const int row = 32 * cb + col;
 #pragma unroll
-      for (int dd = 0; dd < 4; ++dd)
+    for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          vec4<E> w;
+      for (int rq = 0; rq < 4; ++rq) {
+        // channels 32dd + 8rq + 4hf .. + 3: chunk 4dd + rq, bytes 8hf .. + 7
+        vec4<E> w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (E)(st.o[cb][dd][4 * rq + e] * inv_l);
-          *reinterpret_cast<vec4<E>*>(op + 32 * dd + 8 * rq) = w;
-        }
-      if (lse != nullptr && hf == 0)
-        lse[(size_t)hq[cb] * T + c.tok[cb]] = (st.m_ref[cb] + __log2f(l[cb])) * kLn2;
-    }
+        for (int e = 0; e < 4; ++e) w[e] = (E)(st.o[cb][dd][4 * rq + e] * inv_l);
+        const int pos = ((4 * dd + rq) ^ (row & 15)) << 4;
+        *reinterpret_cast<vec4<E>*>(obuf + row * 256 + pos + 8 * hf) = w;
+      }
   }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    // row r = 4j + lane/16 of the wave (column r: token tw0 + r/G, head g G + r%G),
+    // chunk lane % 16
+    const int r = 4 * j + (lane >> 4), k = lane & 15;
+    const vec8<E> v = *reinterpret_cast<const vec8<E>*>(obuf + r * 256 + ((k ^ (r & 15)) << 4));
+    const int tr = c.tw0 + (r >> log2G);
+    if (tr < a_end)
+      *reinterpret_cast<vec8<E>*>(out + ((size_t)tr * Hq + g * G + (r & (G - 1))) * kHeadDim +
+                                  8 * k) = v;
+  }
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+    if (c.ok[cb] && lse != nullptr && hf == 0)
+      lse[(size_t)hq[cb] * T + c.tok[cb]] = (st.m_ref[cb] + __log2f(l[cb])) * kLn2;
 }
 
 }  // namespace
