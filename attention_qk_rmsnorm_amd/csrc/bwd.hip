@@ -142,19 +142,30 @@ __device__ __forceinline__ void copy_col_tile(const char* __restrict__ src, int 
                                      (lds_void*)(uintptr_t)a, 16, 0, 0);
 }
 
+// Rows of 128 16-bit channels staged in LDS: row r at r * 256, its 16-byte
+// chunk k at position k ^ (r % 16).  A lane of the MFMA accumulator layout
+// holds 4-channel pieces of one row (channels 32dd + 8rq + 4hf .. + 3: chunk
+// 4dd + rq, bytes 8hf .. + 7); global memory is read and written 4 whole
+// rows per instruction (row 4j + lane/16, chunk lane % 16) and the pieces go
+// through LDS, instead of 32 rows x 8 bytes per instruction.
+__device__ __forceinline__ int stage_pos(int r, int k) { return r * 256 + ((k ^ (r & 15)) << 4); }
+
 // Backward of the rotation and the RMSNorm for one head vector held by a lane
 // pair: lane half hf holds the gradient w.r.t. the normalised, rotated vector
 // for channels 32dd + 8rq + 4hf + e at dy[16dd + 4rq + e] (dd, rq, e < 4).
-// xp points at the raw input row (+ 4hf), w at the norm weight; pos is the
-// document position (rope only).  ok: the row is a real token (a padding row
-// may hold anything and gets a zero gradient).  Writes dx (zero when !ok) to
-// dxp when store, and dy x r (zero when !ok) to wsum in dy's order.
+// The raw input row is staged row `row` of `rows`, and dx replaces it there
+// (in place: each piece is read before it is written); w is the norm weight,
+// pos the document position (rope only).  ok: the row is a real token (a
+// padding row may hold anything and gets a zero gradient).  dx is zero when
+// !ok, and dy x r (zero when !ok) goes to wsum in dy's order.
 template <typename E>
-__device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const E* __restrict__ xp,
-                                              const float* __restrict__ w, bool ok, bool store,
-                                              bool rope,
-                                              int pos, const double* s_invf, float eps, int hf,
-                                              E* __restrict__ dxp, float (&wsum)[64]) {
+__device__ __forceinline__ void norm_rope_bwd_staged(float (&dy)[64], char* rows, int row,
+                                                     const float* __restrict__ w, bool ok,
+                                                     bool rope, int pos, const double* s_invf,
+                                                     float eps, int hf, float (&wsum)[64]) {
+  auto piece = [&](int dd, int rq) {
+    return reinterpret_cast<vec4<E>*>(rows + stage_pos(row, 4 * dd + rq) + 8 * hf);
+  };
   if (rope && ok) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {  // channel 32dd + 8rq + 4hf + e (dd < 2), partner + 64
@@ -171,7 +182,7 @@ __device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const E* __restri
   for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const vec4<E> xv = *reinterpret_cast<const vec4<E>*>(xp + 32 * dd + 8 * rq);
+      const vec4<E> xv = *piece(dd, rq);
       const f32x4 wv = *reinterpret_cast<const f32x4*>(w + 32 * dd + 8 * rq + 4 * hf);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -188,7 +199,7 @@ __device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const E* __restri
   for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
-      const vec4<E> xv = *reinterpret_cast<const vec4<E>*>(xp + 32 * dd + 8 * rq);
+      const vec4<E> xv = *piece(dd, rq);  // read again rather than held in registers
       const f32x4 wv = *reinterpret_cast<const f32x4*>(w + 32 * dd + 8 * rq + 4 * hf);
       vec4<E> o;
 #pragma unroll
@@ -197,9 +208,13 @@ __device__ __forceinline__ void norm_rope_bwd(float (&dy)[64], const E* __restri
         o[e] = (E)(ok ? wv[e] * g * r - x * coef : 0.f);
         wsum[16 * dd + 4 * rq + e] = g * x * r;
       }
-      if (store) *reinterpret_cast<vec4<E>*>(dxp + 32 * dd + 8 * rq) = o;
+      *piece(dd, rq) = o;
     }
 }
+
+// LDS writes and reads of one wave in program order (the rows a lane reads
+// were written by other lanes of the same wave)
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // ============================================================================
 // bwd_keys_kernel: one block per (64-key tile, kv head)
@@ -697,18 +712,37 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
   agpr_fence();
 
   // ---- epilogue: lane holds channels 32dd + 8(r/4) + 4hf + r%4 of key u ----
+  // Each wave stages its 32 keys' rows in ring slot 2 + wave (past the
+  // barrier above no copy is in flight and no wave reads a tile): dv rows in
+  // the first 8 KiB, k rows (then dk in place) in the second.
+  char* vrows = slot(2 + wave);
+  char* krows = vrows + 32 * 256;
+  // row r of the wave: key ua + r (ua = kb0 + 32 wave)
   // dv: the accumulation is the gradient
-  if (u_ok) {
-    E* vp = dv + ((size_t)u * Hkv + g) * kHeadDim + 4 * hf;
 #pragma unroll
-    for (int dd = 0; dd < 4; ++dd)
+  for (int dd = 0; dd < 4; ++dd)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        vec4<E> w;
+    for (int rq = 0; rq < 4; ++rq) {
+      vec4<E> w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (E)acc_dv[dd][4 * rq + e];
-        *reinterpret_cast<vec4<E>*>(vp + 32 * dd + 8 * rq) = w;
-      }
+      for (int e = 0; e < 4; ++e) w[e] = (E)acc_dv[dd][4 * rq + e];
+      *reinterpret_cast<vec4<E>*>(vrows + stage_pos(col, 4 * dd + rq) + 8 * hf) = w;
+    }
+  // k rows of the wave's keys, 4 whole rows per load (keys past T read key T - 1)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 4 * j + (lane >> 4), kc = lane & 15;
+    const int ur = min(ua + r, T - 1);
+    *reinterpret_cast<vec8<E>*>(krows + stage_pos(r, kc)) =
+        *reinterpret_cast<const vec8<E>*>(k + ((size_t)ur * Hkv + g) * kHeadDim + 8 * kc);
+  }
+  wave_lds_fence();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 4 * j + (lane >> 4), kc = lane & 15;
+    if (ua + r < T)
+      *reinterpret_cast<vec8<E>*>(dv + ((size_t)(ua + r) * Hkv + g) * kHeadDim + 8 * kc) =
+          *reinterpret_cast<const vec8<E>*>(vrows + stage_pos(r, kc));
   }
   // dk_hat = ln2 * acc (q was scaled by scale*log2e); rotate back; RMSNorm
   // bwd; dy x r per channel into LDS rows [key][channel] for the weight sum
@@ -720,9 +754,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       for (int r = 0; r < 16; ++r) dy[16 * dd + r] = acc_dk[dd][r] * kLn2;
     const int pos = u_real && use_rope ? u - u_start : 0;
     float wsum[64];
-    norm_rope_bwd(dy, k + ((size_t)uc * Hkv + g) * kHeadDim + 4 * hf, knorm_w, u_real, u_ok,
-                  use_rope != 0, pos, s_invf, eps, hf,
-                  dk + ((size_t)uc * Hkv + g) * kHeadDim + 4 * hf, wsum);
+    norm_rope_bwd_staged<E>(dy, krows, col, knorm_w, u_real, use_rope != 0, pos, s_invf, eps,
+                            hf, wsum);
+    wave_lds_fence();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * j + (lane >> 4), kc = lane & 15;
+      if (ua + r < T)
+        *reinterpret_cast<vec8<E>*>(dk + ((size_t)(ua + r) * Hkv + g) * kHeadDim + 8 * kc) =
+            *reinterpret_cast<const vec8<E>*>(krows + stage_pos(r, kc));
+    }
     // the weight gradient sums dy x r over the block's keys in a fixed order,
     // one wave (32 keys) at a time through LDS rows [key][channel]
     static_assert(32 * 129 * 4 <= kColTileBytes, "one wave's rows fit a ring slot");
@@ -947,7 +988,22 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
   agpr_fence();
 
   // ---- epilogue: dq_hat = scale * acc; rotate back; RMSNorm bwd ------------
-  float part = 0.f;
+  // Each wave stages its 32 columns' q rows (then dq in place) in LDS, 8 KiB
+  // per wave in slots 0 and 1 (past the barrier above no copy is in flight
+  // and no wave reads a tile).  Row r of the wave is column r: token
+  // ct tpt + r / G, head g G + r % G.
+  char* qrows = slot(wave >> 2) + (wave & 3) * (32 * 256);
+  const bool ct_in = ct < n_ct;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 4 * j + (lane >> 4), kc = lane & 15;
+    const int tr = ct * tpt + (r >> log2G), hr = g * G + (r & (G - 1));
+    const int trc = ct_in && tr < T ? tr : 0;
+    *reinterpret_cast<vec8<E>*>(qrows + stage_pos(r, kc)) =
+        *reinterpret_cast<const vec8<E>*>(q + ((size_t)trc * Hq + hr) * kHeadDim + 8 * kc);
+  }
+  wave_lds_fence();
+  float wsum[64];
   {
     float dy[64];
 #pragma unroll
@@ -955,28 +1011,56 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) dy[16 * dd + r] = acc[dd][r] * scale;
     const int pos = t_ok && use_rope ? t - t_start : 0;
-    float wsum[64];
-    norm_rope_bwd(dy, q + ((size_t)tcl * Hq + h) * kHeadDim + 4 * hf, qnorm_w, t_ok, t_in,
-                  use_rope != 0, pos, s_invf, eps, hf,
-                  dq + ((size_t)tcl * Hq + h) * kHeadDim + 4 * hf, wsum);
-    // the weight gradient sums dy x r over the block's 256 columns in a fixed
-    // order, one wave (32 columns) at a time through LDS rows
-    static_assert(32 * 129 * 4 <= kKeyTileBytes, "one wave's rows fit a ring slot");
-    float* red = reinterpret_cast<float*>(ring0);
-#pragma unroll
-    for (int round = 0; round < kDqWaves; ++round) {
-      if (wave == round) {
-        float* row = red + col * 129;
-#pragma unroll
-        for (int i = 0; i < 64; ++i) row[32 * (i >> 4) + 8 * ((i >> 2) & 3) + 4 * hf + (i & 3)] = wsum[i];
-      }
-      __syncthreads();
-      if (tid < kHeadDim)
-        for (int cr = 0; cr < 32; ++cr) part += red[cr * 129 + tid];
-      __syncthreads();
-    }
+    norm_rope_bwd_staged<E>(dy, qrows, col, qnorm_w, t_ok, use_rope != 0, pos, s_invf, eps, hf,
+                            wsum);
   }
-  if (tid < kHeadDim) dwq_part[(size_t)blockIdx.x * kHeadDim + tid] = part;
+  wave_lds_fence();
+  // dq rows of every column in the grid (zero for document padding)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r = 4 * j + (lane >> 4), kc = lane & 15;
+    const int tr = ct * tpt + (r >> log2G), hr = g * G + (r & (G - 1));
+    if (ct_in && tr < T)
+      *reinterpret_cast<vec8<E>*>(dq + ((size_t)tr * Hq + hr) * kHeadDim + 8 * kc) =
+          *reinterpret_cast<const vec8<E>*>(qrows + stage_pos(r, kc));
+  }
+  // The weight gradient sums dy x r over the block's 256 columns in a fixed
+  // order: every wave writes its 32 rows of 128 sums (16 KiB per wave, all
+  // four slots; float4 chunk k of row r at position k ^ r), then thread
+  // (quarter, channel c) adds rows 0 .. 31 of waves 2 quarter and
+  // 2 quarter + 1, and the four quarters are added in order.
+  __shared__ float s_quarter[4][kHeadDim];
+  __syncthreads();  // every wave is done with its staged rows
+  {
+    float* wrows = reinterpret_cast<float*>(slot(wave >> 1) + (wave & 1) * (32 * 512));
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        // channels 32dd + 8rq + 4hf .. + 3: float4 chunk 8dd + 2rq + hf
+        const int kc = 8 * dd + 2 * rq + hf;
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = wsum[16 * dd + 4 * rq + e];
+        *reinterpret_cast<f32x4*>(wrows + col * 128 + ((kc ^ col) << 2)) = v;
+      }
+  }
+  __syncthreads();
+  {
+    static_assert(kDqThreads == 4 * kHeadDim, "four quarters of 128 channels");
+    const int c = tid & (kHeadDim - 1), quarter = tid >> 7;
+    float part = 0.f;
+#pragma unroll
+    for (int w = 2 * quarter; w < 2 * quarter + 2; ++w) {
+      const float* wrows = reinterpret_cast<const float*>(slot(w >> 1) + (w & 1) * (32 * 512));
+      for (int cr = 0; cr < 32; ++cr) part += wrows[cr * 128 + ((((c >> 2) ^ cr) << 2) | (c & 3))];
+    }
+    s_quarter[quarter][c] = part;
+  }
+  __syncthreads();
+  if (tid < kHeadDim)
+    dwq_part[(size_t)blockIdx.x * kHeadDim + tid] =
+        ((s_quarter[0][tid] + s_quarter[1][tid]) + s_quarter[2][tid]) + s_quarter[3][tid];
 }
 
 // ============================================================================
