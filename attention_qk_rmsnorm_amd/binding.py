@@ -324,7 +324,8 @@ class BwdCall:
 
     def __init__(self, q, k, v, cu_seqlens, sinks, qnorm_w, knorm_w, window, use_rope, out,
                  lse, dout, *, rms_eps=1e-6, rope_theta=1e6, softmax_scale=None,
-                 workspace=None, stream=None, grads=None, cu_seqlens_padded=None):
+                 workspace=None, stream=None, grads=None, cu_seqlens_padded=None,
+                 tile_config=SINK_ATTN_TILE_AUTO):
         if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
             raise ValueError("q, k, v must be THD tensors [tokens, heads, head_dim]")
         if q.dtype not in (torch.bfloat16, torch.float16):
@@ -349,8 +350,10 @@ class BwdCall:
             _check_tensor(name, t, torch.float32, dev)
         if lse.shape != (Hq, T):
             raise ValueError("lse must be [Hq, T]")
+        # tile_config: narrow / wide force the dQ kernel's small / large
+        # workgroups (automatic by default)
         self.desc = make_desc(T, cu_seqlens.numel() - 1, Hq, Hkv, d, q.dtype, rms_eps,
-                              rope_theta, softmax_scale or 0.0)
+                              rope_theta, softmax_scale or 0.0, tile_config=tile_config)
         need = bwd_workspace_bytes(self.desc)
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)

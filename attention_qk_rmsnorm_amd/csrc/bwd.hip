@@ -786,27 +786,36 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 }
 
 // ============================================================================
-// bwd_dq_kernel: one block per (256-column block, kv head); 8 waves
+// bwd_dq_kernel: one block per (WAVES x 32-column block, kv head).  Two
+// configurations: 8 waves with a ring of 4 key tiles (128 KiB of LDS, one
+// block per CU) for long key walks, and 4 waves with a ring of 2 (64 KiB, two
+// blocks per CU) for short documents, where a block's set-up and epilogue
+// latencies are as long as its key loop and a second block hides them.
 // ============================================================================
-constexpr int kDqWaves = 8;
-constexpr int kDqThreads = kDqWaves * 64;
-constexpr int kKeyBufs = 4;  // ring of key tiles in LDS
-constexpr int kKeyCopyOps = kKeyTileBytes / (16 * kDqThreads);  // copies per wave per tile
-static_assert(kKeyCopyOps * (kKeyBufs - 2) < 64, "vmcnt holds 6 bits");
+template <int WAVES>
+struct DqConfig {
+  static_assert(WAVES == 4 || WAVES == 8, "two configurations");
+  static constexpr int kThreads = WAVES * 64;
+  static constexpr int kBufs = WAVES == 8 ? 4 : 2;  // ring of key tiles in LDS
+  static constexpr int kCopyOps = kKeyTileBytes / (16 * kThreads);  // copies per wave per tile
+  static_assert(kCopyOps * (kBufs - 2) < 64, "vmcnt holds 6 bits");
+};
 
-template <typename E>
-__global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
+template <typename E, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void bwd_dq_kernel(
     const E* __restrict__ q, const char* __restrict__ keys, const char* __restrict__ cols,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_end,
     const float* __restrict__ qnorm_w, int T, int D, int Hq,
     int Hkv, int G, int log2G, int n_kt, int n_ct, int window, int use_rope, float eps,
     double theta, float scale, E* __restrict__ dq, float* __restrict__ dwq_part) {
+  using Cfg = DqConfig<WAVES>;
+  constexpr int kDqWaves = WAVES, kDqThreads = Cfg::kThreads, kKeyBufs = Cfg::kBufs;
+  constexpr int kKeyCopyOps = Cfg::kCopyOps;
   // the ring of key tiles, one array per slot (see the dK/dV kernel)
   __shared__ __attribute__((aligned(1024))) char ring0[kKeyTileBytes];
   __shared__ __attribute__((aligned(1024))) char ring1[kKeyTileBytes];
-  __shared__ __attribute__((aligned(1024))) char ring2[kKeyTileBytes];
-  __shared__ __attribute__((aligned(1024))) char ring3[kKeyTileBytes];
-  static_assert(kKeyBufs == 4, "one array per ring slot");
+  __shared__ __attribute__((aligned(1024))) char ring2[kKeyBufs > 2 ? kKeyTileBytes : 16];
+  __shared__ __attribute__((aligned(1024))) char ring3[kKeyBufs > 2 ? kKeyTileBytes : 16];
   auto slot = [&](int b) -> char* {
     return b == 0 ? ring0 : b == 1 ? ring1 : b == 2 ? ring2 : ring3;
   };
@@ -1024,12 +1033,13 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
       *reinterpret_cast<vec8<E>*>(dq + ((size_t)tr * Hq + hr) * kHeadDim + 8 * kc) =
           *reinterpret_cast<const vec8<E>*>(qrows + stage_pos(r, kc));
   }
-  // The weight gradient sums dy x r over the block's 256 columns in a fixed
-  // order: every wave writes its 32 rows of 128 sums (16 KiB per wave, all
-  // four slots; float4 chunk k of row r at position k ^ r), then thread
-  // (quarter, channel c) adds rows 0 .. 31 of waves 2 quarter and
-  // 2 quarter + 1, and the four quarters are added in order.
-  __shared__ float s_quarter[4][kHeadDim];
+  // The weight gradient sums dy x r over the block's columns in a fixed
+  // order: every wave writes its 32 rows of 128 sums (16 KiB per wave, two
+  // waves per 32 KiB ring slot; float4 chunk k of row r at position k ^ r),
+  // then thread (part, channel c) adds rows 0 .. 31 of waves 2 part and
+  // 2 part + 1, and the WAVES / 2 parts are added in order.
+  constexpr int kParts = kDqWaves / 2;
+  __shared__ float s_quarter[kParts][kHeadDim];
   __syncthreads();  // every wave is done with its staged rows
   {
     float* wrows = reinterpret_cast<float*>(slot(wave >> 1) + (wave & 1) * (32 * 512));
@@ -1047,7 +1057,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
   }
   __syncthreads();
   {
-    static_assert(kDqThreads == 4 * kHeadDim, "four quarters of 128 channels");
+    static_assert(kDqThreads == kParts * kHeadDim, "one part of 128 channels per 2 waves");
     const int c = tid & (kHeadDim - 1), quarter = tid >> 7;
     float part = 0.f;
 #pragma unroll
@@ -1058,9 +1068,12 @@ __global__ __launch_bounds__(kDqThreads, 1) void bwd_dq_kernel(
     s_quarter[quarter][c] = part;
   }
   __syncthreads();
-  if (tid < kHeadDim)
-    dwq_part[(size_t)blockIdx.x * kHeadDim + tid] =
-        ((s_quarter[0][tid] + s_quarter[1][tid]) + s_quarter[2][tid]) + s_quarter[3][tid];
+  if (tid < kHeadDim) {
+    float sum = s_quarter[0][tid];
+#pragma unroll
+    for (int pt = 1; pt < kParts; ++pt) sum += s_quarter[pt][tid];
+    dwq_part[(size_t)blockIdx.x * kHeadDim + tid] = sum;
+  }
 }
 
 // ============================================================================
@@ -1118,7 +1131,9 @@ BwdWorkspace plan_bwd_workspace(int64_t T, int64_t D, int Hq, int Hkv) {
   w.n_kt = (T + kKeyTile - 1) / kKeyTile;
   w.n_ct = (T + tpt - 1) / tpt;
   w.n_kblk = (int64_t)((T + 127) / 128) * Hkv;
-  w.n_qblk = (int64_t)((w.n_ct + kDqWaves - 1) / kDqWaves) * Hkv;
+  // the dQ partial sums are sized for the smaller (4-wave) blocks, which
+  // need more of them; the 8-wave blocks use the first half
+  w.n_qblk = (int64_t)((w.n_ct + 3) / 4) * Hkv;
   size_t off = 0;
   w.keys_off = off;
   off += (size_t)Hkv * w.n_kt * kKeyTileBytes;
@@ -1143,7 +1158,7 @@ hipError_t launch_bwd(const E* q, const E* k, const E* v, const int32_t* cu,
                            E* dk, E* dv, float* dsinks, float* dqnorm_w,
                            float* dknorm_w, int T, int D, int Hq, int Hkv, int window,
                            int use_rope, double eps, double theta, double scale, char* ws,
-                           const BwdWorkspace& w, hipStream_t stream) {
+                           const BwdWorkspace& w, int dq_waves, hipStream_t stream) {
   const int G = Hq / Hkv;
   int log2G = 0;
   while ((1 << log2G) < G) ++log2G;
@@ -1161,11 +1176,17 @@ hipError_t launch_bwd(const E* q, const E* k, const E* v, const int32_t* cu,
   bwd_dkdv_kernel<E><<<dim3((unsigned)w.n_kblk), dim3(kThreads), 0, stream>>>(
       k, keys, cols, cu, cu_end, knorm_w, T, D, Hkv, log2G, (int)w.n_kt, (int)w.n_ct, window, use_rope,
       (float)eps, theta, dk, dv, dwk_part);
-  bwd_dq_kernel<E><<<dim3((unsigned)w.n_qblk), dim3(kDqThreads), 0, stream>>>(
-      q, keys, cols, cu, cu_end, qnorm_w, T, D, Hq, Hkv, G, log2G, (int)w.n_kt, (int)w.n_ct, window,
-      use_rope, (float)eps, theta, (float)scale, dq, dwq_part);
+  const int64_t n_qblk = (w.n_ct + dq_waves - 1) / dq_waves * Hkv;
+  if (dq_waves == 4)
+    bwd_dq_kernel<E, 4><<<dim3((unsigned)n_qblk), dim3(4 * 64), 0, stream>>>(
+        q, keys, cols, cu, cu_end, qnorm_w, T, D, Hq, Hkv, G, log2G, (int)w.n_kt, (int)w.n_ct,
+        window, use_rope, (float)eps, theta, (float)scale, dq, dwq_part);
+  else
+    bwd_dq_kernel<E, 8><<<dim3((unsigned)n_qblk), dim3(8 * 64), 0, stream>>>(
+        q, keys, cols, cu, cu_end, qnorm_w, T, D, Hq, Hkv, G, log2G, (int)w.n_kt, (int)w.n_ct,
+        window, use_rope, (float)eps, theta, (float)scale, dq, dwq_part);
   bwd_reduce_kernel<<<dim3(Hq + 2 * kHeadDim), dim3(kThreads), 0, stream>>>(
-      dsink_part, dwq_part, dwk_part, Hq, G, (int)w.n_ct, (int)w.n_qblk, (int)w.n_kblk,
+      dsink_part, dwq_part, dwk_part, Hq, G, (int)w.n_ct, (int)n_qblk, (int)w.n_kblk,
       dsinks, dqnorm_w, dknorm_w);
   return hipGetLastError();
 }
@@ -1175,7 +1196,7 @@ hipError_t launch_bwd(const E* q, const E* k, const E* v, const int32_t* cu,
       const E*, const E*, const E*, const int32_t*, const int32_t*, const float*,             \
       const float*, const float*, const E*, const float*, const E*, E*, E*, E*, float*,       \
       float*, float*, int, int, int, int, int, int, double, double, double, char*,            \
-      const BwdWorkspace&, hipStream_t);
+      const BwdWorkspace&, int, hipStream_t);
 SA_INSTANTIATE(bf16)
 SA_INSTANTIATE(f16)
 #undef SA_INSTANTIATE

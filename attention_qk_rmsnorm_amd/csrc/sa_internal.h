@@ -77,7 +77,7 @@ struct BwdWorkspace {
   int64_t n_kt = 0;    // 64-key tiles per kv head
   int64_t n_ct = 0;    // 32-column tiles per kv head (32 / G tokens each)
   int64_t n_kblk = 0;  // dK/dV workgroups (128 keys x kv head)
-  int64_t n_qblk = 0;  // dQ workgroups (256 columns x kv head)
+  int64_t n_qblk = 0;  // dQ partial-sum rows: 4-wave workgroups (128 columns x kv head)
   size_t keys_off = 0, cols_off = 0, dsink_off = 0, dwq_off = 0, dwk_off = 0;
   size_t ends_off = 0;  // int32 [D]: real end of every document (padded THD)
   size_t total = 0;
@@ -130,7 +130,7 @@ hipError_t launch_bwd(const E* q, const E* k, const E* v, const int32_t* cu,
                            E* dk, E* dv, float* dsinks, float* dqnorm_w,
                            float* dknorm_w, int T, int D, int Hq, int Hkv, int window,
                            int use_rope, double eps, double theta, double scale, char* ws,
-                           const BwdWorkspace& w, hipStream_t stream);
+                           const BwdWorkspace& w, int dq_waves, hipStream_t stream);
 
 hipError_t launch_prologue_f32(const float* k, const float* v, const int32_t* cu,
                                const int32_t* cu_end, const float* knorm_w, int T, int D, int Hkv, int d,

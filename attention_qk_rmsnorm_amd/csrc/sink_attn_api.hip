@@ -263,12 +263,28 @@ sa::Workspace plan(const sink_attn_desc* d) {
 // CU, shorter blocks) win on short documents and narrow windows.  The
 // automatic choice estimates the keys a query sees: the window, capped by the
 // mean document length, or half that length when causal.
+// Keys per query at and above which the backward's dQ kernel takes 8-wave
+// workgroups (see dq_waves).
+constexpr int64_t kDqWideKeys = 2048;
+
 int select_tile(const sink_attn_desc* d, int32_t window) {
   if (d->tile_config != sa::kTileAuto) return d->tile_config;
   if (d->num_docs <= 0) return sa::kTileNarrow;
   const int64_t mean_len = (int64_t)d->total_tokens / d->num_docs;
   const int64_t keys = window > 0 ? (window < mean_len ? window : mean_len) : mean_len / 2;
   return keys >= 2048 ? sa::kTileWide : sa::kTileNarrow;
+}
+
+// Workgroup size of the backward's dQ kernel: 4 waves (two workgroups per CU)
+// when a query sees few keys, 8 waves (one per CU, a deeper ring of key
+// tiles) otherwise; tile_config narrow / wide force either.
+int dq_waves(const sink_attn_desc* d, int32_t window) {
+  if (d->tile_config == sa::kTileNarrow) return 4;
+  if (d->tile_config != sa::kTileAuto) return 8;
+  if (d->num_docs <= 0) return 4;
+  const int64_t mean_len = (int64_t)d->total_tokens / d->num_docs;
+  const int64_t keys = window > 0 ? (window < mean_len ? window : mean_len) : mean_len / 2;
+  return keys >= kDqWideKeys ? 8 : 4;
 }
 
 double softmax_scale(const sink_attn_desc* d) {
@@ -578,7 +594,7 @@ int bwd_impl(const sink_attn_desc* desc, const void* q, const void* k, const voi
         static_cast<const E*>(dout), static_cast<E*>(dq), static_cast<E*>(dk),
         static_cast<E*>(dv), dsinks, dqnorm_w, dknorm_w, desc->total_tokens, desc->num_docs,
         Hq, desc->num_kv_heads, window, use_rope, desc->rms_eps, desc->rope_theta,
-        softmax_scale(desc), static_cast<char*>(desc->workspace), w, s);
+        softmax_scale(desc), static_cast<char*>(desc->workspace), w, dq_waves(desc, window), s);
   };
   const hipError_t e = desc->dtype == SINK_ATTN_F16 ? run(sa::f16{}) : run(sa::bf16{});
   return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;

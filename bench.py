@@ -395,7 +395,8 @@ def run_bwd(args, A, w, d_inp, call, dev):
     bc = A.BwdCall(d_inp["q"], d_inp["k"], d_inp["v"], d_inp["cu_seqlens"], d_inp["sinks"],
                    d_inp["qnorm_w"], d_inp["knorm_w"], w.window, w.use_rope, call.out, call.lse,
                    dout, rms_eps=w.rms_eps, rope_theta=w.rope_theta,
-                   cu_seqlens_padded=d_inp.get("cu_seqlens_padded"))
+                   cu_seqlens_padded=d_inp.get("cu_seqlens_padded"),
+                   tile_config=TILE_CHOICES[args.tile])
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
         bc.run()

@@ -107,7 +107,11 @@ typedef enum {
  * one workgroup per compute unit, half the LDS operand traffic per matrix
  * instruction; best when every query sees thousands of keys (long causal
  * documents, wide windows).  The fp32 path has a single configuration and
- * ignores the setting. */
+ * ignores the setting.  In the backward, narrow selects dQ workgroups of
+ * 128 query columns (two per compute unit) and wide of 256 (one per compute
+ * unit); automatic takes the former when a query sees fewer than 2,048 keys.
+ * dq, dk, dv and dsinks do not depend on the setting; dqnorm_w is summed
+ * over the dQ workgroups, so its rounding does. */
 typedef enum {
   SINK_ATTN_TILE_AUTO = 0,
   SINK_ATTN_TILE_NARROW = 1,

@@ -136,7 +136,11 @@ def gpu_backward(inp_dev: dict, window: int, use_rope: bool, dout=None, seed=0,
         w = workloads.Workload("g", (T,), Hq, inp_dev["k"].shape[1], d,
                                dtype_name(inp_dev["q"].dtype))
         dout = workloads.make_grad_output(w, seed).to(inp_dev["q"].device)
+    # bwd_tile_config goes to the backward only (the forward keeps its own choice)
+    bwd_tile = kw.pop("bwd_tile_config", None)
     fkw = {k: v for k, v in kw.items() if k in ("rms_eps", "rope_theta", "softmax_scale")}
+    if bwd_tile is not None:
+        fkw["tile_config"] = bwd_tile
     out, lse = A.sink_attn_fwd(inp_dev["q"], inp_dev["k"], inp_dev["v"], inp_dev["cu_seqlens"],
                                inp_dev["sinks"], inp_dev["qnorm_w"], inp_dev["knorm_w"],
                                window, use_rope, **kw)

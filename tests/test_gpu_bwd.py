@@ -156,6 +156,27 @@ def test_determinism_and_empty_batch():
         assert torch.all(grads[key] == 0), key
 
 
+def test_dq_workgroup_sizes_agree():
+    # the dQ kernel's two workgroup sizes (forced through tile_config): every
+    # wave walks the same key tiles in the same order, so dq is bitwise equal;
+    # dqnorm_w is summed over other workgroups, so only its rounding differs
+    _say("case bwd dQ workgroups 128 vs 256 columns")
+    import attention_qk_rmsnorm_amd as A
+    inp = to_device(custom_inputs([333, 1, 900, 64, 1500], seed=4))
+    res = {}
+    for tile in (A.SINK_ATTN_TILE_NARROW, A.SINK_ATTN_TILE_WIDE):
+        res[tile] = gpu_backward(inp, 300, True, bwd_tile_config=tile)
+    a, b = res[A.SINK_ATTN_TILE_NARROW], res[A.SINK_ATTN_TILE_WIDE]
+    for key in ("dq", "dk", "dv", "dsinks", "dknorm_w"):
+        assert torch.equal(a[key], b[key]), key
+    d = (a["dqnorm_w"] - b["dqnorm_w"]).abs().max().item()
+    assert d <= 1e-5 * b["dqnorm_w"].abs().max().item(), d
+    check_bwd_parity(custom_inputs([333, 1, 900, 64, 1500], seed=4), 300, True,
+                     label="dQ 128 columns", bwd_tile_config=A.SINK_ATTN_TILE_NARROW)
+    check_bwd_parity(custom_inputs([333, 1, 900, 64, 1500], seed=4), 300, True,
+                     label="dQ 256 columns", bwd_tile_config=A.SINK_ATTN_TILE_WIDE)
+
+
 def test_sliding_layer_scale():
     # two documents of 2500 and 3500 tokens with the sliding layers' 1024-key
     # window and RoPE: many key blocks and column tiles per document
