@@ -25,10 +25,10 @@
 //                      dout^T P, dK^T += q^T dS (AGPR accumulators, the
 //                      transposed operands by LDS transpose reads); epilogue:
 //                      dv, and dk through the rotation and norm backward
-//   bwd_dq_kernel      per 256-column block (8 waves of 32 columns): walks the
-//                      key tiles the columns see; S^T = K q^T, P^T, dP^T - D,
-//                      dS^T; dq^T += K^T dS^T; epilogue: dq through the
-//                      rotation and norm backward
+//   bwd_dq_kernel      per 256- or 128-column block (8 or 4 waves of 32
+//                      columns): walks the key tiles the columns see;
+//                      S^T = K q^T, P^T, dP^T - D, dS^T; dq^T += K^T dS^T;
+//                      epilogue: dq through the rotation and norm backward
 //   bwd_reduce_kernel  dsinks and both norm-weight gradients from per-tile and
 //                      per-block partial sums, in a fixed order
 // MFMA operand layouts (32x32x16, wave64): A lane l holds A[l%32][8(l/32)..+7],
