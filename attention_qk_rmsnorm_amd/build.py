@@ -29,6 +29,10 @@ HIPCC_FLAGS = [
     # accumulators in VGPRs for the softmax and its O accumulators in AGPRs
     # through inline asm (code of the other kernels is unchanged by this)
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    # loops marked for full unrolling stay fully unrolled even when their
+    # bodies are large: the backward's dK/dV loop is unrolled over its 8 ring
+    # slots, and left rolled it would index its score registers at run time
+    "-mllvm", "-pragma-unroll-threshold=65536",
 ]
 
 

@@ -19,7 +19,11 @@ correctness rest on, checked on the CPU from hipcc's assembly output:
   states of an MFMA writing it (the compiler cannot see that inline-asm MFMAs
   wrote the accumulators it copies; a missed case returned stale values for
   the last accumulator rows of the dK/dV tail);
-* the backward's tile loops wait for copies only right before their barrier.
+* the backward's tile loops wait for copies only right before their barrier;
+* no kernel moves registers by run-time index (s_set_gpr_idx / v_movrel): a
+  loop the compiler declines to unroll fully indexes its register arrays
+  that way, as the dK/dV loop over its 8 ring slots did past the default
+  unrolling threshold.
 """
 import os
 import re
@@ -278,3 +282,10 @@ def test_backward_loops_wait_for_copies_only_at_barriers(asm):
                     assert nxt - k <= 8, (marker, code[k], code[k + 1:k + 4])
             checked += 1
         assert checked >= minimum, (marker[:60], checked)
+
+
+def test_no_indexed_register_moves(asm):
+    for name, text in asm.items():
+        for kname, body in _kernels(text):
+            hits = re.findall(r"^\s*(s_set_gpr_idx_on|v_movrel\w*)", body, flags=re.M)
+            assert not hits, (name, kname[:70], len(hits))
