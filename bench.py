@@ -497,8 +497,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the library runs on one GPU and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
     import torch
