@@ -308,8 +308,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
   // ---- Q: load, RMSNorm, RoPE, round to E B operands -----------------------
   // lane holds channels 16kk + 8hf + e (kk < 8, e < 8) of its column; NeoX
   // partners i and i + 64 (kk and kk + 4) sit in the same lane.  The global
-  // loads go out before the first tile's copy: vmcnt retires in order, so
-  // waiting for them then does not wait for the copy.
+  // loads go out before the first tile's copy; the compiler's wait before the
+  // prologue covers that copy as well (with a copy into LDS in flight it
+  // waits for the vector memory counter to reach zero).
   {
     vec8<E> qraw[8];
     float w[64];

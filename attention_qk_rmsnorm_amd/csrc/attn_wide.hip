@@ -446,8 +446,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_wide_kernel(
   // ---- Q: load, RMSNorm, RoPE, scale, round to E B operands ---------------
   // lane holds channels 16kk + 8hf + e (kk < 8, e < 8) of its columns; NeoX
   // partners i and i + 64 (kk and kk + 4) sit in the same lane.  The global
-  // loads go out before the first tiles' copies: vmcnt retires in order, so
-  // waiting for them then does not wait for the copies.
+  // loads go out before the first tiles' copies; the compiler's wait before
+  // the prologue covers those copies as well (with a copy into LDS in flight
+  // it waits for the vector memory counter to reach zero).
   {
     vec8<E> qraw[2][8], kself[2][8];
 #pragma unroll
