@@ -282,6 +282,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
 
   __shared__ double s_invf[64];
   __shared__ __attribute__((aligned(1024))) char lds[2 * kBuf];
+  __shared__ __attribute__((aligned(16))) char s_rope[16 * kRopeRow];
 
   // ---- key range of the block: [lo, hi), visited in 64-aligned tiles ------
   const int hi = a_end;
@@ -295,10 +296,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
   // the compiler prove the next tile's LDS copy does not alias the buffer
   // being read, so it does not wait for that copy before the reads
   const int wave_u = __builtin_amdgcn_readfirstlane(wave) & (kWaves - 1);
-  // RoPE angles: a table of the block's tokens in the second tile buffer
-  // (unused until the key loop's first barrier) when it fits, i.e. for G >= 4;
+  // RoPE angles: a table of the block's tokens when it fits (G >= 8);
   // otherwise each lane computes its own from the frequencies in s_invf
-  const bool rope_tab = use_rope && m_tok * kRopeRow <= kBuf;
+  const bool rope_tab = use_rope && m_tok * kRopeRow <= (int)sizeof(s_rope);
   if (use_rope && !rope_tab) {
     if (tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
     __syncthreads();
@@ -307,29 +307,52 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
   ColState<E> st;
   // ---- Q: load, RMSNorm, RoPE, round to E B operands -----------------------
   // lane holds channels 16kk + 8hf + e (kk < 8, e < 8) of its column; NeoX
-  // partners i and i + 64 (kk and kk + 4) sit in the same lane.  The global
-  // loads go out before the first tile's copy; the compiler's wait before the
-  // prologue covers that copy as well (with a copy into LDS in flight it
-  // waits for the vector memory counter to reach zero).
+  // partners i and i + 64 (kk and kk + 4) sit in the same lane.  The wave's 32
+  // rows are loaded four whole rows per instruction (row 4j + lane/16, chunk
+  // lane % 16) and handed to the lanes that hold them through the second tile
+  // buffer (not used before the key loop's first barrier; row r at r * 256,
+  // chunk k at position k ^ (r % 16)) -- one load per lane and row quarter
+  // instead of 32-byte pieces of 32 rows per instruction.  The global loads go
+  // out before the first tile's copy; the compiler's wait before the staging
+  // covers that copy as well (with a copy into LDS in flight it waits for the
+  // vector memory counter to reach zero).
   {
-    vec8<E> qraw[8];
+    vec8<E> qrow[8];
     float w[64];
-    const E* qp = q + ((size_t)(tok_ok ? tok : a) * Hq + hq) * kHeadDim + 8 * hf;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      qraw[kk] = *reinterpret_cast<const vec8<E>*>(qp + 16 * kk);
+    for (int j = 0; j < 8; ++j) {
+      // column r of the wave: token tw0 + r / G, head g G + r % G; a column
+      // past the block's tokens loads the first token's row (its norm factor
+      // is zero below)
+      const int r = 4 * j + (lane >> 4);
+      const int tr = tw0 + (r >> log2G);
+      const E* rp = q + ((size_t)(tr < a_end ? tr : a) * Hq + g * G + (r & (G - 1))) * kHeadDim;
+      qrow[j] = *reinterpret_cast<const vec8<E>*>(rp + 8 * (lane & 15));
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) w[8 * kk + e] = qnorm_w[16 * kk + 8 * hf + e];
-    }
     __builtin_amdgcn_sched_barrier(0);
     // the first tile's copy overlaps the Q prologue
     if (kt_lo < hi)
       issue_tile(kimg + (size_t)kt_lo * 256, vimg + (size_t)kt_lo * 256, tid, wave_u, lds);
     __builtin_amdgcn_sched_barrier(0);
     if (rope_tab) {
-      rope_table(lds + kBuf, tid, kThreads, m_tok, a, a_end, doc_start, theta);
+      rope_table(s_rope, tid, kThreads, m_tok, a, a_end, doc_start, theta);
       barrier_keep_copies();
     }
+    char* stg = lds + kBuf + wave * (32 * 256);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = 4 * j + (lane >> 4);
+      *reinterpret_cast<vec8<E>*>(stg + r * 256 + (((lane & 15) ^ (r & 15)) << 4)) = qrow[j];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    vec8<E> qraw[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      qraw[kk] = *reinterpret_cast<const vec8<E>*>(stg + col * 256 + (((2 * kk + hf) ^ (col & 15)) << 4));
 
     float x[64];
 #pragma unroll
@@ -348,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
     for (int i = 0; i < 64; ++i) x[i] *= inv * w[i];
     if (use_rope && tok_ok) {
       if (rope_tab) {
-        rope_from_table(lds + kBuf + (tok - a) * kRopeRow, hf, x);
+        rope_from_table(s_rope + (tok - a) * kRopeRow, hf, x);
       } else {
         const int p = tok - doc_start;
 #pragma unroll
