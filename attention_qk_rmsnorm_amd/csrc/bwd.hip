@@ -889,11 +889,41 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void bwd_dq_kernel(
   {
     const int ctc = min(ct, n_ct - 1);
     const char* cimg = cols + ((size_t)g * n_ct + ctc) * kColTileBytes;
+    if constexpr (WAVES == 4) {
+      // Both row images of the wave's column tile are read as whole 1 KiB
+      // runs (image rows 4j .. 4j + 3 per load) and handed to the lanes that
+      // hold each row's operand pieces through this wave's 8 KiB of ring slot
+      // 1, which no copy fills before the key loop's first barrier: first
+      // the q image, then, in place, the dout image (the q operand
+      // reads are complete before the dout rows overwrite them).  Short blocks
+      // spend a good part of their life here.
+      vec8<E> qi[8], di[8];
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const int off = col * 256 + (((2 * kk + hf) ^ bswz(col)) << 4);
-      qB[kk] = rd<E>(cimg + off);
-      dB[kk] = rd<E>(cimg + kCT + off);
+      for (int j = 0; j < 8; ++j) {
+        qi[j] = rd<E>(cimg + 1024 * j + 16 * lane);
+        di[j] = rd<E>(cimg + kCT + 1024 * j + 16 * lane);
+      }
+      char* stg = ring1 + wave * 8192;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) *reinterpret_cast<vec8<E>*>(stg + 1024 * j + 16 * lane) = qi[j];
+      wave_lds_fence();
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        qB[kk] = *reinterpret_cast<const vec8<E>*>(stg + col * 256 + (((2 * kk + hf) ^ bswz(col)) << 4));
+      wave_lds_fence();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) *reinterpret_cast<vec8<E>*>(stg + 1024 * j + 16 * lane) = di[j];
+      wave_lds_fence();
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        dB[kk] = *reinterpret_cast<const vec8<E>*>(stg + col * 256 + (((2 * kk + hf) ^ bswz(col)) << 4));
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const int off = col * 256 + (((2 * kk + hf) ^ bswz(col)) << 4);
+        qB[kk] = rd<E>(cimg + off);
+        dB[kk] = rd<E>(cimg + kCT + off);
+      }
     }
     if (t_ok) {
       nlse = reinterpret_cast<const float*>(cimg + kColLd)[col];
