@@ -495,7 +495,35 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
 
   // K and V rows of this lane's key as B operands (channels 16kk + 8hf ..)
   vec8<E> kB[8], vB[8];
-  {
+  if (ua + 31 < T) {
+    // (every key of the wave is below T, wave-uniform) the wave's 32 rows of
+    // both images are 8 KiB runs: read as whole 1 KiB pieces (rows 4j ..
+    // 4j + 3 per load) and handed to the lanes that hold each row's operand
+    // pieces through ring slot `wave`, which the tile copies fill only after
+    // the barrier below
+    const char* kimg = keys + ((size_t)g * n_kt + (ua >> 6)) * kKeyTileBytes + (ua & 63) * 256;
+    vec8<E> ki[8], vi[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ki[j] = rd<E>(kimg + 1024 * j + 16 * lane);
+      vi[j] = rd<E>(kimg + kKT + 1024 * j + 16 * lane);
+    }
+    // row r of the staged runs is key ua + r; its chunk positions follow the
+    // image's swizzle of row (ua & 63) + r, and ua & 63 is 0 or 32
+    char* stg = slot(wave);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      *reinterpret_cast<vec8<E>*>(stg + 1024 * j + 16 * lane) = ki[j];
+      *reinterpret_cast<vec8<E>*>(stg + 8192 + 1024 * j + 16 * lane) = vi[j];
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const int pos = ((2 * kk + hf) ^ bswz(col)) << 4;
+      kB[kk] = *reinterpret_cast<const vec8<E>*>(stg + col * 256 + pos);
+      vB[kk] = *reinterpret_cast<const vec8<E>*>(stg + 8192 + col * 256 + pos);
+    }
+  } else {
     const char* kimg = keys + ((size_t)g * n_kt + (uc >> 6)) * kKeyTileBytes;
     const int r = uc & 63;
 #pragma unroll
@@ -504,10 +532,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(
       kB[kk] = rd<E>(kimg + r * 256 + pos);
       vB[kk] = rd<E>(kimg + kKT + r * 256 + pos);
     }
-    // land them before the tile copies start (a later wait would drain those)
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) asm volatile("" ::"v"(kB[kk]), "v"(vB[kk]));
   }
+  // land them before the tile copies start (a later wait would drain those),
+  // and let every wave finish reading its staged rows before the copies
+  // overwrite the slots
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) asm volatile("" ::"v"(kB[kk]), "v"(vB[kk]));
+  __syncthreads();
   f32x16 acc_dv[4], acc_dk[4];
   {
     vec8<E> zero;
