@@ -38,7 +38,7 @@ from _harness import (BF16_MAX, BF16_MEAN, check_bwd_parity, check_parity, custo
 BOUNDARY_LENGTHS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129,
                     255, 256, 257, 511, 512, 513]
 WINDOWS = [1, 2, 63, 64, 65, 512, 513, 1024, -1]
-HEADS = [(32, 4), (32, 4), (32, 4), (16, 2), (8, 8), (32, 1), (4, 2)]
+HEADS = [(32, 4), (32, 4), (32, 4), (16, 2), (8, 8), (32, 1), (4, 2), (16, 4), (16, 1)]
 TILES = [0, 1, 2]  # automatic, narrow, wide
 N_FWD, N_BWD = 96, 24  # cases per run (seeds OFFSET .. OFFSET + N - 1)
 N_FP16, N_PADDED = 16, 16
