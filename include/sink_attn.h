@@ -199,9 +199,10 @@ int sink_attn_attention(const sink_attn_desc* desc, const void* q,
  * path, or a negative status for an invalid descriptor or window == 0.
  * Not on the pages: a choice between two kernels of this library that
  * compute the same function.  The
- * automatic choice takes the wide tiles when the window (capped by the mean
- * document length T / D), or half the mean length when causal, is at least
- * 2048 keys.  Reads no device memory. */
+ * automatic choice takes the wide tiles when a query sees at least 1,024
+ * keys on average, estimated from the mean document length L = T / D: L / 2
+ * when causal or when the window is at least L, W - W^2 / 2L for a window
+ * W < L.  Reads no device memory. */
 int sink_attn_tile_config(const sink_attn_desc* desc, int32_t window);
 
 /* Padded THD.  Defined by "flint.layers" FlintAttention.forward

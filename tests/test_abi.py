@@ -190,9 +190,11 @@ def test_empty_batch_is_a_no_op(A):
     (131072, 2, 4096, 2),   # long documents, 4096-key window: wide
     (12450, 8, 1024, 1),    # 1024-key window: narrow
     (111378, 512, -1, 1),   # short documents: narrow
-    (8192, 1, 1024, 1),     # long document, narrow window: narrow
-    (8192, 2, -1, 2),       # two 4096-token causal documents: wide (2048 keys)
-    (8190, 2, -1, 1),       # just under: narrow
+    (8192, 1, 1024, 1),     # long document, 1024-key window: 960 keys, narrow
+    (32768, 1, 1536, 2),    # long document, 1536-key window: 1500 keys, wide
+    (4096, 2, -1, 2),       # two 2048-token causal documents: wide (1024 keys)
+    (4094, 2, -1, 1),       # just under: narrow
+    (1024, 1, 2048, 1),     # window past the document: causal estimate (512 keys)
 ])
 def test_automatic_tile_choice(A, T, D, window, expected):
     assert A.sink_attn_tile_config(T, D, 32, 4, 128, window) == expected
