@@ -261,40 +261,51 @@ sa::Workspace plan(const sink_attn_desc* d) {
 // workgroup per CU, half the LDS operand traffic per MFMA) win once a query
 // block visits many key tiles; narrow ones (32 columns, two workgroups per
 // CU, shorter blocks) win on short documents and narrow windows.  The
-// automatic choice estimates the keys a query sees: the window, capped by the
-// mean document length, or half that length when causal.
-// Keys per query at and above which the backward's dQ kernel takes 8-wave
-// workgroups (see dq_waves).
-constexpr int64_t kDqWideKeys = 2048;
-// Mean keys per query (the estimate in select_tile) from which the automatic
-// choice takes the wide attention tiles.  Both configurations timed on one
-// box over causal documents of 1,024 to 32,768 tokens and windows of 1,024 to
-// 3,072 keys: wide 3-16 % faster from 1,024 keys on; from ~700 to 1,024
-// either one by up to 5 %; narrow up to 8 % faster at 512.
+// automatic choice estimates the mean number of keys a query sees from the
+// mean document length L = T / D (the host does not read cu_seqlens): L / 2
+// when causal or when the window reaches past L, W - W^2 / 2L for a window
+// W < L (the first W tokens of a document see fewer than W keys).
+int64_t mean_keys(const sink_attn_desc* d, int32_t window) {
+  const int64_t mean_len = (int64_t)d->total_tokens / d->num_docs;
+  const int64_t w = window;
+  return w > 0 && w < mean_len ? w - w * w / (2 * mean_len) : mean_len / 2;
+}
+// Mean keys per query from which the automatic choice takes the wide
+// attention tiles.  Both configurations timed on one box over causal
+// documents of 1,024 to 32,768 tokens and windows of 1,024 to 3,072 keys:
+// wide 3-16 % faster from 1,024 keys on; from ~700 to 1,024 either one by up
+// to 5 %; narrow up to 8 % faster at 512.
 constexpr int64_t kWideKeys = 1024;
+// The backward's dQ kernel takes 8-wave workgroups (one per CU, a 4-slot key
+// ring) from kDqWideKeys mean keys per query, or from kDqMidKeys when the
+// 8-wave grid still has kDqMinBlocks workgroups (eight rounds of the CUs);
+// 4-wave ones (two per CU, a 2-slot ring) otherwise.  Timed on one box: 8
+// waves 1-7 % faster on 23,417- and 32,768-token batches from 512 mean keys
+// on and on one 8,192-token causal document; 4 waves 2-7 % faster on the
+// 12,450-token Sliding batch (687 keys) and on 512 short documents (108).
+constexpr int64_t kDqWideKeys = 2048;
+constexpr int64_t kDqMidKeys = 512;
+constexpr int64_t kDqMinBlocks = 2048;
 
 int select_tile(const sink_attn_desc* d, int32_t window) {
   if (d->tile_config != sa::kTileAuto) return d->tile_config;
   if (d->num_docs <= 0) return sa::kTileNarrow;
-  // the mean number of keys a query sees, for documents of the mean length L:
-  // L / 2 when causal (or when the window covers whole documents); with a
-  // window W < L, W - W^2 / 2L (the first W tokens of a document see fewer)
-  const int64_t mean_len = (int64_t)d->total_tokens / d->num_docs;
-  const int64_t w = window;
-  const int64_t keys = w > 0 && w < mean_len ? w - w * w / (2 * mean_len) : mean_len / 2;
-  return keys >= kWideKeys ? sa::kTileWide : sa::kTileNarrow;
+  return mean_keys(d, window) >= kWideKeys ? sa::kTileWide : sa::kTileNarrow;
 }
 
-// Workgroup size of the backward's dQ kernel: 4 waves (two workgroups per CU)
-// when a query sees few keys, 8 waves (one per CU, a deeper ring of key
-// tiles) otherwise; tile_config narrow / wide force either.
-int dq_waves(const sink_attn_desc* d, int32_t window) {
+// Workgroup size of the backward's dQ kernel (4 or 8 waves, see above);
+// tile_config narrow / wide force either.  In a padded batch T counts the
+// padding, so only the first rule applies there (the 12,450 real tokens of
+// the Sliding lengths in 8 slots of 4,096: 4 waves 3 % faster).
+int dq_waves(const sink_attn_desc* d, int32_t window, bool padded) {
   if (d->tile_config == sa::kTileNarrow) return 4;
   if (d->tile_config != sa::kTileAuto) return 8;
   if (d->num_docs <= 0) return 4;
-  const int64_t mean_len = (int64_t)d->total_tokens / d->num_docs;
-  const int64_t keys = window > 0 ? (window < mean_len ? window : mean_len) : mean_len / 2;
-  return keys >= kDqWideKeys ? 8 : 4;
+  const int64_t keys = mean_keys(d, window);
+  // workgroups of the 8-wave grid: 256 query columns each
+  const int64_t blocks = (int64_t)d->total_tokens * d->num_q_heads / 256;
+  if (keys >= kDqWideKeys) return 8;
+  return !padded && keys >= kDqMidKeys && blocks >= kDqMinBlocks ? 8 : 4;
 }
 
 double softmax_scale(const sink_attn_desc* d) {
@@ -604,7 +615,8 @@ int bwd_impl(const sink_attn_desc* desc, const void* q, const void* k, const voi
         static_cast<const E*>(dout), static_cast<E*>(dq), static_cast<E*>(dk),
         static_cast<E*>(dv), dsinks, dqnorm_w, dknorm_w, desc->total_tokens, desc->num_docs,
         Hq, desc->num_kv_heads, window, use_rope, desc->rms_eps, desc->rope_theta,
-        softmax_scale(desc), static_cast<char*>(desc->workspace), w, dq_waves(desc, window), s);
+        softmax_scale(desc), static_cast<char*>(desc->workspace), w,
+        dq_waves(desc, window, cu_padded != nullptr), s);
   };
   const hipError_t e = desc->dtype == SINK_ATTN_F16 ? run(sa::f16{}) : run(sa::bf16{});
   return e == hipSuccess ? SINK_ATTN_OK : SINK_ATTN_ELAUNCH;

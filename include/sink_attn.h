@@ -109,9 +109,11 @@ typedef enum {
  * documents, wide windows).  The fp32 path has a single configuration and
  * ignores the setting.  In the backward, narrow selects dQ workgroups of
  * 128 query columns (two per compute unit) and wide of 256 (one per compute
- * unit); automatic takes the former when a query sees fewer than 2,048 keys.
- * dq, dk, dv and dsinks do not depend on the setting; dqnorm_w is summed
- * over the dQ workgroups, so its rounding does. */
+ * unit); automatic takes the latter when a query sees at least 2,048 keys on
+ * average, or at least 512 in an unpadded batch of T * num_q_heads >= 524,288
+ * (the estimate of sink_attn_tile_config).  dq, dk, dv and dsinks do not
+ * depend on the setting; dqnorm_w is summed over the dQ workgroups, so its
+ * rounding does. */
 typedef enum {
   SINK_ATTN_TILE_AUTO = 0,
   SINK_ATTN_TILE_NARROW = 1,
