@@ -241,13 +241,19 @@ __device__ __forceinline__ void attend_tile(const char* lds, const int (&koff)[8
   }
 }
 
-template <typename E>
+// RoPE of the queries: none, from an LDS table of the block's tokens (G >= 8,
+// where a token's G heads share its angles), or per lane.  A template
+// argument rather than a run-time flag, so that the code without RoPE has no
+// branches around the rotation and no register copies where they rejoin.
+enum RopeMode { kRopeNone = 0, kRopeTable = 1, kRopeLane = 2 };
+
+template <typename E, int RM>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
     const E* __restrict__ q, const E* __restrict__ khat,
     const E* __restrict__ vt, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ cu_end, const int32_t* __restrict__ sched, const float* __restrict__ sinks,
     const float* __restrict__ qnorm_w, E* __restrict__ out, float* __restrict__ lse,
-    int T, int Hq, int Hkv, int G, int log2G, int64_t t_pad, int window, int use_rope,
+    int T, int Hq, int Hkv, int G, int log2G, int64_t t_pad, int window,
     float eps, double theta, float c_log2, int xcd_per) {
   // ---- work item: blocks of one kv head stay on one group of XCDs --------
   const int bid = blockIdx.x;
@@ -296,10 +302,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
   // the compiler prove the next tile's LDS copy does not alias the buffer
   // being read, so it does not wait for that copy before the reads
   const int wave_u = __builtin_amdgcn_readfirstlane(wave) & (kWaves - 1);
-  // RoPE angles: a table of the block's tokens when it fits (G >= 8);
-  // otherwise each lane computes its own from the frequencies in s_invf
-  const bool rope_tab = use_rope && m_tok * kRopeRow <= (int)sizeof(s_rope);
-  if (use_rope && !rope_tab) {
+  // RoPE angles: a table of the block's tokens (kRopeTable, G >= 8, so the
+  // block's 128 / G tokens fit the table), or per lane from the frequencies
+  // in s_invf (kRopeLane)
+  if constexpr (RM == kRopeLane) {
     if (tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
     __syncthreads();
   }
@@ -308,27 +314,55 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
   // ---- Q: load, RMSNorm, RoPE, round to E B operands -----------------------
   // lane holds channels 16kk + 8hf + e (kk < 8, e < 8) of its column; NeoX
   // partners i and i + 64 (kk and kk + 4) sit in the same lane.  The wave's 32
-  // rows are loaded four whole rows per instruction (row 4j + lane/16, chunk
-  // lane % 16) and handed to the lanes that hold them through the second tile
-  // buffer (not used before the key loop's first barrier; row r at r * 256,
-  // chunk k at position k ^ (r % 16)) -- one load per lane and row quarter
-  // instead of 32-byte pieces of 32 rows per instruction.  The global loads go
-  // out before the first tile's copy; the compiler's wait before the staging
-  // covers that copy as well (with a copy into LDS in flight it waits for the
-  // vector memory counter to reach zero).
+  // rows are copied global -> LDS by global_load_lds_dwordx4 into the second
+  // tile buffer (not used before the key loop's first barrier), four whole
+  // rows per instruction, and each lane then reads the pieces of its own
+  // column from there.  Instruction j fills rows 4j .. 4j + 3 (1 KiB) and lane
+  // l writes its 16 bytes at byte 16 l of that, i.e. row r = 4j + l / 16 at
+  // position l % 16; lane l therefore fetches chunk (l % 16) ^ (r % 16) of
+  // row r, so that chunk k of row r sits at position k ^ (r % 16).  Rows are
+  // addressed by 32-bit offsets from the block's first (token, head) row.
+  // The copies go out before the first tile's copy, and the wait before the
+  // reads covers both.
+  char* stg = lds + kBuf + wave_u * (32 * 256);
+  // Column r of the wave is (token tw0 + r / G, head g G + r % G); its row
+  // sits r * 256 + (r / G) * (Hq - G) * 256 bytes past the wave's first row.
+  // A column past the block's tokens reads the wave's first row instead (its
+  // norm factor is zero below), or, in a wave without tokens, the block's.
+  // (both wave-uniform; readfirstlane makes them scalars for the compiler)
+  const int tpw_live = __builtin_amdgcn_readfirstlane(tw1 - tw0);  // tokens of this wave (may be <= 0)
+  const int t_base = __builtin_amdgcn_readfirstlane(tpw_live > 0 ? tw0 : a);
+  const uint32_t gap = (uint32_t)(Hq - G) * (kHeadDim * (uint32_t)sizeof(E));
   {
-    vec8<E> qrow[8];
-    float w[64];
+    const char* qwave = reinterpret_cast<const char*>(q + ((size_t)t_base * Hq + g * G) * kHeadDim);
+    // with G >= 4 the token r / G = (4j + lane/16) / G = 4j / G of row group j
+    // is the same for the whole wave (G is a power of two), so the row offset
+    // is a per-lane constant plus a uniform term and the bounds test is uniform
+    const uint32_t lane_off = ((uint32_t)(lane >> 4) << 8) | ((uint32_t)((lane & 15) ^ (lane >> 4)) << 4);
+    if (G >= 4) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      // column r of the wave: token tw0 + r / G, head g G + r % G; a column
-      // past the block's tokens loads the first token's row (its norm factor
-      // is zero below)
-      const int r = 4 * j + (lane >> 4);
-      const int tr = tw0 + (r >> log2G);
-      const E* rp = q + ((size_t)(tr < a_end ? tr : a) * Hq + g * G + (r & (G - 1))) * kHeadDim;
-      qrow[j] = *reinterpret_cast<const vec8<E>*>(rp + 8 * (lane & 15));
+      for (int j = 0; j < 8; ++j) {
+        // row 4j + lane/16, chunk position (lane%16) ^ (r%16) with
+        // r%16 = 4(j%4) + lane/16; a row past the tokens reads row 0
+        const int tq = (4 * j) >> log2G;
+        const uint32_t off = tq < tpw_live
+                                 ? (uint32_t)(1024 * j) + (uint32_t)tq * gap + (lane_off ^ ((j & 3) << 6))
+                                 : (lane_off & 0xF0u) ^ ((uint32_t)(j & 3) << 6);
+        __builtin_amdgcn_global_load_lds(qwave + off, (lds_void*)(stg + 1024 * j), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 4 * j + (lane >> 4);
+        const int tq = r >> log2G;
+        uint32_t off = tq < tpw_live ? (uint32_t)r * 256 + (uint32_t)tq * gap : 0u;
+        off += (uint32_t)((lane & 15) ^ (r & 15)) << 4;
+        __builtin_amdgcn_global_load_lds(qwave + off, (lds_void*)(stg + 1024 * j), 16, 0, 0);
+      }
     }
+  }
+  {
+    float w[64];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
@@ -338,17 +372,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
     if (kt_lo < hi)
       issue_tile(kimg + (size_t)kt_lo * 256, vimg + (size_t)kt_lo * 256, tid, wave_u, lds);
     __builtin_amdgcn_sched_barrier(0);
-    if (rope_tab) {
+    if constexpr (RM == kRopeTable) {
       rope_table(s_rope, tid, kThreads, m_tok, a, a_end, doc_start, theta);
       barrier_keep_copies();
     }
-    char* stg = lds + kBuf + wave * (32 * 256);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = 4 * j + (lane >> 4);
-      *reinterpret_cast<vec8<E>*>(stg + r * 256 + (((lane & 15) ^ (r & 15)) << 4)) = qrow[j];
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the q rows (and the first tile) landed
     vec8<E> qraw[8];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
@@ -369,10 +397,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
     const float inv = tok_ok ? c_log2 / sqrtf(ss * (1.0f / kHeadDim) + eps) : 0.f;
 #pragma unroll
     for (int i = 0; i < 64; ++i) x[i] *= inv * w[i];
-    if (use_rope && tok_ok) {
-      if (rope_tab) {
-        rope_from_table(s_rope + (tok - a) * kRopeRow, hf, x);
-      } else {
+    if constexpr (RM == kRopeTable) {
+      if (tok_ok) rope_from_table(s_rope + (tok - a) * kRopeRow, hf, x);
+    } else if constexpr (RM == kRopeLane) {
+      if (tok_ok) {
         const int p = tok - doc_start;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
@@ -403,10 +431,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
     for (int e = 0; e < 8; ++e) st.ones_a[e] = (E)0.f;
     if (hf == 0) st.ones_a[0] = (E)1.f;
   }
+  // O^T starts at zero: four MFMAs of zero operands on the otherwise idle
+  // matrix cores, instead of 64 VALU moves; the fence keeps them after the Q
+  // prologue, whose 128 live floats per lane leave no room for O
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    f32x16 zc;
 #pragma unroll
-  for (int dd = 0; dd < 4; ++dd)
+    for (int r = 0; r < 16; ++r) zc[r] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st.o[dd][r] = 0.f;
+    for (int dd = 0; dd < 4; ++dd) {
+      vec8<E> z;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) z[e] = (E)0.f;
+      // an opaque copy per product, so the compiler keeps four MFMAs rather
+      // than one and 48 register copies of its result
+      asm volatile("" : "+v"(z));
+      st.o[dd] = mfma32(z, z, zc);
+    }
+  }
 
   // swizzled LDS byte offsets of this lane's operand reads inside a buffer
   int koff[8], voff[4];
@@ -475,16 +518,35 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
       }
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  {
+    // rows addressed by 32-bit offsets from the wave's first row, as the Q copy
+    char* owave = reinterpret_cast<char*>(out + ((size_t)t_base * Hq + g * G) * kHeadDim);
+    // an opaque copy of the lane index: the row terms below are the Q copy's
+    // again, and without it the compiler keeps those alive through the key
+    // loop instead of recomputing them, which costs registers it does not have
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    // row r = 4j + lane/16 of the wave, chunk lane % 16; as in the Q copy, the
+    // token r / G of row group j is uniform when G >= 4
+    if (G >= 4) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    // row r = 4j + lane/16 of the wave (column r: token tw0 + r/G, head g G + r%G),
-    // chunk lane % 16
-    const int r = 4 * j + (lane >> 4), c = lane & 15;
-    const vec8<E> v = *reinterpret_cast<const vec8<E>*>(obuf + r * 256 + ((c ^ (r & 15)) << 4));
-    const int tr = tw0 + (r >> log2G);
-    if (tr < a_end)
-      *reinterpret_cast<vec8<E>*>(out + ((size_t)tr * Hq + g * G + (r & (G - 1))) * kHeadDim +
-                                  8 * c) = v;
+      for (int j = 0; j < 8; ++j) {
+        const int r = 4 * j + (ln >> 4), c = ln & 15;
+        const vec8<E> v = *reinterpret_cast<const vec8<E>*>(obuf + r * 256 + ((c ^ (r & 15)) << 4));
+        const int tq = (4 * j) >> log2G;
+        if (tq < tpw_live)
+          *reinterpret_cast<vec8<E>*>(owave + (uint32_t)r * 256 + (uint32_t)tq * gap + 16 * c) = v;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 4 * j + (ln >> 4), c = ln & 15;
+        const vec8<E> v = *reinterpret_cast<const vec8<E>*>(obuf + r * 256 + ((c ^ (r & 15)) << 4));
+        const int tq = r >> log2G;
+        if (tq < tpw_live)
+          *reinterpret_cast<vec8<E>*>(owave + (uint32_t)r * 256 + (uint32_t)tq * gap + 16 * c) = v;
+      }
+    }
   }
   if (tok_ok && lse != nullptr && hf == 0)
     lse[(size_t)hq * T + tok] = (st.m_ref + __log2f(l)) * kLn2;
@@ -515,9 +577,17 @@ hipError_t launch_attention_narrow(const E* q, const E* khat, const E* vt,
   }
   if (grid <= 0) return hipSuccess;
   const float c_log2 = (float)(scale * 1.4426950408889634);
-  attn_fwd_narrow_kernel<E><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(
-      q, khat, vt, cu, cu_end, sched, sinks, qnorm_w, out, lse, T, Hq, Hkv, G, log2G, t_pad,
-      window, use_rope, (float)eps, theta, c_log2, xcd_per);
+  // the block's 128 / G tokens fit the 16-row angle table from G = 8 on
+  const int rm = !use_rope ? kRopeNone : ((kWaves * kColsPerWave) >> log2G) <= 16 ? kRopeTable
+                                                                                   : kRopeLane;
+#define SA_LAUNCH(RMV)                                                                        \
+  attn_fwd_narrow_kernel<E, RMV><<<dim3((unsigned)grid), dim3(kThreads), 0, stream>>>(        \
+      q, khat, vt, cu, cu_end, sched, sinks, qnorm_w, out, lse, T, Hq, Hkv, G, log2G, t_pad, \
+      window, (float)eps, theta, c_log2, xcd_per)
+  if (rm == kRopeNone) SA_LAUNCH(kRopeNone);
+  else if (rm == kRopeTable) SA_LAUNCH(kRopeTable);
+  else SA_LAUNCH(kRopeLane);
+#undef SA_LAUNCH
   return hipGetLastError();
 }
 

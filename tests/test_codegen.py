@@ -86,13 +86,21 @@ def test_tile_copy_not_waited_before_reads(asm):
     lines = [l.strip() for l in text.splitlines()]
     lds_dma = [i for i, l in enumerate(lines) if l.startswith("global_load_lds_dwordx4")]
     assert lds_dma, "attention kernel copies tiles with global_load_lds_dwordx4"
-    # the in-loop copies follow the per-tile barrier; after each such group a
-    # vmcnt wait may only be the one right before the next barrier, never one
-    # ahead of an LDS read
+    # the in-loop copies follow the per-tile barrier, which the loop takes
+    # right after waiting for the current tile's copy (vmcnt(0)); after each
+    # such group a vmcnt wait may only be the one right before the next
+    # barrier, never one ahead of an LDS read.  (The Q rows' copy before the
+    # loop may follow another barrier, and is waited for on purpose.)
     groups = [i for j, i in enumerate(lds_dma) if j + 1 == len(lds_dma) or lds_dma[j + 1] - i > 8]
     firsts = [i for j, i in enumerate(lds_dma) if j == 0 or i - lds_dma[j - 1] > 8]
-    in_loop = [last for first, last in zip(firsts, groups)
-               if any(l.startswith("s_barrier") for l in lines[max(0, first - 48):first])]
+
+    def after_tile_barrier(first):
+        for k in range(first - 1, max(0, first - 48) - 1, -1):
+            if lines[k].startswith("s_barrier"):
+                return lines[k - 1].startswith("s_waitcnt") and "vmcnt(0)" in lines[k - 1]
+        return False
+
+    in_loop = [last for first, last in zip(firsts, groups) if after_tile_barrier(first)]
     assert len(in_loop) >= 2, "expected the tile copies of both loop halves"
     checked = 0
     for i in in_loop:
