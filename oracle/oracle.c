@@ -96,10 +96,14 @@ static void rope_neox_vec(int d, double p, double theta, double* y) {
 }
 
 /* Steps 1-2 for a whole [rows, H, d] tensor.  x and y may not alias.
- * pos[r] is the document-local position of row r. */
+ * pos[r] is the document-local position of row r.  Rows are independent, so
+ * they are spread over threads with no effect on the values. */
 static void prologue_rows(int rows, const int32_t* pos, int H, int d,
                           const double* x, const double* w, double eps,
                           double theta, int use_rope, double* y) {
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
   for (int r = 0; r < rows; ++r)
     for (int h = 0; h < H; ++h) {
       const double* xi = x + ((size_t)r * H + h) * d;
@@ -297,6 +301,12 @@ int oracle_sink_attn_fwd(int T, int num_docs, const int32_t* cu, int Hq,
  * weights are the RMSNorm parameters ([L] q_norm / k_norm).
  * ------------------------------------------------------------------------ */
 
+static int all_zero(int d, const double* x) {
+  for (int i = 0; i < d; ++i)
+    if (x[i] != 0.0) return 0;
+  return 1;
+}
+
 /* Transpose of step 2 for one head vector: turn each pair by -angle. */
 static void rope_neox_vec_t(int d, double p, double theta, double* y) {
   int half = d / 2;
@@ -334,7 +344,12 @@ static void rmsnorm_vec_bwd(int d, const double* x, const double* w, double eps,
  *   sum is added in a fixed order -- dq_hat over keys in token order; dk_hat
  *   and dv over queries in token order, then head order; dsink and the norm
  *   weights over tokens in order -- so the result does not depend on the
- *   thread count. */
+ *   thread count.  A row whose dout is zero contributes exactly nothing: its
+ *   D is 0, so dS = P (0 - 0) = 0 for every key it sees and its dv terms are
+ *   P * 0 (its lse is finite, since a query always sees its own key).  Both
+ *   passes skip such rows; that changes no value (adding a signed zero to a
+ *   sum leaves it as it is) and makes a backward whose dout is non-zero on a
+ *   sample of rows cost time in proportion to the sample. */
 int oracle_sink_attn_bwd(int T, int num_docs, const int32_t* cu, int Hq, int Hkv,
                          int d, const double* q, const double* k, const double* v,
                          const double* sinks, const double* qnorm_w,
@@ -364,6 +379,20 @@ int oracle_sink_attn_bwd(int T, int num_docs, const int32_t* cu, int Hq, int Hkv
   double* row_lse = (double*)malloc(sizeof(double) * (nrow + 1));
   double* row_D = (double*)malloc(sizeof(double) * (nrow + 1));
   double* row_sink = (double*)malloc(sizeof(double) * (nrow + 1));
+  /* rows with a non-zero dout, and per (token, kv head) whether any row of
+   * the group has one */
+  unsigned char* row_live = (unsigned char*)malloc(nrow + 1);
+  unsigned char* grp_live = (unsigned char*)malloc((size_t)T * Hkv + 1);
+  for (size_t r = 0; r < nrow; ++r) {
+    int live = 0;
+    for (int i = 0; i < d && !live; ++i) live = dout[r * d + i] != 0.0;
+    row_live[r] = (unsigned char)live;
+  }
+  for (size_t c = 0; c < (size_t)T * Hkv; ++c) {
+    int live = 0;
+    for (int j = 0; j < group; ++j) live |= row_live[c * group + j];
+    grp_live[c] = (unsigned char)live;
+  }
   prologue_rows(T, pos_of, Hq, d, q, qnorm_w, eps, theta, use_rope, qh);
   prologue_rows(T, pos_of, Hkv, d, k, knorm_w, eps, theta, use_rope, kh);
   for (size_t i = 0; i < nk; ++i) dv[i] = 0.0;
@@ -386,6 +415,12 @@ int oracle_sink_attn_bwd(int T, int num_docs, const int32_t* cu, int Hq, int Hkv
       const int n = doc_of[t];
       const double* qrow = qh + (size_t)r * d;
       const double* dorow = dout + (size_t)r * d;
+      if (!row_live[r]) {  /* zero dout: D = 0, no dsink term, dq_hat stays 0 */
+        row_lse[r] = 0.0;
+        row_D[r] = 0.0;
+        row_sink[r] = 0.0;
+        continue;
+      }
       double lse;
       attend_row(t, T, Hkv, g, d, qrow, kh, v, sinks[h], scale, window, doc_of, pos_of,
                  scores, out_row, &lse);
@@ -419,10 +454,14 @@ int oracle_sink_attn_bwd(int T, int num_docs, const int32_t* cu, int Hq, int Hkv
       const double* ku = kh + (size_t)c * d;
       double* dku = dkh + (size_t)c * d;
       double* dvu = dv + (size_t)c * d;
-      for (int t = u; t < cu[n + 1]; ++t) {
-        if (!visible(t, u, doc_of, pos_of, window)) continue;
+      /* the queries that can see u: [u, end of its document), and under a
+       * window only the first `window` of them (visible() is 0 past that) */
+      const int t_end = window > 0 && window < cu[n + 1] - u ? u + window : cu[n + 1];
+      for (int t = u; t < t_end; ++t) {
+        if (!grp_live[(size_t)t * Hkv + g] || !visible(t, u, doc_of, pos_of, window)) continue;
         for (int h = g * group; h < (g + 1) * group; ++h) {
           const size_t r = (size_t)t * Hq + h;
+          if (!row_live[r]) continue;
           const double* qrow = qh + r * d;
           const double* dorow = dout + r * d;
           double dot = 0.0;
@@ -454,19 +493,29 @@ int oracle_sink_attn_bwd(int T, int num_docs, const int32_t* cu, int Hq, int Hkv
   }
   /* steps 2 and 1 backwards, token by token in order (fixed summation order
    * for the norm weights) */
+  /* (a row whose dy is all zero has dx = 0 and adds nothing to dw, so it is
+   * written as zeros without the rotation and norm steps) */
   for (int i = 0; i < d; ++i) dqnorm_w[i] = dknorm_w[i] = 0.0;
   for (int t = 0; t < T; ++t) {
     for (int h = 0; h < Hq; ++h) {
       double* dy = dqh + ((size_t)t * Hq + h) * d;
+      double* dx = dq + ((size_t)t * Hq + h) * d;
+      if (all_zero(d, dy)) {
+        for (int i = 0; i < d; ++i) dx[i] = 0.0;
+        continue;
+      }
       if (use_rope) rope_neox_vec_t(d, (double)pos_of[t], theta, dy);
-      rmsnorm_vec_bwd(d, q + ((size_t)t * Hq + h) * d, qnorm_w, eps, dy,
-                      dq + ((size_t)t * Hq + h) * d, dqnorm_w);
+      rmsnorm_vec_bwd(d, q + ((size_t)t * Hq + h) * d, qnorm_w, eps, dy, dx, dqnorm_w);
     }
     for (int g = 0; g < Hkv; ++g) {
       double* dy = dkh + ((size_t)t * Hkv + g) * d;
+      double* dx = dk + ((size_t)t * Hkv + g) * d;
+      if (all_zero(d, dy)) {
+        for (int i = 0; i < d; ++i) dx[i] = 0.0;
+        continue;
+      }
       if (use_rope) rope_neox_vec_t(d, (double)pos_of[t], theta, dy);
-      rmsnorm_vec_bwd(d, k + ((size_t)t * Hkv + g) * d, knorm_w, eps, dy,
-                      dk + ((size_t)t * Hkv + g) * d, dknorm_w);
+      rmsnorm_vec_bwd(d, k + ((size_t)t * Hkv + g) * d, knorm_w, eps, dy, dx, dknorm_w);
     }
   }
   free(qh);
@@ -476,6 +525,8 @@ int oracle_sink_attn_bwd(int T, int num_docs, const int32_t* cu, int Hq, int Hkv
   free(row_lse);
   free(row_D);
   free(row_sink);
+  free(row_live);
+  free(grp_live);
   free(doc_of);
   free(pos_of);
   return ORACLE_OK;

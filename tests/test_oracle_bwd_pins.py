@@ -7,7 +7,8 @@ not come from its own formulas:
   and a disabled sink;
 * torch.autograd in float64 through a dense masked-softmax formulation of
   the forward (its forward is first checked against the forward oracle), on
-  every element;
+  every element, also with a dout that is zero on most rows (rows the oracle
+  skips);
 * exact identities: RMSNorm's scale invariance makes every (token, head) row
   of dq orthogonal to the raw q row (and dk to k) when eps = 0; out is linear
   in v, so sum(dv * v) = sum(dout * out); a disabled sink has zero gradient;
@@ -124,6 +125,27 @@ def test_autograd_every_element(window, rope):
     g = _grads(cu, p, dout, window, rope, theta, eps)
     for name, key in KEYS.items():
         assert np.allclose(g[key], tp[name].grad.numpy(), rtol=1e-9, atol=1e-11), name
+
+
+@pytest.mark.parametrize("window, rope", [(-1, False), (4, True)])
+def test_autograd_sparse_dout(window, rope):
+    # dout non-zero on a few (token, head) rows only, some tokens with a single
+    # live head: the oracle skips the zero rows in both of its passes, and
+    # every gradient must still be autograd's on every element
+    cu, p, dout = _problem(seed=4, lengths=(5, 11, 1, 8))
+    T, Hq, _ = dout.shape
+    live = np.zeros((T, Hq), dtype=bool)
+    live[[0, 4, 9, 15, 16, 24], :] = True
+    live[[2, 12, 20], [1, 3, 0]] = True
+    dout = np.where(live[:, :, None], dout, 0.0)
+    theta, eps = 100.0, 1e-6
+    tp = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True) for k, v in p.items()}
+    out = _torch_forward(cu, tp, window, rope, theta, eps, 1.0 / np.sqrt(8))
+    (out * torch.tensor(dout)).sum().backward()
+    g = _grads(cu, p, dout, window, rope, theta, eps)
+    for name, key in KEYS.items():
+        assert np.allclose(g[key], tp[name].grad.numpy(), rtol=1e-9, atol=1e-11), name
+    assert np.all(g["dq"][~live] == 0.0)
 
 
 def test_norm_scale_invariance_and_value_linearity():
