@@ -1,14 +1,18 @@
 """The backward at the sizes the backward bench times, checked against the fp64
 oracle on every output element.
 
-Workloads: full (one causal document of 32,768 tokens, no RoPE) and long (two
-documents of 65,536 tokens, window 4,096, NeoX RoPE, sinks N(2, 1)), 32 query
-/ 4 kv heads, d = 128, bf16, through sink_attn_bwd with its automatic kernel
-choices (the launch configuration the bench times).
+Workloads: every named one -- full (one causal document of 32,768 tokens, no
+RoPE), long (two documents of 65,536 tokens, window 4,096, NeoX RoPE, sinks
+N(2, 1)), sliding (8 documents of U[256, 4096] tokens, window 1,024, RoPE) and
+the two mixed ones (512 documents of geometric lengths with mean 200, causal
+without RoPE, or window 512 with RoPE) -- 32 query / 4 kv heads, d = 128,
+bf16, through sink_attn_bwd with its automatic kernel choices (the launch
+configuration the bench times).
 
 dout is zero except on a seeded sample of query tokens, every head of each:
-each document's first and last 64 tokens, the tokens around the window edge,
-and 128 random ones (workloads.sample_rows).  A row whose dout is zero adds
+each document's first and last 64 tokens (8 for the mixed workloads' short
+documents), the tokens around the window edge, and 128 random ones
+(workloads.sample_rows).  A row whose dout is zero adds
 exactly nothing to any gradient (its D = dout . out is 0, so dS = P (dP - D)
 is 0 for every key it sees, and its dv terms are P * 0), so every gradient is
 a sum over the sampled rows alone.  The oracle skips the zero rows, which
@@ -32,13 +36,16 @@ def _say(msg):
     print(msg, flush=True)
 
 
-@pytest.mark.parametrize("name", ["full", "long"])
-def test_full_size_backward_on_sampled_rows(name):
+# (workload, rows sampled at each document end): the mixed workloads' 512
+# short documents take 8 rows at each end (64 would be half their tokens)
+@pytest.mark.parametrize("name,edge", [("full", 64), ("long", 64), ("sliding", 64),
+                                       ("mixed_causal", 8), ("mixed_sliding", 8)])
+def test_full_size_backward_on_sampled_rows(name, edge):
     require_gpu()
     w = workloads.named_workloads()[name]
     _say(f"case bwd {name} T={w.total_tokens} sampled dout rows")
     inp = workloads.make_inputs(w, seed=0)
-    rows = workloads.sample_rows(w.lengths, w.window, 128, seed=5)
+    rows = workloads.sample_rows(w.lengths, w.window, 128, seed=5, edge=edge)
     live = torch.zeros(w.total_tokens, dtype=torch.bool)
     live[torch.from_numpy(rows).long()] = True
     dout = workloads.make_grad_output(w, seed=0)
