@@ -121,45 +121,84 @@ __global__ __launch_bounds__(kThreads) void prologue_16_kernel(
   if (use_rope && tid >= 64 && tid < 128)
     s_invf[tid - 64] = pow(theta, -(double)(tid - 64) / 64.0) * kInvTwoPi;
 
-  // Documents of the tile's tokens.  Wave 0 finds the document d0 of the
-  // first token (the largest d < D with cu[d] <= t0) level by level: each
+  // The tile's V and K rows go out first: the document lookup below takes a
+  // few dependent loads, and without this the rows would be requested only
+  // after it.  The loads are unconditional -- a token at or past T reads row
+  // T - 1 -- so that no register merge makes the compiler wait for them
+  // here; rows of padding keys and of document padding are zeroed once the
+  // documents are known (s_real).
+  uint4 vval[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + kThreads * i;
+    const int t = min(t0 + (c >> 4), T - 1);
+    vval[i] = *reinterpret_cast<const uint4*>(v + ((size_t)t * Hkv + g) * kHeadDim + (c & 15) * 8);
+  }
+  // K rows: 8 lanes per token; lane c holds channels 8c..8c+7 and 64+8c..64+8c+7
+  vec8<E> krow[2][2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int t = min(t0 + (tid >> 3) + 32 * it, T - 1);
+    const E* kp = k + ((size_t)t * Hkv + g) * kHeadDim;
+    krow[it][0] = *reinterpret_cast<const vec8<E>*>(kp + 8 * (tid & 7));
+    krow[it][1] = *reinterpret_cast<const vec8<E>*>(kp + 64 + 8 * (tid & 7));
+  }
+  // the norm weights of the lane's channels, with the rows
+  float wk[16];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    wk[e] = knorm_w[8 * (tid & 7) + e];
+    wk[8 + e] = knorm_w[64 + 8 * (tid & 7) + e];
+  }
+
+  // Documents of the tile's tokens.  cu[d0 .. d0 + 64] and cu_end[d0 ..
+  // d0 + 63] go to LDS, where each token finds its own document, its start
+  // and whether it is real.  With at most 64 documents d0 = 0 and the LDS
+  // copy holds every start.  Otherwise wave 0 first finds the document d0 of
+  // the first token (the largest d < D with cu[d] <= t0) level by level: each
   // lane tests one of 64 evenly spaced candidates and a ballot keeps the last
   // one that passes (cu is non-decreasing), so D <= 4096 takes two dependent
-  // loads instead of a binary search's 12.  cu[d0 .. d0 + 64] then go to LDS,
-  // where each token finds its own document; a tile that crosses more than 64
+  // loads instead of a binary search's 12; a tile that crosses more than 64
   // document starts (empty documents) falls back to a search in memory.
   __shared__ int s_d0;
   __shared__ int s_cu[kKeyTile + 1];
+  __shared__ int s_end[kKeyTile];
   __shared__ int s_real[kKeyTile];  // token inside [0, T) and not document padding
   __shared__ int s_pos0[kKeyTile];  // start of the token's document (RoPE positions)
-  if (tid < 64) {
-    int lo = 0, hi = D - 1;  // cu[lo] <= t0 (cu[0] == 0)
-    const int tq = min(t0, T - 1);
-    while (hi > lo) {
-      const int step = (hi - lo + 64) / 64;
-      const int idx = lo + tid * step;
-      const bool le = idx <= hi && cu[idx] <= tq;
-      const int cnt = __popcll(__ballot(le));
-      // (cnt is 0 only for a malformed cu with cu[0] > t0; clamping keeps
-      // every read in bounds whatever cu holds)
-      lo += max(cnt - 1, 0) * step;
-      hi = min(hi, lo + step - 1);
+  if (D > kKeyTile) {
+    if (tid < 64) {
+      int lo = 0, hi = D - 1;  // cu[lo] <= t0 (cu[0] == 0)
+      const int tq = min(t0, T - 1);
+      while (hi > lo) {
+        const int step = (hi - lo + 64) / 64;
+        const int idx = lo + tid * step;
+        const bool le = idx <= hi && cu[idx] <= tq;
+        const int cnt = __popcll(__ballot(le));
+        // (cnt is 0 only for a malformed cu with cu[0] > t0; clamping keeps
+        // every read in bounds whatever cu holds)
+        lo += max(cnt - 1, 0) * step;
+        hi = min(hi, lo + step - 1);
+      }
+      if (tid == 0) s_d0 = lo;
     }
-    if (tid == 0) s_d0 = lo;
+    __syncthreads();
   }
-  __syncthreads();
-  const int d0 = s_d0;
+  const int d0 = D > kKeyTile ? s_d0 : 0;
   if (tid <= kKeyTile) s_cu[tid] = d0 + tid <= D ? cu[d0 + tid] : INT_MAX;
+  if (tid >= 128 && tid < 128 + kKeyTile) {
+    const int j = tid - 128;
+    s_end[j] = d0 + j < D ? cu_end[d0 + j] : 0;
+  }
   __syncthreads();
   if (tid < kKeyTile) {
     const int t = t0 + tid;
     int real = 0, pos0 = 0;
     if (t < T) {
       const int jmax = min(kKeyTile, D - 1 - d0);  // documents d0 .. d0 + jmax
-      int d;
       if (jmax == kKeyTile && s_cu[kKeyTile] <= t) {
-        d = doc_of_token(cu, D, t);
+        const int d = doc_of_token(cu, D, t);
         pos0 = cu[d];
+        real = t < cu_end[d];
       } else {
         int a = 0, b = jmax;  // largest j <= jmax with s_cu[j] <= t
         while (a < b) {
@@ -167,10 +206,9 @@ __global__ __launch_bounds__(kThreads) void prologue_16_kernel(
           if (s_cu[mid] <= t) a = mid;
           else b = mid - 1;
         }
-        d = d0 + a;
         pos0 = s_cu[a];
+        real = t < s_end[a];
       }
-      real = t < cu_end[d];
     }
     s_real[tid] = real;
     s_pos0[tid] = pos0;
@@ -182,14 +220,13 @@ __global__ __launch_bounds__(kThreads) void prologue_16_kernel(
   for (int i = 0; i < 4; ++i) {
     const int c = tid + kThreads * i;
     const int tt = c >> 4, cc = c & 15;
-    const int t = t0 + tt;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (s_real[tt]) val = *reinterpret_cast<const uint4*>(v + ((size_t)t * Hkv + g) * kHeadDim + cc * 8);
+    // (a mask per word: a select of the whole vector goes through scratch)
+    const unsigned m = s_real[tt] ? 0xFFFFFFFFu : 0u;
+    const uint4 val = make_uint4(vval[i].x & m, vval[i].y & m, vval[i].z & m, vval[i].w & m);
     *reinterpret_cast<uint4*>(&s_v[tt][cc * 8]) = val;
   }
   __syncthreads();
 
-  // K rows: 8 lanes per token; lane c holds channels 8c..8c+7 and 64+8c..64+8c+7
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int tt = (tid >> 3) + 32 * it;
@@ -197,18 +234,10 @@ __global__ __launch_bounds__(kThreads) void prologue_16_kernel(
     const int t = t0 + tt;
     const bool real = s_real[tt];
     float x[16];
-    if (real) {
-      const E* kp = k + ((size_t)t * Hkv + g) * kHeadDim;
-      const vec8<E> lo = *reinterpret_cast<const vec8<E>*>(kp + 8 * c);
-      const vec8<E> hi = *reinterpret_cast<const vec8<E>*>(kp + 64 + 8 * c);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        x[e] = (float)lo[e];
-        x[8 + e] = (float)hi[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] = 0.f;
+    for (int e = 0; e < 8; ++e) {
+      x[e] = real ? (float)krow[it][0][e] : 0.f;
+      x[8 + e] = real ? (float)krow[it][1][e] : 0.f;
     }
     float ss = 0.f;
 #pragma unroll
@@ -220,8 +249,8 @@ __global__ __launch_bounds__(kThreads) void prologue_16_kernel(
     const float inv = real ? 1.0f / sqrtf(ss * (1.0f / kHeadDim) + eps) : 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      x[e] *= inv * knorm_w[8 * c + e];
-      x[8 + e] *= inv * knorm_w[64 + 8 * c + e];
+      x[e] *= inv * wk[e];
+      x[8 + e] *= inv * wk[8 + e];
     }
     if (use_rope && real) {
       const int p = t - s_pos0[tt];
