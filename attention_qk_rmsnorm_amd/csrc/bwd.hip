@@ -907,7 +907,6 @@ __global__ __launch_bounds__(WAVES * 64, 8 / WAVES) void bwd_dq_kernel(
     return;
   }
   if (use_rope && tid < 64) s_invf[tid] = pow(theta, -(double)tid / 64.0) * kInvTwoPi;
-  const int tcl = t_in ? t : 0;
   // the block's key range: the keys its real tokens see (document padding
   // sees none)
   const int kt_lo = lo & ~(kKeyTile - 1);
