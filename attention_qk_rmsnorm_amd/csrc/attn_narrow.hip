@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
   // l writes its 16 bytes at byte 16 l of that, i.e. row r = 4j + l / 16 at
   // position l % 16; lane l therefore fetches chunk (l % 16) ^ (r % 16) of
   // row r, so that chunk k of row r sits at position k ^ (r % 16).  Rows are
-  // addressed by 32-bit offsets from the block's first (token, head) row.
+  // addressed by 32-bit offsets from the wave's first (token, head) row.
   // The copies go out before the first tile's copy, and the wait before the
   // reads covers both.
   char* stg = lds + kBuf + wave_u * (32 * 256);
@@ -329,7 +329,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_narrow_kernel(
   // sits r * 256 + (r / G) * (Hq - G) * 256 bytes past the wave's first row.
   // A column past the block's tokens reads the wave's first row instead (its
   // norm factor is zero below), or, in a wave without tokens, the block's.
-  // (both wave-uniform; readfirstlane makes them scalars for the compiler)
+  // The wave's token count and base token are wave-uniform; readfirstlane
+  // makes them scalars for the compiler.
   const int tpw_live = __builtin_amdgcn_readfirstlane(tw1 - tw0);  // tokens of this wave (may be <= 0)
   const int t_base = __builtin_amdgcn_readfirstlane(tpw_live > 0 ? tw0 : a);
   const uint32_t gap = (uint32_t)(Hq - G) * (kHeadDim * (uint32_t)sizeof(E));
