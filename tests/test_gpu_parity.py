@@ -4,6 +4,8 @@ Small cases compare every output element; the full-size workloads (the sizes
 and launch configuration the benchmark times) compare a deterministic sample of
 rows the oracle computes one by one: each document's first and last 64 tokens,
 the tokens around the window edge and seeded random tokens."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -134,6 +136,19 @@ def test_bf16_softmax_scale_override():
     _say("case bf16 scale 0.06")
     inp = custom_inputs([120, 45])
     check_parity(inp, 50, True, label="scale", softmax_scale=0.06)
+
+
+@pytest.mark.parametrize("scale", [0.2, 0.3])
+@pytest.mark.parametrize("tile", [1, 2])
+def test_bf16_large_softmax_scale_scaled_bound(scale, tile):
+    # a score's error from rounding q_hat and k_hat to bf16 is proportional to
+    # softmax_scale (and to the norm weights, near 1 here), so the bounds that
+    # hold at Flint's default scale 1/sqrt(128) are taken times
+    # scale * sqrt(128): 2.26x at 0.2, 3.39x at 0.3
+    f = scale * math.sqrt(128)
+    _say(f"case bf16 scale {scale} tile={tile} bounds x{f:.2f}")
+    check_parity(custom_inputs([120, 45, 300]), 50, True, label=f"scale {scale} tile={tile}",
+                 bound_scale=f, softmax_scale=scale, tile_config=tile)
 
 
 def test_bf16_window_at_least_length_equals_causal():
